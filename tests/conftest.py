@@ -1,0 +1,31 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def kq():
+    """The HIP library binding; GPU tests fail loudly if it cannot be loaded."""
+    if not gpu_available():
+        pytest.skip("no GPU visible")
+    import w4a4_post_quantization_amd as kq_mod
+    kq_mod.load()          # raises if libkq.so is missing or fails to load
+    return kq_mod

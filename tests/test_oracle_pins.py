@@ -1,0 +1,451 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each test pins one part of the oracle to something other than the oracle itself:
+values fixed by the format definition or a published table (tests/golden/),
+brute force over small cases, closed forms, invariants and library routines.
+All CPU, all fast.
+"""
+
+import fractions
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import linear, lloyd_max, mxfp4, pipeline, ties, transforms
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- P1: E2M1 RNE
+
+def test_e2m1_golden_table():
+    for v, c in _golden_rows("e2m1_rne.txt"):
+        assert int(mxfp4.e2m1_encode(np.array(float(v)))) == int(c), v
+
+
+def test_e2m1_roundtrip_all_codes():
+    codes = np.arange(16, dtype=np.uint8)
+    vals = mxfp4.e2m1_decode(codes)
+    back = mxfp4.e2m1_encode(vals)
+    # -0 (code 8) decodes to 0.0 == -0.0, and an exact zero encodes as +0 (code 0)
+    expect = codes.copy()
+    expect[8] = 0
+    assert np.array_equal(back, expect)
+    assert sorted(set(np.abs(vals).tolist())) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_brute_force_nearest_even():
+    """Brute force: for many values, the chosen code is a nearest representable value,
+    and on an exact midpoint it is the one with an even mantissa bit."""
+    grid = mxfp4.e2m1_decode(np.arange(16, dtype=np.uint8))
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([rng.uniform(-7, 7, 20000),
+                           [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0]])
+    got = mxfp4.e2m1_decode(mxfp4.e2m1_encode(vals))
+    for v, g in zip(vals, got):
+        dist = np.abs(grid - v)
+        assert abs(g - v) == dist.min(), v
+        near = np.unique(np.abs(grid[dist == dist.min()]))
+        if len(near) == 2:      # a true tie: even code index, i.e. mantissa bit 0
+            idx = int(np.where(mxfp4.E2M1_MAGNITUDES == abs(g))[0][0])
+            assert idx % 2 == 0
+
+
+def test_e2m1_boundaries_nextafter_and_saturation():
+    bounds = [(0.25, 0, 1), (0.75, 1, 2), (1.25, 2, 3), (1.75, 3, 4), (2.5, 4, 5), (3.5, 5, 6), (5.0, 6, 7)]
+    for b, below, above in bounds:
+        assert int(mxfp4.e2m1_encode(np.nextafter(b, 0.0))) == below
+        assert int(mxfp4.e2m1_encode(np.nextafter(b, 10.0))) == above
+        assert int(mxfp4.e2m1_encode(-np.nextafter(b, 10.0))) == 8 + above
+    for big in (6.0 * (1 + 2.0 ** -23), 7.99, 1e30):
+        assert int(mxfp4.e2m1_encode(np.array(big))) == 7
+        assert int(mxfp4.e2m1_encode(np.array(-big))) == 15
+    assert int(mxfp4.e2m1_encode(np.array(-0.0))) == 0          # exact zero is +0
+    assert int(mxfp4.e2m1_encode(np.array(-1e-300))) == 8       # negative rounding to zero
+
+
+# ---------------------------------------------------------------- P2: E8M0
+
+def test_e8m0_powers_of_two():
+    for k in range(-120, 125):
+        a = math.ldexp(1.0, k)
+        e = int(mxfp4.e8m0_exponent(np.array([a]))[0])
+        assert e == k - 2
+        assert a * 2.0 ** -e == 4.0
+        below = np.nextafter(a, 0.0)
+        assert int(mxfp4.e8m0_exponent(np.array([below]))[0]) == k - 3
+        # block maximum scaled into [4, 8)
+        assert 4.0 <= below * 2.0 ** (-(k - 3)) < 8.0
+
+
+def test_e8m0_clamps_and_zero():
+    assert int(mxfp4.e8m0_exponent(np.array([0.0]))[0]) == -127
+    assert int(mxfp4.e8m0_exponent(np.array([2.0 ** -140]))[0]) == -127
+    assert int(mxfp4.e8m0_exponent(np.array([2.0 ** 140]))[0]) == 127
+    codes, sb, e = mxfp4.quantize_blocks(np.zeros((1, 32)))
+    assert sb[0, 0] == 0 and np.all(codes == 0)
+
+
+def test_pack_nibble_order():
+    codes = np.array([[1, 2, 15, 0]], dtype=np.uint8)
+    p = mxfp4.pack_nibbles(codes)
+    assert p.tolist() == [[0x21, 0x0F]]
+    assert np.array_equal(mxfp4.unpack_nibbles(p), codes)
+
+
+def test_quantization_error_bound():
+    """P10: unsaturated values are within half a local grid step of their dequantized
+    value; saturated values (above 6 after scaling) within 2 scale units."""
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    codes, sb, e = mxfp4.quantize_blocks(y)
+    d = mxfp4.dequantize(codes, sb)
+    s = (y.reshape(64, 8, 32) * np.ldexp(1.0, -e)[..., None]).reshape(64, 256)
+    err = np.abs(y - d) * np.repeat(np.ldexp(1.0, -e), 32, axis=1)
+    a = np.abs(s)
+    half_step = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+    sat = a > 6
+    assert np.all(err[~sat] <= half_step[~sat] + 1e-15)
+    assert np.all(err[sat] < 2.0)
+    assert np.all(a < 8.0) and np.all(a.reshape(64, 8, 32).max(axis=2) >= 4.0)
+
+
+# ---------------------------------------------------------------- P3: Kronecker
+
+def _random_factors(seed):
+    rng = np.random.default_rng(seed)
+    A = (rng.standard_normal((4, 4)) + 2 * np.eye(4)).astype(np.float32)
+    B = (rng.standard_normal((8, 8)) + 2 * np.eye(8)).astype(np.float32)
+    return A, B
+
+
+def test_kron_dense_matches_factored_form():
+    """y = x (A (x) B) equals the mixed-product form Ym = A^T Xm B with Xm[i][j] = x[8i+j]."""
+    A, B = _random_factors(2)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((16, 32 * 6))
+    y = transforms.apply_block_matrix(x, transforms.kron_block_matrix(A, B))
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    for m in range(16):
+        for b in range(6):
+            Xm = x[m, 32 * b:32 * b + 32].reshape(4, 8)
+            Ym = A64.T @ Xm @ B64
+            ref = Ym.reshape(32)
+            got = y[m, 32 * b:32 * b + 32]
+            assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_kron_entries_and_inverse():
+    A, B = _random_factors(4)
+    P = transforms.kron_block_matrix(A, B)
+    for i, j, k, l in itertools.product(range(4), range(8), range(4), range(8)):
+        assert P[8 * i + j, 8 * k + l] == np.float64(A[i, k]) * np.float64(B[j, l])
+    Pinv = np.linalg.inv(P)
+    ref = np.kron(np.linalg.inv(A.astype(np.float64)), np.linalg.inv(B.astype(np.float64)))
+    assert np.max(np.abs(Pinv - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- P4: Hadamard / RPBH
+
+def test_hadamard_sylvester_and_orthogonality():
+    H = transforms.hadamard32()
+    Hi = H.astype(np.int64)
+    assert np.array_equal(Hi @ Hi.T, 32 * np.eye(32, dtype=np.int64))
+    # Sylvester recursion built here, and the closed form (-1)^popcount(i & j)
+    S = np.array([[1]], dtype=np.int64)
+    for _ in range(5):
+        S = np.block([[S, S], [S, -S]])
+    assert np.array_equal(Hi, S)
+    for i in range(32):
+        for j in range(32):
+            assert Hi[i, j] == (-1) ** bin(i & j).count("1")
+
+
+def test_rpbh_orthogonal_and_matches_dense():
+    K = 128
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(K)
+    sign = rng.choice([-1, 1], K)
+    R = transforms.rpbh_dense(perm, sign)
+    assert np.max(np.abs(R @ R.T - np.eye(K))) <= 1e-14
+    x = rng.standard_normal((7, K))
+    y = transforms.rpbh_apply(x, perm, sign)
+    assert np.max(np.abs(y - x @ R)) <= 1e-13
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    # the gather convention: (x Pi)_j = x_{pi(j)}
+    xp = x @ R @ R.T
+    assert np.allclose(xp, x, atol=1e-13)
+    u = np.zeros(K)
+    u[perm[3]] = 1.0
+    v = transforms.rpbh_apply(u[None, :], perm, sign)[0]
+    blk = 0
+    assert np.allclose(np.abs(v[blk * 32:(blk + 1) * 32]), 1 / math.sqrt(32))
+
+
+# ---------------------------------------------------------------- P5: the identity
+
+@pytest.mark.parametrize("kind", ["kron", "rpbh"])
+def test_invertible_transform_identity(kind):
+    """(XP)(P^-1 W) = XW (KroQuant section 01; OrbitQuant section 03 W' = R^-1 W)."""
+    rng = np.random.default_rng(6)
+    K, N, M = 256, 96, 20
+    X = rng.standard_normal((M, K))
+    Wt = rng.standard_normal((N, K))             # W^T, [out][in]
+    if kind == "kron":
+        A, B = _random_factors(7)
+        xf = {"kind": "kron", "A": A, "B": B}
+    else:
+        xf = {"kind": "rpbh", "perm": rng.permutation(K), "sign": rng.choice([-1, 1], K)}
+    lhs = pipeline.apply_transform(X, xf) @ pipeline.inverse_fold(Wt, xf).T
+    rhs = X @ Wt.T
+    assert np.linalg.norm(lhs - rhs) <= 1e-12 * np.linalg.norm(rhs)
+
+
+def test_fold_solves_forward_transform():
+    """P W' = W block by block (the fold is the inverse, checked with a linear solve)."""
+    A, B = _random_factors(8)
+    rng = np.random.default_rng(9)
+    Wt = rng.standard_normal((10, 96))
+    wpt = transforms.fold_kron(Wt, A, B)
+    P = transforms.kron_block_matrix(A, B)
+    for b in range(3):
+        W_blk = Wt[:, 32 * b:32 * b + 32].T          # [32, N]
+        sol = scipy.linalg.solve(P, W_blk)           # P^-1 W
+        assert np.allclose(wpt[:, 32 * b:32 * b + 32].T, sol, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P6: centring + rank-1
+
+def test_centring_restore_exact():
+    rng = np.random.default_rng(10)
+    X = (rng.standard_normal((8, 64)) * 3 + 5).astype(np.float16)
+    mu = pipeline.token_mean_f16(X)
+    xc = pipeline.centre(X, mu)
+    assert np.array_equal(xc + mu.astype(np.float64)[:, None], X.astype(np.float64))
+    # exact rational arithmetic: (x - mu 1^T) W + mu (1^T W) = x W
+    W = rng.integers(-5, 6, size=(64, 3))
+    for m in range(2):
+        xf = [fractions.Fraction(float(v)) for v in X[m]]
+        muf = fractions.Fraction(float(mu[m]))
+        for n in range(3):
+            lhs = sum((xf[k] - muf) * int(W[k, n]) for k in range(64)) + muf * sum(int(W[k, n]) for k in range(64))
+            rhs = sum(xf[k] * int(W[k, n]) for k in range(64))
+            assert lhs == rhs
+
+
+def test_centred_rotation_plus_rank1_equals_xw():
+    rng = np.random.default_rng(11)
+    K, N = 128, 40
+    X = (rng.standard_normal((12, K)) + rng.normal(0, 4, (12, 1))).astype(np.float16)
+    Wt = rng.standard_normal((N, K))
+    xf = {"kind": "rpbh", "perm": rng.permutation(K), "sign": rng.choice([-1, 1], K)}
+    mu = pipeline.token_mean_f16(X)
+    y = pipeline.apply_transform(pipeline.centre(X, mu), xf)
+    wbar = Wt.sum(axis=1)
+    lhs = y @ pipeline.inverse_fold(Wt, xf).T + mu.astype(np.float64)[:, None] * wbar[None, :]
+    rhs = X.astype(np.float64) @ Wt.T
+    assert np.linalg.norm(lhs - rhs) <= 1e-12 * np.linalg.norm(rhs)
+
+
+# ---------------------------------------------------------------- P7: mean survives Hadamard
+
+def test_constant_token_survives_rotation_as_one_direction():
+    """CentriQ abstract: a per-token mean survives the Hadamard rotation as one dominant
+    coordinate per block; after centring it is gone."""
+    K = 256
+    rng = np.random.default_rng(12)
+    perm, sign = rng.permutation(K), rng.choice([-1, 1], K)
+    c = 2.75
+    x = np.full((1, K), c)
+    y = transforms.rpbh_apply(x, perm, sign)[0].reshape(K // 32, 32)
+    for blk in y:
+        nz = np.flatnonzero(np.abs(blk) > 1e-12)
+        assert len(nz) == 1 and nz[0] == 0
+        assert abs(abs(blk[0]) - math.sqrt(32) * c) <= 1e-12
+    mu = pipeline.token_mean_f16(x.astype(np.float16))
+    yc = pipeline.apply_transform(pipeline.centre(x.astype(np.float16), mu), {"kind": "rpbh", "perm": perm, "sign": sign})
+    assert np.all(yc == 0.0)
+    out = pipeline.transform_quantize(x.astype(np.float16), {"kind": "rpbh", "perm": perm, "sign": sign},
+                                      center=True)
+    assert np.all(out["codes"] == 0) and np.all(out["scales"] == 0)
+
+
+# ---------------------------------------------------------------- P8: Lloyd-Max
+
+def test_lloyd_max_against_published_table():
+    rows = _golden_rows("lloyd_max_normal.txt")
+    for r in rows:
+        if r[0] == "levels":
+            n = int(r[1])
+            ref = np.array([float(v) for v in r[2:]])
+            got = lloyd_max.lloyd_max_levels(n)
+            assert np.allclose(got, ref, atol=6e-4), (n, got)
+        elif r[0] == "thresholds":
+            got = lloyd_max.thresholds(lloyd_max.lloyd_max_levels(int(r[1])))
+            assert np.allclose(got, [float(v) for v in r[2:]], atol=6e-4)
+        elif r[0] == "mse":
+            got = lloyd_max.mse(lloyd_max.lloyd_max_levels(int(r[1])))
+            assert abs(got - float(r[2])) <= 2e-3 * float(r[2])
+
+
+def test_lloyd_max_fixed_point_and_empirical_mse():
+    for n in (4, 16):
+        lv = lloyd_max.lloyd_max_levels(n)
+        assert lloyd_max.fixed_point_residual(lv) <= 1e-12
+        assert np.all(np.diff(lv) > 0)
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((64, 4096))
+    codes, s = lloyd_max.lm4_token_quantize(z)
+    zq = lloyd_max.lm4_dequantize(codes, s)
+    emp = np.mean((zq - z) ** 2)
+    assert abs(emp - lloyd_max.mse(lloyd_max.LEVELS16)) < 1.5e-3
+
+
+def test_lm4_edges():
+    thr = lloyd_max.thresholds(lloyd_max.LEVELS16)
+    # a value exactly on a threshold goes to the smaller magnitude; sign-magnitude layout
+    assert int(lloyd_max.sign_magnitude_encode(np.array(thr[2]), thr)) == 2
+    assert int(lloyd_max.sign_magnitude_encode(np.array(-thr[2]), thr)) == 8 + 2
+    assert int(lloyd_max.sign_magnitude_encode(np.array(np.nextafter(thr[2], 9)), thr)) == 3
+    assert int(lloyd_max.sign_magnitude_encode(np.array(100.0), thr)) == 7
+    codes, s = lloyd_max.lm4_token_quantize(np.zeros((2, 64)))
+    assert np.all(codes == 0) and np.all(s == 0)
+    # decode undoes encode for level values
+    lv = lloyd_max.LEVELS16
+    c = lloyd_max.sign_magnitude_encode(np.concatenate([lv, -lv]), thr)
+    assert np.array_equal(lloyd_max.sign_magnitude_decode(c, lv), np.concatenate([lv, -lv]))
+
+
+def test_w2_pack_and_groups():
+    rng = np.random.default_rng(14)
+    wt = rng.standard_normal((6, 128))
+    codes, s = lloyd_max.w2_group_quantize(wt)
+    assert codes.max() <= 3 and s.dtype == np.float16
+    p = lloyd_max.pack_2bit(codes)
+    assert np.array_equal(lloyd_max.unpack_2bit(p), codes)
+    assert lloyd_max.pack_2bit(np.array([[1, 2, 3, 0]], dtype=np.uint8)).tolist() == [[1 | (2 << 2) | (3 << 4)]]
+    d = lloyd_max.w2_dequantize(codes, s)
+    # every dequantized weight is +-level * its group scale
+    g = np.abs(d.reshape(6, 4, 32)) / s.astype(np.float64)[..., None]
+    assert np.all(np.isclose(g, lloyd_max.LEVELS4[0]) | np.isclose(g, lloyd_max.LEVELS4[1]))
+
+
+# ---------------------------------------------------------------- P9: GEMM
+
+def test_gemm_triple_loop_and_block_form():
+    rng = np.random.default_rng(15)
+    M, N, K = 3, 5, 64
+    y = rng.standard_normal((M, K)) * 3
+    w = rng.standard_normal((N, K))
+    xc, xs, _ = mxfp4.quantize_blocks(y)
+    wc, ws, _ = mxfp4.quantize_blocks(w)
+    xp, wp = mxfp4.pack_nibbles(xc), mxfp4.pack_nibbles(wc)
+    Xf = rng.standard_normal((M, K)).astype(np.float16)
+    L1 = rng.standard_normal((4, K)).astype(np.float16)
+    L2 = rng.standard_normal((N, 4)).astype(np.float16)
+    mu = rng.standard_normal(M).astype(np.float16)
+    wbar = rng.standard_normal(N).astype(np.float16)
+    Y = linear.w4a4_linear(xp, xs, wp, ws, Xf, L1, L2, mu, wbar)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for b in range(K // 32):             # per-block scaled sums of code products
+                sub = 0.0
+                for k in range(32 * b, 32 * b + 32):
+                    sub += mxfp4.e2m1_decode(xc[m, k]) * mxfp4.e2m1_decode(wc[n, k])
+                acc += sub * 2.0 ** (int(xs[m, b]) - 127 + int(ws[n, b]) - 127)
+            t = sum(sum(float(Xf[m, k]) * float(L1[r, k]) for k in range(K)) * float(L2[n, r]) for r in range(4))
+            acc += t + float(mu[m]) * float(wbar[n])
+            assert abs(Y[m, n] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_gemm_sampled_rows_cols_match_full():
+    rng = np.random.default_rng(16)
+    M, N, K = 9, 11, 96
+    xc, xs, _ = mxfp4.quantize_blocks(rng.standard_normal((M, K)))
+    wc, ws, _ = mxfp4.quantize_blocks(rng.standard_normal((N, K)))
+    xp, wp = mxfp4.pack_nibbles(xc), mxfp4.pack_nibbles(wc)
+    full = linear.w4a4_linear(xp, xs, wp, ws)
+    rows, cols = np.array([0, 4, 8]), np.array([1, 10])
+    part = linear.w4a4_linear(xp, xs, wp, ws, rows=rows, cols=cols)
+    assert np.array_equal(part, full[np.ix_(rows, cols)])
+
+
+# ---------------------------------------------------------------- P11: tie bound
+
+def test_float32_kron_within_gamma_bound():
+    """A float32 evaluation of the factored Kronecker product (the same operation count
+    as a register implementation) stays within the gamma_n bound used to classify ties."""
+    A, B = _random_factors(17)
+    rng = np.random.default_rng(18)
+    x16 = (rng.standard_normal((64, 32 * 8)) * np.where(rng.random(32 * 8) < 0.05, 50, 1)).astype(np.float16)
+    x = x16.astype(np.float64)
+    P = transforms.kron_block_matrix(A, B)
+    y = transforms.apply_block_matrix(x, P)
+    tau = ties.gamma_tau(12, transforms.apply_block_matrix(np.abs(x), np.abs(P)))
+    A32, B32 = A.astype(np.float32), B.astype(np.float32)
+    for m in range(64):
+        for b in range(8):
+            Xm = x16[m, 32 * b:32 * b + 32].astype(np.float32).reshape(4, 8)
+            Z = np.zeros((4, 8), np.float32)
+            for j in range(8):
+                Z = (Z + Xm[:, j:j + 1] * B32[j:j + 1, :]).astype(np.float32)
+            Y = np.zeros((4, 8), np.float32)
+            for i in range(4):
+                Y = (Y + A32[i:i + 1, :].T * Z[i:i + 1, :]).astype(np.float32)
+            err = np.abs(Y.reshape(32).astype(np.float64) - y[m, 32 * b:32 * b + 32])
+            assert np.all(err <= tau[m, 32 * b:32 * b + 32])
+
+
+def test_tie_classifier_catches_planted_errors():
+    """A code flipped far from any boundary is an error; a float32 rounding of a value on
+    a boundary is a tie."""
+    rng = np.random.default_rng(19)
+    y = rng.standard_normal((4, 64)) * 3
+    tau = np.full(y.shape, 1e-6)
+    codes, sb, e = mxfp4.quantize_blocks(y)
+    rep = ties.classify_mxfp4(codes, sb, y, tau)
+    assert rep["errors"] == [] and rep["code_mismatch"] == 0
+    bad = codes.copy()
+    bad[1, 5] ^= 0x3            # flip magnitude bits: not a rounding neighbour
+    rep = ties.classify_mxfp4(bad, sb, y, tau)
+    assert len(rep["errors"]) == 1
+    # a value exactly on a boundary, and a "kernel" that picked the other side of it
+    y2 = np.zeros((1, 32))
+    y2[0, 0], y2[0, 1], y2[0, 2] = 4.0, 1.25, -2.5          # block max 4 -> e = 0
+    c2, s2, e2 = mxfp4.quantize_blocks(y2)
+    assert int(e2[0, 0]) == 0 and c2[0, 1] == 2 and c2[0, 2] == 12
+    alt = c2.copy()
+    alt[0, 1] = 3              # 1.5 instead of the even 1.0
+    alt[0, 2] = 13             # -3 instead of the even -2
+    rep = ties.classify_mxfp4(alt, s2, y2, np.full(y2.shape, 1e-9))
+    assert rep["errors"] == [] and rep["code_ties"] == 2
+    rep = ties.classify_mxfp4(alt, s2, y2, np.zeros(y2.shape))   # no error budget: not a tie
+    assert len(rep["errors"]) == 2
+    bad_scale = sb.copy()
+    bad_scale[0, 0] += 3
+    rep = ties.classify_mxfp4(codes, bad_scale, y, tau)
+    assert any(err[0] == "scale" for err in rep["errors"])
+
+
+def test_mean_tie_rule():
+    x = np.array([1.0, np.float16(1.0) + np.float16(2.0 ** -10)], dtype=np.float16)
+    exact = float(np.mean(x.astype(np.float64)))     # the fp16 midpoint of 1 and 1+2^-10
+    lo, hi = np.float16(1.0), np.float16(1.0 + 2.0 ** -10)
+    assert exact == 0.5 * (float(lo) + float(hi))
+    assert ties.mean_tie(x, lo, hi, 2)
+    assert not ties.mean_tie(x, np.float16(2.0), hi, 2)
