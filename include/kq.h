@@ -1,0 +1,165 @@
+/*
+ * kq — the online 4-bit activation path of a quantized diffusion-transformer linear
+ * layer, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The method (from the pages this library implements):
+ *   - KroQuant (Kronecker-Structured Block Transforms for Efficient Post-Training
+ *     Quantization of Diffusion Transformers), §01: Y = (XP)(P^-1 W) — an invertible
+ *     transform P applied to the activations online, its inverse folded into the
+ *     weights offline; §02: P = A (x) B (A 4x4, B 8x8) on every 32-element block of
+ *     the activation vector; §03: 4-bit MXFP4 target format.
+ *   - OrbitQuant (Data-Free Quantization for Image and Video DiTs), §03:
+ *     RPBH(X) = X.P.H.D (random permutation, block Hadamard, random signs), the
+ *     inverse folded offline as W' = R^-1 W, one Lloyd-Max codebook for all
+ *     rotated coordinates.
+ *   - CentriQ (Calibration-Free Quantization of DiTs via Exact Mean Centering),
+ *     arXiv abstract: centre each token before the rotation, restore the mean
+ *     exactly through a rank-1 full-precision branch; closed-form per-token scale.
+ *   - SVDQuant explainer, §3: a 16-bit low-rank branch L1 L2 added to the 4-bit
+ *     product, fused into the 4-bit kernel so it costs no separate pass.
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   X     fp16 [M][K]           activations, K a multiple of 32
+ *   codes u8   [M][K/2]         two 4-bit codes per byte, element 2i in bits 0-3
+ *   MXFP4 scales u8 [M][K/32]   E8M0 bytes (e + 127), one per 32 consecutive values
+ *   LM4 scales  f32 [M]         per-token scale
+ *   mu    fp16 [M]              per-token mean (centring)
+ *   W     fp16 [N][K]           weights in the [out][in] layout (row n = column n of
+ *                               the W in Y = XW)
+ *   wcodes u8 [N][K/2] (MXFP4) or [N][K/4] (2-bit, element 4i in bits 0-1)
+ *   wscales u8 [N][K/32] (MXFP4) or fp16 [N][K/32] (2-bit group scales)
+ *   wbar  fp16 [N]              column sums of W (rank-1 mean restore)
+ *   L1    fp16 [r][K], L2 fp16 [N][r]   low-rank factors, [out][in] layout
+ *   Y     fp16 [M][N]
+ *
+ * Ownership: the caller allocates and owns every buffer; the library never
+ * allocates, frees or caches device memory, and holds no per-call state (it is
+ * re-entrant).  Descriptor contents (kind, K, A, B) travel by value; perm/sign are
+ * caller-owned device arrays.  Every call is asynchronous on `stream` (0 = the
+ * null stream); inputs must stay alive until the stream has passed the call.
+ *
+ * Errors: the return value is a status.  Arguments are validated on the host
+ * before anything is launched; a non-zero status means nothing was enqueued
+ * (KQ_ERR_HIP: the launch itself failed, reported by hipGetLastError).  Faults
+ * inside kernels surface at the caller's next synchronisation, as HIP defines.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KQ_ABI_VERSION 1
+
+typedef int32_t kq_status;
+enum {
+  KQ_OK = 0,
+  KQ_ERR_NULL = 1,         /* a required pointer is NULL */
+  KQ_ERR_SHAPE = 2,        /* M, N < 1; K % 32 != 0; descriptor K != K; bad rank; mu without wbar */
+  KQ_ERR_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
+  KQ_ERR_UNSUPPORTED = 4,  /* unknown enum, or a size outside the supported range */
+  KQ_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kq_w4a4_linear_workspace_bytes */
+  KQ_ERR_VALUE = 6,        /* a transform factor is singular or not finite */
+  KQ_ERR_HIP = 7           /* a HIP launch failed */
+};
+
+/* transform kinds */
+enum { KQ_XFORM_NONE = 0, KQ_XFORM_KRON_4X8 = 1, KQ_XFORM_RPBH_32 = 2 };
+/* formats */
+enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
+
+/* One layer's block transform.
+ * KRON_4X8 (KroQuant §02): every 32-element block x_b of a token is replaced by
+ *   x_b . (A (x) B), i.e. with Xm[i][j] = x_b[8i+j]: Ym = A^T Xm B, y_b[8k+l] = Ym[k][l].
+ *   A (4x4) and B (8x8) are row-major floats, one pair shared by all blocks.
+ * RPBH_32 (OrbitQuant §03): y = x . Pi . blockdiag(H32) . D / sqrt(32) with
+ *   (x.Pi)_j = x[perm[j]] over all K, H32 the Sylvester Hadamard matrix
+ *   (H[i][j] = (-1)^popcount(i&j)), D = diag(sign), sign[j] in {-1, +1}.
+ *   perm (int32 [K], a permutation of 0..K-1) and sign (int8 [K]) are device arrays.
+ * NONE: identity. */
+typedef struct kq_xform {
+  int32_t kind;
+  int32_t reserved;          /* must be 0 */
+  int64_t K;                 /* must equal the K of the call */
+  float A[16];
+  float B[64];
+  const int32_t* perm;
+  const int8_t* sign;
+} kq_xform;
+
+/* KQ_ABI_VERSION of the built library. */
+int32_t kq_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kq_status_str(kq_status s);
+
+/* Positive levels (ascending) of the symmetric n-level Lloyd-Max quantizer for a
+ * unit Gaussian (OrbitQuant §03: one fixed codebook), as the library computes and
+ * uses them; n = 4 or 16.  Host memory, n/2 doubles.  Runs on the host only. */
+kq_status kq_lloyd_max_levels(int32_t n, double* levels_out);
+
+/* Online activation path (KroQuant §01-§03; OrbitQuant §03; CentriQ abstract):
+ *   [centre]  mu_t = fp16(mean_k X[t,k]) (float32 sum), x <- x - mu_t      if center
+ *   transform y = x . P  (xf->kind)
+ *   quantize  fmt MXFP4: per 32-block a = max|y|, e = max(floor(log2 a) - 2, -127),
+ *                        scale byte e + 127, code = E2M1 round-to-nearest-even of
+ *                        y 2^-e, saturating at 6, sign bit = (y < 0); packed.
+ *             fmt LM4_TOKEN: s_t = sqrt(mean_k y^2) (float32), code = sign-magnitude
+ *                        index of y / s_t in the 16-level Lloyd-Max codebook
+ *                        (a value on a threshold takes the smaller magnitude).
+ * X fp16 [M][K]; codes u8 [M][K/2]; scales u8 [M][K/32] (MXFP4) or f32 [M] (LM4);
+ * mu fp16 [M], required iff center != 0 (else ignored).
+ * K % 32 == 0; K <= 32768 when centring or LM4 is used, K <= 16384 for RPBH (the row is
+ * staged on chip).
+ * All device pointers 16-byte aligned except mu and scales (4-byte for LM4). */
+kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
+                                const void* X, int64_t M, int64_t K,
+                                uint8_t* codes, void* scales, void* mu,
+                                hipStream_t stream);
+
+/* Offline fold (KroQuant §01; OrbitQuant §03 W' = R^-1 W; CentriQ abstract):
+ *   W' = P^-1 W (KRON: blockdiag(A^-1 (x) B^-1), the inverses computed on the host in
+ *   double precision; RPBH: R^T), computed in float32 on the device, then each
+ *   row n of W'^T quantized along K: fmt MXFP4 with the activation rule, or
+ *   LM2_G32: s_g = fp16(RMS of the 32-group), 2-bit sign-magnitude code of w / s_g in
+ *   the 4-level Lloyd-Max codebook.  wbar[n] = fp16(sum_k W[n][k]) if wbar != NULL.
+ * W fp16 [N][K]; wcodes u8 [N][K/2] (MXFP4) or [N][K/4] (LM2); wscales u8 [N][K/32]
+ * (MXFP4) or fp16 [N][K/32] (LM2).  Returns KQ_ERR_VALUE if A or B is singular. */
+kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt,
+                                       const void* W, int64_t N, int64_t K,
+                                       uint8_t* wcodes, void* wscales, void* wbar,
+                                       hipStream_t stream);
+
+/* Bytes of device workspace kq_w4a4_linear needs: M * r * 2 (the low-rank
+ * intermediate T = X L1^T, held in fp16) rounded up to 256; 0 when r == 0. */
+size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r);
+
+/* The 4-bit linear with its full-precision branches:
+ *   Y = Xq . Wq^T  +  (X L1^T) L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
+ * fmt MXFP4: Xq, Wq MXFP4 (xscales u8 [M][K/32], wscales u8 [N][K/32]); products on
+ *   the scaled-FP4 matrix cores, each block pair scaled by 2^(ex+ew).  K % 128 == 0.
+ * fmt LM2_G32 (W2A4): Xq per-token Lloyd-Max 4-bit (xscales f32 [M]), Wq 2-bit groups
+ *   (wcodes u8 [N][K/4], wscales fp16 [N][K/32]); the codebooks are the library's own
+ *   (kq_lloyd_max_levels).  K % 32 == 0.  No low-rank or rank-1 branch (r must be 0).
+ * Low-rank branch (SVDQuant §3): r in {0, 16, 32, 64}; X fp16 [M][K] is the original
+ *   (uncentred, untransformed) activation; T = X L1^T is formed in fp32 and held as
+ *   fp16 in `workspace`; T L2^T is added in the fp32 accumulator before the store.
+ * Rank-1 restore (CentriQ): mu fp16 [M] and wbar fp16 [N], both or neither.
+ * Y fp16 [M][N]. */
+kq_status kq_w4a4_linear(int32_t fmt,
+                         const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                         const uint8_t* wcodes, const void* wscales, int64_t N,
+                         const void* X, const void* L1, const void* L2, int32_t r,
+                         const void* mu, const void* wbar,
+                         void* Y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

@@ -1,0 +1,75 @@
+"""Shared helpers of the GPU parity tests: error bounds of the kernels' float32
+arithmetic (used to classify ties), and running the oracle on the same inputs."""
+
+import numpy as np
+
+from oracle import mxfp4, pipeline, ties, transforms
+
+U = 2.0 ** -24
+
+# Forward-error operation counts of the kernels' float32 arithmetic per output element:
+#  Kronecker: an 8-term FMA chain (x B) feeding a 4-term chain (A^T .), plus the rounding
+#             of the folded inverse factors to float32 in the weight fold;
+#  RPBH: five butterfly stages, the rounded 1/sqrt(32) and the final product;
+#  centring adds one rounding (x - mu in float32).
+N_OPS = {"kron": 13, "rpbh": 8, "none": 1}
+
+
+def abs_transform(x_abs, xform):
+    """sum_i |x_i| |P_ik| (the quantity the float32 error bound scales with)."""
+    kind = xform["kind"]
+    if kind == "kron":
+        P = np.abs(transforms.kron_block_matrix(xform["A"], xform["B"]))
+        return transforms.apply_block_matrix(x_abs, P)
+    if kind == "rpbh":
+        u = x_abs[:, np.asarray(xform["perm"], dtype=np.int64)]
+        return transforms.apply_block_matrix(u, np.abs(transforms.hadamard32())) / np.sqrt(32.0)
+    return x_abs
+
+
+def tau_for(x_c, xform, center):
+    n = N_OPS[xform["kind"]] + (1 if center else 0)
+    return ties.gamma_tau(n, abs_transform(np.abs(x_c), xform))
+
+
+def oracle_activation_reference(X16, xform, center, mu_gpu=None):
+    """Exact transformed values y (float64) and the error bound tau, using the kernel's mean
+    where it differs from the oracle's only by a rounding tie."""
+    X = X16.astype(np.float64)
+    mu = None
+    if center:
+        mu = pipeline.token_mean_f16(X16)
+        if mu_gpu is not None:
+            mu = mu_gpu.copy()
+        xc = pipeline.centre(X, mu)
+    else:
+        xc = X
+    y = pipeline.apply_transform(xc, xform)
+    return y, tau_for(xc, xform, center), mu
+
+
+def check_mu(X16, mu_gpu):
+    """fp16 means: equal to the oracle's, or an adjacent rounding at a tie.  Returns the
+    number of ties; raises on any other difference."""
+    ref = pipeline.token_mean_f16(X16)
+    diff = np.flatnonzero(ref.view(np.uint16) != mu_gpu.view(np.uint16))
+    K = X16.shape[1]
+    for m in diff:
+        n_terms = K + 16
+        assert ties.mean_tie(X16[m], mu_gpu[m], ref[m], n_terms), (m, float(mu_gpu[m]), float(ref[m]))
+    return len(diff)
+
+
+def assert_mx_parity(codes_gpu_packed, scales_gpu, y, tau, max_frac=1e-4, label=""):
+    codes = mxfp4.unpack_nibbles(codes_gpu_packed)
+    rep = ties.classify_mxfp4(codes, scales_gpu, y, tau)
+    frac = rep["code_mismatch"] / rep["codes"]
+    msg = (f"{label}: code mismatches {rep['code_mismatch']}/{rep['codes']} (ties {rep['code_ties']}), "
+           f"scale mismatches {rep['scale_mismatch']} (ties {rep['scale_ties']}), errors {rep['errors'][:5]}")
+    print(msg)
+    for t in rep["ties"][:10]:
+        print("  tie", t)
+    assert not rep["errors"], msg
+    assert frac <= max_frac, msg
+    assert rep["scale_mismatch"] / rep["blocks"] <= max_frac, msg
+    return rep

@@ -1,0 +1,141 @@
+"""The C-ABI library: loads, exports every symbol include/kq.h declares, and rejects bad
+arguments on the host before anything is launched (no GPU needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import w4a4_post_quantization_amd as kq
+from oracle import lloyd_max
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kq.lib_path()):
+        pytest.fail("libkq.so is not built (run python -m w4a4_post_quantization_amd.build)")
+    return kq.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"kq_transform_quantize", "kq_w4a4_linear", "kq_fold_inverse_into_weights"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kq.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kq_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert kq.abi_version() == 1
+    for s in range(0, 8):
+        assert kq.status_str(s).startswith("KQ_")
+    assert "UNKNOWN" in kq.status_str(99)
+
+
+def test_library_codebook_matches_oracle(lib):
+    """The library's own Lloyd-Max solver (C++) and the oracle's (SciPy) agree."""
+    for n, ref in ((16, lloyd_max.LEVELS16), (4, lloyd_max.LEVELS4)):
+        got = np.array(kq.lloyd_max_levels(n))
+        assert np.max(np.abs(got - ref)) <= 1e-12
+    with pytest.raises(kq.KQError):
+        kq.lloyd_max_levels(8)
+
+
+def _xf(kind=1, K=64):
+    x = kq._XformC()
+    x.kind, x.reserved, x.K = kind, 0, K
+    for i in range(4):
+        x.A[5 * i] = 1.0
+    for i in range(8):
+        x.B[9 * i] = 1.0
+    return x
+
+
+FAKE = ctypes.c_void_p(0x100000)       # 16-byte aligned, never dereferenced on error paths
+FAKE_ODD = ctypes.c_void_p(0x100008)
+
+
+def test_transform_quantize_validation(lib):
+    f = lib.kq_transform_quantize
+    xf = _xf()
+    assert f(ctypes.byref(xf), 0, 0, None, 4, 64, FAKE, FAKE, None, None) == 1          # NULL X
+    assert f(None, 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 1                      # NULL xform
+    assert f(ctypes.byref(xf), 0, 1, FAKE, 4, 64, FAKE, FAKE, None, None) == 1          # centre without mu
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 0, 64, FAKE, FAKE, None, None) == 2          # M < 1
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 48, FAKE, FAKE, None, None) == 2          # K % 32
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 96, FAKE, FAKE, None, None) == 2          # descriptor K
+    assert f(ctypes.byref(xf), 7, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # bad fmt
+    assert f(ctypes.byref(xf), 0, 0, FAKE_ODD, 4, 64, FAKE, FAKE, None, None) == 3      # alignment
+    bad = _xf(kind=9)
+    assert f(ctypes.byref(bad), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4         # bad kind
+    rp = _xf(kind=2)
+    assert f(ctypes.byref(rp), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 1          # RPBH without perm
+    nan = _xf()
+    nan.A[0] = float("nan")
+    assert f(ctypes.byref(nan), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 6         # non-finite factor
+    big = _xf(kind=2, K=65536 + 32)
+    big.perm, big.sign = 0x100000, 0x100000
+    assert f(ctypes.byref(big), 0, 0, FAKE, 4, 65536 + 32, FAKE, FAKE, None, None) == 4  # row too long
+
+
+def test_fold_validation(lib):
+    f = lib.kq_fold_inverse_into_weights
+    xf = _xf()
+    assert f(ctypes.byref(xf), 0, None, 8, 64, FAKE, FAKE, None, None) == 1
+    assert f(ctypes.byref(xf), 1, FAKE, 8, 64, FAKE, FAKE, None, None) == 4             # LM4 is not a weight format
+    sing = _xf()
+    for i in range(16):
+        sing.A[i] = 0.0
+    assert f(ctypes.byref(sing), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 6           # singular A
+    rank1 = _xf()
+    for i in range(8):
+        for j in range(8):
+            rank1.B[8 * i + j] = float(i + 1)                                           # rank-1 B
+    assert f(ctypes.byref(rank1), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 6
+
+
+def test_linear_validation(lib):
+    f = lib.kq_w4a4_linear
+    ws = lib.kq_w4a4_linear_workspace_bytes
+    assert ws(100, 32) == ((100 * 32 * 2 + 255) // 256) * 256 and ws(100, 0) == 0
+    args = dict(fmt=0, xc=FAKE, xs=FAKE, M=16, K=256, wc=FAKE, wsc=FAKE, N=32, X=None, L1=None, L2=None, r=0,
+                mu=None, wbar=None, Y=FAKE, w=None, wb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["X"], a["L1"], a["L2"],
+                 a["r"], a["mu"], a["wbar"], a["Y"], a["w"], a["wb"], None)
+    assert call(Y=None) == 1
+    assert call(N=0) == 2
+    assert call(r=24) == 2
+    assert call(mu=FAKE) == 2                          # mu without wbar
+    assert call(K=96) == 4                             # MXFP4 needs K % 128
+    assert call(N=40) == 4                             # N % 16
+    assert call(fmt=5) == 4
+    assert call(r=32) == 1                             # low rank without X/L1/L2
+    assert call(r=32, X=FAKE, L1=FAKE, L2=FAKE) == 5   # no workspace
+    assert call(r=32, X=FAKE, L1=FAKE, L2=FAKE, w=FAKE, wb=16) == 5
+    assert call(fmt=2, r=32, X=FAKE, L1=FAKE, L2=FAKE, w=FAKE, wb=1 << 20) == 4   # W2A4 has no low-rank branch
+    assert call(xc=FAKE_ODD) == 3
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        kq.transform_quantize(X, kq.Xform.none(64))

@@ -1,0 +1,192 @@
+"""GPU parity of the offline fold and of the 4-bit linear (W4A4 + low-rank + rank-1, and
+W2A4) against the oracle.
+
+The fold's codes follow the same tie rule as the activations.  The linear is checked on
+the kernel's own packed operands (so code ties cannot leak into it): the oracle
+dequantizes them in float64 and adds the branches exactly; the fp16 result must be within
+2e-3 relative Frobenius error.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import linear, lloyd_max, mxfp4, pipeline, ties
+from tests import gpu_util
+from tests.test_gpu_transform import _dev_xform
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _fold(kq, W16, xf, fmt):
+    import torch
+    W = torch.from_numpy(W16).cuda()
+    dxf = _dev_xform(kq, torch, xf, W16.shape[1])
+    wc, ws, wbar = kq.fold_inverse_into_weights(W, dxf, fmt=fmt)
+    torch.cuda.synchronize()
+    return wc, ws, wbar
+
+
+def _wbar_check(W16, wbar_gpu):
+    ref = pipeline.column_sums_f16(W16)
+    exact = W16.astype(np.float64).sum(axis=1)
+    bad = np.flatnonzero(ref.view(np.uint16) != wbar_gpu.view(np.uint16))
+    for n in bad:   # only adjacent fp16 roundings of a sum within float32 error of their midpoint
+        a, b = float(ref[n]), float(wbar_gpu[n])
+        mid = 0.5 * (a + b)
+        bound = float(ties.gamma_tau(64 + W16.shape[1] // 64, np.sum(np.abs(W16[n].astype(np.float64)))))
+        assert abs(exact[n] - mid) <= bound and np.nextafter(np.float16(min(a, b)), np.float16(np.inf)) == max(a, b)
+
+
+@pytest.mark.parametrize("cfg,layer,nrows", [(0, 0, 1152), (1, 1, 200), (3, 2, 96), (4, 0, 160), (1, 3, 80)])
+def test_fold_mxfp4_matches_oracle(kq, cfg, layer, nrows):
+    c = synth.CONFIGS[cfg]
+    _, K, N = c["layers"][layer]
+    W16, _, _ = synth.weights(K, N, cfg, layer, 0)
+    W16 = np.ascontiguousarray(W16[:nrows])
+    xf = synth.xform_for(cfg, layer, K)
+    wc, ws, wbar = _fold(kq, W16, xf, "mxfp4")
+    wt = pipeline.inverse_fold(W16, xf)
+    if xf["kind"] == "kron":
+        # w'_b = P^-1 w_b, so the bound scales with sum_k |P^-1[j][k]| |w_k| = (|w| |P^-T|)_j
+        inv_t = {"kind": "kron", "A": np.linalg.inv(xf["A"].astype(np.float64)).T,
+                 "B": np.linalg.inv(xf["B"].astype(np.float64)).T}
+        tau = gpu_util.tau_for(W16.astype(np.float64), inv_t, False)
+    else:
+        tau = gpu_util.tau_for(W16.astype(np.float64), xf, False)     # W'^T = W^T R
+    gpu_util.assert_mx_parity(wc.cpu().numpy(), ws.cpu().numpy(), wt, tau, label=f"fold cfg{cfg} layer{layer}")
+    _wbar_check(W16, wbar.cpu().numpy())
+
+
+def test_fold_w2_matches_oracle(kq):
+    c = synth.CONFIGS[2]
+    _, K, N = c["layers"][0]
+    W16, _, _ = synth.weights(K, N, 2, 0, 0)
+    W16 = np.ascontiguousarray(W16[:200])
+    xf = synth.xform_for(2, 0, K)
+    wc, ws, _ = _fold(kq, W16, xf, "lm2")
+    codes = lloyd_max.unpack_2bit(wc.cpu().numpy())
+    s_gpu = ws.cpu().numpy()
+    wt = pipeline.inverse_fold(W16, xf)
+    ref_codes, ref_s = lloyd_max.w2_group_quantize(wt)
+    tau = gpu_util.tau_for(W16.astype(np.float64), xf, False).reshape(wt.shape)
+    # group scales: fp16 of the RMS; differences only at fp16 rounding ties
+    g = wt.reshape(wt.shape[0], -1, 32)
+    rms = np.sqrt(np.mean(g * g, axis=2))
+    ds = np.argwhere(s_gpu.view(np.uint16) != ref_s.view(np.uint16))
+    for (n, b) in ds:
+        a, bb = float(s_gpu[n, b]), float(ref_s[n, b])
+        assert abs(rms[n, b] - 0.5 * (a + bb)) <= 1e-5 * rms[n, b]
+    assert len(ds) <= 2
+    thr = lloyd_max.thresholds(lloyd_max.LEVELS4)[0]
+    s_used = np.repeat(s_gpu.astype(np.float64), 32, axis=1)
+    mism = np.argwhere(codes != lloyd_max.sign_magnitude_encode(
+        np.where(s_used > 0, wt / np.where(s_used > 0, s_used, 1), 0), np.array([thr])))
+    for (n, k) in mism:
+        v = abs(wt[n, k]) / s_used[n, k]
+        assert abs(v - thr) <= (tau[n, k] / s_used[n, k]) + 4 * gpu_util.U * thr, (n, k, v)
+    assert len(mism) / codes.size <= 1e-4
+
+
+def _linear_case(kq, cfg, layer, M, N=None, rank=None, with_mu=None, K=None, seed_shift=0):
+    import torch
+    c = synth.CONFIGS[cfg]
+    _, K0, N0 = c["layers"][layer]
+    K = K0 if K is None else K
+    N = N0 if N is None else N
+    r = c["rank"] if rank is None else rank
+    center = c["center"] if with_mu is None else with_mu
+    X16 = synth.activations(M, K, cfg + seed_shift, c["sigma_mu"], c["frames"])
+    W16, L1, L2 = synth.weights(K, N, cfg + seed_shift, layer, max(r, 1))
+    if r == 0:
+        L1 = L2 = None
+    else:
+        L1, L2 = L1[:r], np.ascontiguousarray(L2[:, :r])
+    xf = synth.xform_for(cfg, layer, K) if K == K0 else {"kind": "kron", "A": synth.kron_factors(cfg, layer)[0],
+                                                          "B": synth.kron_factors(cfg, layer)[1]}
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, mu = kq.transform_quantize(X, dxf, fmt="mxfp4", center=center)
+    wc, ws, wbar = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    L1d = None if L1 is None else torch.from_numpy(np.ascontiguousarray(L1)).cuda()
+    L2d = None if L2 is None else torch.from_numpy(L2).cuda()
+    Y = kq.w4a4_linear(xc, xs, wc, ws, X=X if r else None, L1=L1d, L2=L2d, mu=mu, wbar=wbar if center else None)
+    torch.cuda.synchronize()
+    return dict(X16=X16, W16=W16, L1=L1, L2=L2, xc=xc.cpu().numpy(), xs=xs.cpu().numpy(), wc=wc.cpu().numpy(),
+                ws=ws.cpu().numpy(), mu=None if mu is None else mu.cpu().numpy(),
+                wbar=None if not center else wbar.cpu().numpy(), Y=Y.cpu().numpy(), xf=xf)
+
+
+def _ref_Y(d, rows=None, cols=None):
+    return linear.w4a4_linear(d["xc"], d["xs"], d["wc"], d["ws"], d["X16"] if d["L1"] is not None else None,
+                              d["L1"], d["L2"], d["mu"], d["wbar"], rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("cfg,layer,M", [(0, 0, 256), (1, 0, 200), (1, 3, 130), (3, 0, 150), (3, 2, 70), (4, 1, 97)])
+def test_w4a4_linear_matches_oracle(kq, cfg, layer, M):
+    d = _linear_case(kq, cfg, layer, M)
+    ref = _ref_Y(d)
+    err = linear.rel_frobenius(d["Y"], ref)
+    print(f"cfg{cfg} layer{layer} M={M}: rel frobenius {err:.3e}")
+    assert err <= TOL
+    # elementwise sanity: no element off by more than a few fp16 ulps of the output scale
+    scale = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(d["Y"].astype(np.float64) - ref)) <= 0.02 * scale + 1e-3 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("rank,with_mu", [(0, False), (16, False), (64, True), (32, True)])
+def test_w4a4_branch_variants(kq, rank, with_mu):
+    d = _linear_case(kq, 1, 1, 77, rank=rank, with_mu=with_mu)
+    err = linear.rel_frobenius(d["Y"], _ref_Y(d))
+    print(f"rank {rank} mu {with_mu}: {err:.3e}")
+    assert err <= TOL
+
+
+def test_w4a4_small_shapes(kq):
+    """One k-step (K = 128), one row, N a multiple of 16 but not of the tile."""
+    for M, N, K in ((1, 16, 128), (5, 48, 128), (33, 144, 256), (130, 272, 384)):
+        d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=32, with_mu=True)
+        err = linear.rel_frobenius(d["Y"], _ref_Y(d))
+        print(f"M={M} N={N} K={K}: {err:.3e}")
+        assert err <= TOL
+
+
+def test_w4a4_end_to_end_quality_informational(kq):
+    """Not graded: the full path vs the unquantized product, with and without the transform."""
+    d = _linear_case(kq, 3, 0, 128)
+    exact = d["X16"].astype(np.float64) @ d["W16"].astype(np.float64).T + \
+        (d["X16"].astype(np.float64) @ d["L1"].astype(np.float64).T) @ d["L2"].astype(np.float64).T
+    print("end-to-end rel error (centred RPBH, MXFP4):", linear.rel_frobenius(d["Y"], exact))
+
+
+def test_w2a4_linear_matches_oracle(kq):
+    import torch
+    c = synth.CONFIGS[2]
+    for layer, M, Nr in ((0, 130, 480), (2, 64, 2240)):
+        _, K, N = c["layers"][layer]
+        X16 = synth.activations(M, K, 2, c["sigma_mu"])
+        W16, _, _ = synth.weights(K, N, 2, layer, 0)
+        W16 = np.ascontiguousarray(W16[:Nr])
+        xf = synth.xform_for(2, layer, K)
+        dxf = _dev_xform(kq, torch, xf, K)
+        xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
+        wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+        Y = kq.w4a4_linear(xc, xs, wc, ws, fmt="lm2")
+        torch.cuda.synchronize()
+        ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy())
+        err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+        print(f"W2A4 layer{layer} M={M} N={Nr} K={K}: {err:.3e}")
+        assert err <= TOL
+
+
+def test_w4a4_full_size_sampled(kq):
+    """FLUX-like qkv at full size (M = 4608, K = 3072, N = 9216) in the bench's launch
+    configuration; oracle on sampled rows and all columns."""
+    d = _linear_case(kq, 3, 0, 4608)
+    rows = np.arange(5, 4608, 151)
+    ref = _ref_Y(d, rows=rows)
+    err = linear.rel_frobenius(d["Y"][rows], ref)
+    print(f"full-size sampled rel frobenius {err:.3e}")
+    assert err <= TOL

@@ -1,0 +1,152 @@
+"""GPU parity of the online activation path (transform + quantize) against the oracle.
+
+Codes and E8M0 scales must match the float64 oracle except at logged float32 rounding
+ties (mismatch fraction <= 1e-4, zero non-tie mismatches); fp16 means must match except
+at rounding ties; per-token Lloyd-Max scales within their float32 error bound.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import lloyd_max, mxfp4, pipeline, ties
+from tests import gpu_util
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_xform(kq, torch, xf, K):
+    if xf["kind"] == "kron":
+        return kq.Xform.kron(xf["A"], xf["B"], K)
+    if xf["kind"] == "rpbh":
+        return kq.Xform.rpbh(torch.from_numpy(np.ascontiguousarray(xf["perm"], dtype=np.int32)).cuda(),
+                             torch.from_numpy(np.ascontiguousarray(xf["sign"], dtype=np.int8)).cuda())
+    return kq.Xform.none(K)
+
+
+def _run(kq, X16, xf, fmt, center):
+    import torch
+    X = torch.from_numpy(X16).cuda()
+    dxf = _dev_xform(kq, torch, xf, X16.shape[1])
+    codes, scales, mu = kq.transform_quantize(X, dxf, fmt=fmt, center=center)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), None if mu is None else mu.cpu().numpy()
+
+
+def _mx_check(kq, X16, xf, center, label):
+    codes, scales, mu = _run(kq, X16, xf, "mxfp4", center)
+    if center:
+        gpu_util.check_mu(X16, mu)
+    y, tau, _ = gpu_util.oracle_activation_reference(X16, xf, center, mu_gpu=mu)
+    return gpu_util.assert_mx_parity(codes, scales, y, tau, label=label)
+
+
+# (config, layer, rows): rows chosen to span several waves/tiles with a ragged tail
+CASES = [(0, 0, 256), (1, 0, 301), (1, 3, 97), (3, 0, 203), (3, 2, 67), (4, 0, 333), (4, 1, 129)]
+
+
+@pytest.mark.parametrize("cfg,layer,rows", CASES)
+def test_mxfp4_codes_match_oracle(kq, cfg, layer, rows):
+    c = synth.CONFIGS[cfg]
+    _, K, _ = c["layers"][layer]
+    X16 = synth.activations(rows, K, cfg, c["sigma_mu"], c["frames"])
+    xf = synth.xform_for(cfg, layer, K)
+    _mx_check(kq, X16, xf, c["center"], f"cfg{cfg} layer{layer} M={rows} K={K}")
+
+
+@pytest.mark.parametrize("kind,center", [("kron", True), ("rpbh", False), ("none", False), ("none", True)])
+def test_mxfp4_other_combinations(kq, kind, center):
+    K, rows = 1152, 150
+    X16 = synth.activations(rows, K, 11, 3.0)
+    if kind == "kron":
+        A, B = synth.kron_factors(11, 0)
+        xf = {"kind": "kron", "A": A, "B": B}
+    elif kind == "rpbh":
+        perm, sign = synth.rpbh_params(K, 11, 0)
+        xf = {"kind": "rpbh", "perm": perm, "sign": sign}
+    else:
+        xf = {"kind": "none"}
+    _mx_check(kq, X16, xf, center, f"{kind} center={center}")
+
+
+def test_edge_rows(kq):
+    """Zero rows, constant rows (centred: all zero), a single row, tiny and huge values."""
+    K = 256
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((9, K)).astype(np.float16)
+    X[0] = 0
+    X[1] = np.float16(3.25)                 # constant token
+    X[2] = np.float16(-0.0)
+    X[3, :] = np.float16(6e-8)               # fp16 subnormals
+    X[4] *= np.float16(1000)
+    X[5, ::2] = 0
+    perm, sign = synth.rpbh_params(K, 1, 0)
+    A, B = synth.kron_factors(1, 0)
+    for xf in ({"kind": "rpbh", "perm": perm, "sign": sign}, {"kind": "kron", "A": A, "B": B}):
+        for center in (False, True):
+            rep = _mx_check(kq, X, xf, center, f"edge {xf['kind']} center={center}")
+            assert rep["code_mismatch"] == 0
+    codes, scales, _ = _run(kq, X[:1], {"kind": "kron", "A": A, "B": B}, "mxfp4", False)
+    assert np.all(codes == 0) and np.all(scales == 0)
+    codes, scales, mu = _run(kq, X[1:2], {"kind": "rpbh", "perm": perm, "sign": sign}, "mxfp4", True)
+    assert float(mu[0]) == 3.25 and np.all(codes == 0) and np.all(scales == 0)
+
+
+def test_single_row_and_ragged_block_count(kq):
+    """M*K/32 not a multiple of 16 blocks (streaming kernel's ragged last chunk)."""
+    A, B = synth.kron_factors(2, 0)
+    xf = {"kind": "kron", "A": A, "B": B}
+    for rows, K in ((1, 32), (1, 96), (3, 160), (7, 1152)):
+        X16 = synth.activations(rows, K, 2, 2.0)
+        rep = _mx_check(kq, X16, xf, False, f"ragged M={rows} K={K}")
+        assert rep["code_mismatch"] <= 1
+
+
+def _lm4_check(kq, X16, xf, label):
+    codes_p, s_gpu, _ = _run(kq, X16, xf, "lm4", False)
+    y, tau, _ = gpu_util.oracle_activation_reference(X16, xf, False)
+    codes = mxfp4.unpack_nibbles(codes_p)
+    # relative error bound of the kernel's scale: the float32 sum of squares (per-thread
+    # chains of <= 32 terms, a 6-level wave tree, <= 16 wave partials), plus the effect
+    # of the transformed values' own error, the division and the square root
+    ss = np.sum(y * y, axis=1)
+    s_rel = (gamma := 60 * gpu_util.U) + np.max(np.sum(2 * np.abs(y) * tau, axis=1) / np.maximum(ss, 1e-300)) + 4 * gpu_util.U
+    rep = ties.classify_lm4(codes, s_gpu, y, tau, s_rel)
+    msg = f"{label}: mismatches {rep['code_mismatch']}/{rep['codes']} ties {rep['code_ties']} errors {rep['errors'][:5]}"
+    print(msg)
+    assert not rep["errors"], msg
+    assert rep["code_mismatch"] / rep["codes"] <= 1e-4, msg
+    return rep
+
+
+@pytest.mark.parametrize("layer,rows", [(0, 190), (2, 75)])
+def test_lm4_codes_match_oracle(kq, layer, rows):
+    c = synth.CONFIGS[2]
+    _, K, _ = c["layers"][layer]
+    X16 = synth.activations(rows, K, 2, c["sigma_mu"])
+    _lm4_check(kq, X16, synth.xform_for(2, layer, K), f"cfg2 layer{layer} M={rows} K={K}")
+
+
+def test_lm4_zero_row(kq):
+    K = 2240
+    X16 = synth.activations(4, K, 2, 2.0)
+    X16[2] = 0
+    codes, s, _ = _run(kq, X16, synth.xform_for(2, 0, K), "lm4", False)
+    assert s[2] == 0 and np.all(codes[2] == 0)
+
+
+@pytest.mark.parametrize("cfg,layer", [(3, 0), (4, 0)])
+def test_full_size_sampled_rows(kq, cfg, layer):
+    """Full workload size in the launch configuration of the bench; parity on sampled rows
+    (rows are independent)."""
+    c = synth.CONFIGS[cfg]
+    _, K, _ = c["layers"][layer]
+    X16 = synth.activations(c["M"], K, cfg, c["sigma_mu"], c["frames"])
+    xf = synth.xform_for(cfg, layer, K)
+    codes, scales, mu = _run(kq, X16, xf, "mxfp4", c["center"])
+    rows = np.unique(np.concatenate([np.arange(0, c["M"], 97), [c["M"] - 1]]))
+    Xs = X16[rows]
+    if c["center"]:
+        gpu_util.check_mu(Xs, mu[rows])
+    y, tau, _ = gpu_util.oracle_activation_reference(Xs, xf, c["center"], mu_gpu=None if mu is None else mu[rows])
+    gpu_util.assert_mx_parity(codes[rows], scales[rows], y, tau, label=f"cfg{cfg} full M={c['M']} sampled {len(rows)}")

@@ -1,0 +1,264 @@
+"""Python binding of libkq (the MI355X HIP library for the online 4-bit activation path).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+Tensors are torch tensors on the ROCm device (PyTorch provides device memory and the
+stream); outputs are allocated here when not given.  The binding fails loudly if the
+library is missing: there is no fallback.
+
+    xf = kq.Xform.kron(A, B, K)                     # or Xform.rpbh(perm, sign), Xform.none(K)
+    codes, scales, mu = kq.transform_quantize(X, xf, fmt="mxfp4", center=False)
+    wcodes, wscales, wbar = kq.fold_inverse_into_weights(W, xf, fmt="mxfp4")
+    Y = kq.w4a4_linear(codes, scales, wcodes, wscales, X=X, L1=L1, L2=L2, mu=mu, wbar=wbar)
+"""
+
+import ctypes
+import os
+
+__all__ = ["load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
+           "transform_quantize", "fold_inverse_into_weights", "w4a4_linear",
+           "linear_workspace_bytes", "KQError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+KQ_OK = 0
+XFORM_NONE, XFORM_KRON, XFORM_RPBH = 0, 1, 2
+FMT_MXFP4, FMT_LM4, FMT_LM2 = 0, 1, 2
+_FMT = {"mxfp4": FMT_MXFP4, "lm4": FMT_LM4, "lm2": FMT_LM2}
+
+
+class KQError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {status_str(status)}")
+        self.status = status
+
+
+class _XformC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("K", ctypes.c_int64),
+                ("A", ctypes.c_float * 16), ("B", ctypes.c_float * 64),
+                ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p)]
+
+
+def lib_path():
+    return os.path.join(_HERE, "libkq.so")
+
+
+def load():
+    """Load libkq.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m w4a4_post_quantization_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kq_abi_version.restype = i32
+    lib.kq_abi_version.argtypes = []
+    lib.kq_status_str.restype = ctypes.c_char_p
+    lib.kq_status_str.argtypes = [i32]
+    lib.kq_lloyd_max_levels.restype = i32
+    lib.kq_lloyd_max_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_double)]
+    lib.kq_transform_quantize.restype = i32
+    lib.kq_transform_quantize.argtypes = [ctypes.POINTER(_XformC), i32, i32, vp, i64, i64, vp, vp, vp, vp]
+    lib.kq_fold_inverse_into_weights.restype = i32
+    lib.kq_fold_inverse_into_weights.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp]
+    lib.kq_w4a4_linear_workspace_bytes.restype = sz
+    lib.kq_w4a4_linear_workspace_bytes.argtypes = [i64, i32]
+    lib.kq_w4a4_linear.restype = i32
+    lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    _LIB = lib
+    return lib
+
+
+def abi_version():
+    return int(load().kq_abi_version())
+
+
+def status_str(s):
+    return load().kq_status_str(int(s)).decode()
+
+
+def lloyd_max_levels(n):
+    """Positive levels of the library's n-level (4 or 16) Lloyd-Max codebook (host call)."""
+    out = (ctypes.c_double * (n // 2))()
+    s = load().kq_lloyd_max_levels(n, out)
+    if s != KQ_OK:
+        raise KQError(s, "kq_lloyd_max_levels")
+    return [float(v) for v in out]
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+class Xform:
+    """One layer's block transform descriptor (KRON_4X8, RPBH_32 or NONE)."""
+
+    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None):
+        self.kind, self.K = kind, int(K)
+        self._c = _XformC()
+        self._c.kind, self._c.reserved, self._c.K = kind, 0, self.K
+        if kind == XFORM_KRON:
+            a = [float(v) for v in _flat(A)]
+            b = [float(v) for v in _flat(B)]
+            if len(a) != 16 or len(b) != 64:
+                raise ValueError("A must be 4x4 and B 8x8")
+            self._c.A[:] = a
+            self._c.B[:] = b
+        self.perm, self.sign = perm, sign      # keep the device arrays alive
+        if kind == XFORM_RPBH:
+            torch = _torch()
+            _check(perm, "perm", torch.int32, (self.K,))
+            _check(sign, "sign", torch.int8, (self.K,))
+            self._c.perm, self._c.sign = perm.data_ptr(), sign.data_ptr()
+
+    @classmethod
+    def kron(cls, A, B, K):
+        return cls(XFORM_KRON, K, A=A, B=B)
+
+    @classmethod
+    def rpbh(cls, perm, sign):
+        return cls(XFORM_RPBH, perm.shape[0], perm=perm, sign=sign)
+
+    @classmethod
+    def none(cls, K):
+        return cls(XFORM_NONE, K)
+
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def _flat(a):
+    try:
+        import numpy as np
+        return np.asarray(a, dtype=np.float32).reshape(-1).tolist()
+    except Exception:
+        return list(a)
+
+
+def transform_quantize(X, xform, fmt="mxfp4", center=False, codes=None, scales=None, mu=None, stream=None):
+    """[centre] -> block transform -> 4-bit quantize + pack.  Returns (codes, scales, mu)."""
+    torch = _torch()
+    _check(X, "X", torch.float16)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M, K]")
+    M, K = X.shape
+    f = _FMT[fmt]
+    if f not in (FMT_MXFP4, FMT_LM4):
+        raise ValueError("fmt must be 'mxfp4' or 'lm4'")
+    dev = X.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    _check(codes, "codes", torch.uint8, (M, K // 2))
+    if f == FMT_MXFP4:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+        _check(scales, "scales", torch.uint8, (M, K // 32))
+    else:
+        scales = torch.empty((M,), dtype=torch.float32, device=dev) if scales is None else scales
+        _check(scales, "scales", torch.float32, (M,))
+    if center:
+        mu = torch.empty((M,), dtype=torch.float16, device=dev) if mu is None else mu
+        _check(mu, "mu", torch.float16, (M,))
+    else:
+        mu = None
+    s = load().kq_transform_quantize(xform.c(), f, int(bool(center)), _ptr(X), M, K, _ptr(codes), _ptr(scales),
+                                     _ptr(mu), _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_transform_quantize")
+    return codes, scales, mu
+
+
+def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None):
+    """Offline: W' = P^-1 W, quantized along K.  W is fp16 [N][K] ([out][in]).
+    Returns (wcodes, wscales, wbar or None)."""
+    torch = _torch()
+    _check(W, "W", torch.float16)
+    N, K = W.shape
+    f = _FMT[fmt]
+    dev = W.device
+    if f == FMT_MXFP4:
+        wcodes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        wscales = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    elif f == FMT_LM2:
+        wcodes = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+        wscales = torch.empty((N, K // 32), dtype=torch.float16, device=dev)
+    else:
+        raise ValueError("fmt must be 'mxfp4' or 'lm2'")
+    wbar = torch.empty((N,), dtype=torch.float16, device=dev) if with_wbar else None
+    s = load().kq_fold_inverse_into_weights(xform.c(), f, _ptr(W), N, K, _ptr(wcodes), _ptr(wscales), _ptr(wbar),
+                                            _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_fold_inverse_into_weights")
+    return wcodes, wscales, wbar
+
+
+def linear_workspace_bytes(M, r):
+    return int(load().kq_w4a4_linear_workspace_bytes(int(M), int(r)))
+
+
+def w4a4_linear(xcodes, xscales, wcodes, wscales, X=None, L1=None, L2=None, mu=None, wbar=None,
+                fmt="mxfp4", Y=None, workspace=None, stream=None):
+    """Y = Xq Wq^T + (X L1^T) L2^T + mu wbar^T (fp16 [M][N]).  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4)."""
+    torch = _torch()
+    f = _FMT[fmt]
+    _check(xcodes, "xcodes", torch.uint8)
+    M = xcodes.shape[0]
+    K = xcodes.shape[1] * 2
+    N = wcodes.shape[0]
+    _check(wcodes, "wcodes", torch.uint8, (N, K // 2) if f == FMT_MXFP4 else (N, K // 4))
+    if f == FMT_MXFP4:
+        _check(xscales, "xscales", torch.uint8, (M, K // 32))
+        _check(wscales, "wscales", torch.uint8, (N, K // 32))
+    else:
+        _check(xscales, "xscales", torch.float32, (M,))
+        _check(wscales, "wscales", torch.float16, (N, K // 32))
+    r = 0
+    if L1 is not None:
+        r = L1.shape[0]
+        _check(X, "X", torch.float16, (M, K))
+        _check(L1, "L1", torch.float16, (r, K))
+        _check(L2, "L2", torch.float16, (N, r))
+    if mu is not None:
+        _check(mu, "mu", torch.float16, (M,))
+        _check(wbar, "wbar", torch.float16, (N,))
+    dev = xcodes.device
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev) if Y is None else Y
+    _check(Y, "Y", torch.float16, (M, N))
+    need = linear_workspace_bytes(M, r)
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = load().kq_w4a4_linear(f, _ptr(xcodes), _ptr(xscales), M, K, _ptr(wcodes), _ptr(wscales), N,
+                              _ptr(X if r else None), _ptr(L1), _ptr(L2), r, _ptr(mu), _ptr(wbar), _ptr(Y),
+                              _ptr(workspace), wsb, _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_w4a4_linear")
+    return Y

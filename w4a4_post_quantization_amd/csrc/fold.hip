@@ -1,0 +1,136 @@
+// Offline weight preparation: W' = P^-1 W folded into the weights and quantized along K
+// (KroQuant §01: Y = (XP)(P^-1 W); OrbitQuant §03: W' = R^-1 W, R^-1 = R^T), plus the
+// column sums wbar = 1^T W used by CentriQ's rank-1 mean restore.  Runs once per
+// layer, outside the timed path; written for clarity, one thread per 32-element block.
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+
+namespace kq {
+
+#define KQ_INV_SQRT32_F 0.17677669529663688110f
+
+// One thread: row n of W^T (= column n of W), block b (32 consecutive k).
+// KIND 1: w'_b = (Ai (x) Bi) w_b, i.e. W'm = Ai Wm Bi^T with Wm[k][l] = w_b[8k+l].
+// KIND 2: w' = w R (the forward RPBH of the row, since W'^T = W^T R).
+// FMT 0: MXFP4 (16 code bytes + 1 E8M0 byte); FMT 2: 2-bit Lloyd-Max + fp16 group scale.
+template <int KIND, int FMT>
+__global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, KronFactors fi,
+                                                   const int32_t* __restrict__ perm, const int8_t* __restrict__ sign,
+                                                   float t4, uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
+  const int64_t nb = K >> 5;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= N * nb) return;
+  const int64_t n = id / nb, b = id % nb;
+  const __half* wr = W + n * K;
+  float w[32], y[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int64_t k = 32 * b + i;
+    w[i] = __half2float(wr[KIND == 2 ? (int64_t)perm[k] : k]);
+  }
+  if (KIND == 1) {
+    float z[32];  // Z = Wm Bi^T : Z[k][j] = sum_l Wm[k][l] Bi[j][l]
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int l = 0; l < 8; ++l) acc = __builtin_fmaf(w[8 * k + l], fi.B[8 * j + l], acc);
+        z[8 * k + j] = acc;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(fi.A[4 * i + k], z[8 * k + j], acc);
+        y[8 * i + j] = acc;
+      }
+  } else if (KIND == 2) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (!(i & h)) { const float a = w[i], c = w[i + h]; w[i] = a + c; w[i + h] = a - c; }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float d = sign[32 * b + i] < 0 ? -KQ_INV_SQRT32_F : KQ_INV_SQRT32_F;
+      y[i] = __builtin_fmaf(w[i], d, 0.0f);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = w[i] + 0.0f;
+  }
+
+  if (FMT == 0) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(y[i]));
+    const uint32_t sb = e8m0_byte(a);
+    const float sc = e8m0_as_cvt_scale(sb);
+    uint4 out;
+    out.x = cvt8_fp4(y + 0, sc);
+    out.y = cvt8_fp4(y + 8, sc);
+    out.z = cvt8_fp4(y + 16, sc);
+    out.w = cvt8_fp4(y + 24, sc);
+    reinterpret_cast<uint4*>(wcodes + n * (K >> 1))[b] = out;
+    reinterpret_cast<uint8_t*>(wscales)[n * nb + b] = (uint8_t)sb;
+  } else {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss = __builtin_fmaf(y[i], y[i], ss);
+    const __half sh = __float2half_rn(sqrtf(ss / 32.0f));
+    const float s = __half2float(sh);
+    const float thr = t4 * s;
+    uint32_t lo = 0, hi = 0;
+    if (s > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t c = (fabsf(y[i]) > thr ? 1u : 0u) | (y[i] < 0.0f ? 2u : 0u);
+        if (i < 16) lo |= c << (2 * i);
+        else hi |= c << (2 * (i - 16));
+      }
+    }
+    reinterpret_cast<uint2*>(wcodes + n * (K >> 2))[b] = make_uint2(lo, hi);
+    reinterpret_cast<__half*>(wscales)[n * nb + b] = sh;
+  }
+}
+
+// wbar[n] = fp16(sum_k W[n][k]); one wavefront per row n.
+__global__ __launch_bounds__(256) void colsum_kernel(const __half* __restrict__ W, int64_t N, int64_t K,
+                                                     __half* __restrict__ wbar) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= N) return;
+  float acc = 0.0f;
+  for (int64_t k = lane; k < K; k += 64) acc += __half2float(W[n * K + k]);
+  acc = wave_sum(acc);
+  if (lane == 0) wbar[n] = __float2half_rn(acc);
+}
+
+template <int KIND>
+static void fold_fmt(int fmt, dim3 g, dim3 b, hipStream_t s, const __half* W, int64_t N, int64_t K,
+                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, float t4, uint8_t* wc, void* ws) {
+  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, t4, wc, ws);
+  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, t4, wc, ws);
+}
+
+hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
+                       const int32_t* perm, const int8_t* sign, uint8_t* wcodes, void* wscales, hipStream_t s) {
+  const int64_t total = N * (K / 32);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const float t4 = lm_tables().t4;
+  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
+  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
+  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, wbar);
+  return hipGetLastError();
+}
+
+}  // namespace kq

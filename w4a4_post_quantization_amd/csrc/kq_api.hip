@@ -1,0 +1,240 @@
+// C ABI of libkq: host-side argument validation and dispatch to the kernels.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "kq.h"
+#include "kq_launch.hpp"
+
+namespace kq {
+
+// ---- Lloyd-Max codebooks (OrbitQuant §03: one fixed codebook for the rotated,
+// approximately Gaussian coordinates).  Symmetric n-level quantizer for N(0, 1): Lloyd's
+// fixed point, levels = conditional means of their cells, thresholds = midpoints.
+static double npdf(double t) { return std::exp(-0.5 * t * t) * 0.39894228040143267794; }
+// P(a < Z < b) for 0 <= a < b <= inf, through erfc so the upper tail keeps its accuracy
+static double nmass(double a, double b) {
+  const double ua = 0.5 * std::erfc(a * 0.70710678118654752440);
+  const double ub = std::isinf(b) ? 0.0 : 0.5 * std::erfc(b * 0.70710678118654752440);
+  return ua - ub;
+}
+
+bool lloyd_max_levels(int n, double* out) {
+  if (n != 4 && n != 16) return false;
+  const int h = n / 2;
+  double lv[8], nx[8];
+  for (int i = 0; i < h; ++i) lv[i] = 3.0 * (i + 0.5) / h;  // any increasing start converges
+  for (int it = 0; it < 200000; ++it) {
+    double diff = 0.0;
+    for (int i = 0; i < h; ++i) {
+      const double lo = i == 0 ? 0.0 : 0.5 * (lv[i - 1] + lv[i]);
+      const double hi = i == h - 1 ? INFINITY : 0.5 * (lv[i] + lv[i + 1]);
+      const double num = npdf(lo) - (std::isinf(hi) ? 0.0 : npdf(hi));
+      nx[i] = num / nmass(lo, hi);
+      diff = std::fmax(diff, std::fabs(nx[i] - lv[i]));
+    }
+    for (int i = 0; i < h; ++i) lv[i] = nx[i];
+    if (diff <= 1e-15) break;
+  }
+  for (int i = 0; i < h; ++i) out[i] = lv[i];
+  return true;
+}
+
+const LmTables& lm_tables() {
+  static LmTables t;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    double l16[8], l4[2];
+    lloyd_max_levels(16, l16);
+    lloyd_max_levels(4, l4);
+    for (int i = 0; i < 8; ++i) t.l16[i] = (float)l16[i];
+    for (int i = 0; i < 7; ++i) t.t16[i] = (float)(0.5 * (l16[i] + l16[i + 1]));
+    t.l4[0] = (float)l4[0];
+    t.l4[1] = (float)l4[1];
+    t.t4 = (float)(0.5 * (l4[0] + l4[1]));
+  });
+  return t;
+}
+
+// inverse of a small row-major matrix by Gauss-Jordan with partial pivoting (double)
+static bool invert(const float* a, int n, float* out) {
+  double m[8][16];
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < 2 * n; ++j) m[i][j] = j < n ? (double)a[i * n + j] : (j - n == i ? 1.0 : 0.0);
+  double scale = 0.0;
+  for (int i = 0; i < n * n; ++i) {
+    if (!std::isfinite(a[i])) return false;
+    scale = std::fmax(scale, std::fabs((double)a[i]));
+  }
+  if (scale == 0.0) return false;
+  for (int c = 0; c < n; ++c) {
+    int p = c;
+    for (int i = c + 1; i < n; ++i)
+      if (std::fabs(m[i][c]) > std::fabs(m[p][c])) p = i;
+    if (std::fabs(m[p][c]) <= 1e-12 * scale) return false;
+    if (p != c)
+      for (int j = 0; j < 2 * n; ++j) std::swap(m[p][j], m[c][j]);
+    const double d = m[c][c];
+    for (int j = 0; j < 2 * n; ++j) m[c][j] /= d;
+    for (int i = 0; i < n; ++i) {
+      if (i == c) continue;
+      const double f = m[i][c];
+      if (f != 0.0)
+        for (int j = 0; j < 2 * n; ++j) m[i][j] -= f * m[c][j];
+    }
+  }
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) out[i * n + j] = (float)m[i][n + j];
+  return true;
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static kq_status hip_status(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
+
+static kq_status check_xform(const kq_xform* xf, int64_t K) {
+  if (!xf) return KQ_ERR_NULL;
+  if (xf->kind < KQ_XFORM_NONE || xf->kind > KQ_XFORM_RPBH_32 || xf->reserved != 0) return KQ_ERR_UNSUPPORTED;
+  if (xf->K != K) return KQ_ERR_SHAPE;
+  if (xf->kind == KQ_XFORM_RPBH_32) {
+    if (!xf->perm || !xf->sign) return KQ_ERR_NULL;
+    if (!aligned(xf->perm, 16)) return KQ_ERR_ALIGN;
+  }
+  if (xf->kind == KQ_XFORM_KRON_4X8) {
+    for (int i = 0; i < 16; ++i)
+      if (!std::isfinite(xf->A[i])) return KQ_ERR_VALUE;
+    for (int i = 0; i < 64; ++i)
+      if (!std::isfinite(xf->B[i])) return KQ_ERR_VALUE;
+  }
+  return KQ_OK;
+}
+
+extern "C" {
+
+int32_t kq_abi_version(void) { return KQ_ABI_VERSION; }
+
+const char* kq_status_str(kq_status s) {
+  switch (s) {
+    case KQ_OK: return "KQ_OK";
+    case KQ_ERR_NULL: return "KQ_ERR_NULL: a required pointer is NULL";
+    case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE: invalid shape (M, N >= 1, K % 32 == 0, descriptor K, rank)";
+    case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN: a device pointer is not suitably aligned";
+    case KQ_ERR_UNSUPPORTED: return "KQ_ERR_UNSUPPORTED: unknown enum or size outside the supported range";
+    case KQ_ERR_WORKSPACE: return "KQ_ERR_WORKSPACE: workspace missing or too small";
+    case KQ_ERR_VALUE: return "KQ_ERR_VALUE: transform factor singular or not finite";
+    case KQ_ERR_HIP: return "KQ_ERR_HIP: a HIP launch failed";
+    default: return "KQ_ERR_UNKNOWN: unknown status code";
+  }
+}
+
+kq_status kq_lloyd_max_levels(int32_t n, double* levels_out) {
+  if (!levels_out) return KQ_ERR_NULL;
+  return lloyd_max_levels(n, levels_out) ? KQ_OK : KQ_ERR_UNSUPPORTED;
+}
+
+kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center, const void* X, int64_t M,
+                                int64_t K, uint8_t* codes, void* scales, void* mu, hipStream_t stream) {
+  if (!X || !codes || !scales) return KQ_ERR_NULL;
+  if (center && !mu) return KQ_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (fmt != KQ_FMT_MXFP4 && fmt != KQ_FMT_LM4_TOKEN) return KQ_ERR_UNSUPPORTED;
+  kq_status st = check_xform(xf, K);
+  if (st != KQ_OK) return st;
+  if (!aligned(X, 16) || !aligned(codes, 16)) return KQ_ERR_ALIGN;
+  if (fmt == KQ_FMT_LM4_TOKEN && !aligned(scales, 4)) return KQ_ERR_ALIGN;
+  if (center && !aligned(mu, 2)) return KQ_ERR_ALIGN;
+  KronFactors f;
+  std::memcpy(f.A, xf->A, sizeof f.A);
+  std::memcpy(f.B, xf->B, sizeof f.B);
+  const bool row_path = center || fmt != KQ_FMT_MXFP4 || xf->kind != KQ_XFORM_KRON_4X8;
+  if (row_path && K > 32768) return KQ_ERR_UNSUPPORTED;
+  if (xf->kind == KQ_XFORM_RPBH_32 && K > 16384) return KQ_ERR_UNSUPPORTED;  // row staged in 32 KiB of LDS
+  hipError_t e;
+  if (!row_path) {
+    e = launch_kron_mx_stream(static_cast<const __half*>(X), M * (K / 32), f, codes,
+                              static_cast<uint8_t*>(scales), stream);
+  } else {
+    e = launch_row_quant(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 1, center != 0, static_cast<const __half*>(X), M, K, f,
+                         xf->perm, xf->sign, codes, scales, static_cast<__half*>(mu), stream);
+  }
+  return hip_status(e);
+}
+
+kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const void* W, int64_t N, int64_t K,
+                                       uint8_t* wcodes, void* wscales, void* wbar, hipStream_t stream) {
+  if (!W || !wcodes || !wscales) return KQ_ERR_NULL;
+  if (N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (fmt != KQ_FMT_MXFP4 && fmt != KQ_FMT_LM2_G32) return KQ_ERR_UNSUPPORTED;
+  kq_status st = check_xform(xf, K);
+  if (st != KQ_OK) return st;
+  if (!aligned(W, 16) || !aligned(wcodes, 16)) return KQ_ERR_ALIGN;
+  if (fmt == KQ_FMT_LM2_G32 && !aligned(wscales, 2)) return KQ_ERR_ALIGN;
+  if (wbar && !aligned(wbar, 2)) return KQ_ERR_ALIGN;
+  KronFactors finv;
+  std::memset(&finv, 0, sizeof finv);
+  if (xf->kind == KQ_XFORM_KRON_4X8) {
+    if (!invert(xf->A, 4, finv.A) || !invert(xf->B, 8, finv.B)) return KQ_ERR_VALUE;
+  }
+  hipError_t e = launch_fold(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 2, static_cast<const __half*>(W), N, K, finv,
+                             xf->perm, xf->sign, wcodes, wscales, stream);
+  if (e != hipSuccess) return KQ_ERR_HIP;
+  if (wbar) e = launch_colsum(static_cast<const __half*>(W), N, K, static_cast<__half*>(wbar), stream);
+  return hip_status(e);
+}
+
+size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r) {
+  if (M < 1 || r <= 0) return 0;
+  const size_t b = (size_t)M * (size_t)r * 2;
+  return (b + 255) & ~(size_t)255;
+}
+
+kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                         const uint8_t* wcodes, const void* wscales, int64_t N, const void* X, const void* L1,
+                         const void* L2, int32_t r, const void* mu, const void* wbar, void* Y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!xcodes || !xscales || !wcodes || !wscales || !Y) return KQ_ERR_NULL;
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (r != 0 && r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if ((mu == nullptr) != (wbar == nullptr)) return KQ_ERR_SHAPE;
+  if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return KQ_ERR_UNSUPPORTED;
+  if (N % 16 != 0) return KQ_ERR_UNSUPPORTED;
+  if (fmt == KQ_FMT_MXFP4) {
+    if (K % 128 != 0) return KQ_ERR_UNSUPPORTED;
+  } else if (fmt == KQ_FMT_LM2_G32) {
+    if (r != 0 || mu) return KQ_ERR_UNSUPPORTED;
+  } else {
+    return KQ_ERR_UNSUPPORTED;
+  }
+  if (r > 0) {
+    if (!X || !L1 || !L2) return KQ_ERR_NULL;
+    if (!workspace) return KQ_ERR_WORKSPACE;
+    if (workspace_bytes < kq_w4a4_linear_workspace_bytes(M, r)) return KQ_ERR_WORKSPACE;
+    if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(L2, 16) || !aligned(workspace, 16)) return KQ_ERR_ALIGN;
+  }
+  if (!aligned(xcodes, 16) || !aligned(wcodes, 16) || !aligned(Y, 16)) return KQ_ERR_ALIGN;
+  if (!aligned(xscales, 4) || !aligned(wscales, 4)) return KQ_ERR_ALIGN;
+  if (mu && (!aligned(mu, 2) || !aligned(wbar, 2))) return KQ_ERR_ALIGN;
+  hipError_t e;
+  if (fmt == KQ_FMT_MXFP4) {
+    __half* T = nullptr;
+    if (r > 0) {
+      T = static_cast<__half*>(workspace);
+      e = launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r, T, stream);
+      if (e != hipSuccess) return KQ_ERR_HIP;
+    }
+    e = launch_w4a4_gemm(xcodes, static_cast<const uint8_t*>(xscales), M, K, wcodes,
+                         static_cast<const uint8_t*>(wscales), N, T, static_cast<const __half*>(L2), r,
+                         static_cast<const __half*>(mu), static_cast<const __half*>(wbar), static_cast<__half*>(Y),
+                         stream);
+  } else {
+    e = launch_w2a4_gemm(xcodes, static_cast<const float*>(xscales), M, K, wcodes,
+                         static_cast<const __half*>(wscales), N, static_cast<__half*>(Y), stream);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

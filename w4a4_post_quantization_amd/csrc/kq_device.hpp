@@ -1,0 +1,80 @@
+// Device-side helpers shared by the kq kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kq {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// DPP quad_perm control word: lane i of each quad reads lane sel[i] of the same quad.
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Value of lane I of this lane's quad.
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) { return dpp_f<quad_perm(I, I, I, I)>(v); }
+
+// Value of the lane whose quad index differs in bit 0 / bit 1.
+__device__ __forceinline__ float quad_xor1(float v) { return dpp_f<quad_perm(1, 0, 3, 2)>(v); }
+__device__ __forceinline__ float quad_xor2(float v) { return dpp_f<quad_perm(2, 3, 0, 1)>(v); }
+
+// Max over the four lanes of a quad (every lane gets the result).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, quad_xor1(v));
+  return fmaxf(v, quad_xor2(v));
+}
+
+// E8M0 shared-scale byte of a block from its largest magnitude a >= 0 (OCP MX rule):
+// e = floor(log2 a) - 2 clamped below at -127, stored as e + 127.  For a normal float
+// floor(log2 a) is its exponent field minus 127; a zero or subnormal a (exponent field
+// 0, i.e. a < 2^-126) gives e < -127, which clamps to byte 0.
+__device__ __forceinline__ uint32_t e8m0_byte(float a) {
+  uint32_t ef = (__float_as_uint(a) >> 23) & 0xFFu;
+  return ef > 2u ? ef - 2u : 0u;
+}
+
+// The conversion scale 2^e as the float whose exponent field is the E8M0 byte.  The
+// gfx950 packed FP4 conversion divides by 2^(exponent field - 127) and ignores the
+// mantissa; exponent field 0 stands for 2^-127.
+__device__ __forceinline__ float e8m0_as_cvt_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// Eight fp32 values -> eight E2M1 codes (round to nearest even, saturating at 6),
+// element 2i in the low nibble of byte i.  Inputs must not be -0.0 (the hardware keeps
+// the sign of a negative zero; the format contract maps exact zeros to code 0).
+__device__ __forceinline__ uint32_t cvt8_fp4(const float* y, float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
+  return w;
+}
+
+__device__ __forceinline__ void unpack8_f16(const uint4& raw, float* x) {
+  const __half2* h = reinterpret_cast<const __half2*>(&raw);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float2 f = __half22float2(h[i]);
+    x[2 * i] = f.x;
+    x[2 * i + 1] = f.y;
+  }
+}
+
+// Sum over a wavefront (every lane gets the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace kq

@@ -1,0 +1,60 @@
+// Host-side launchers of the kq kernels (internal to the library; the C ABI in kq.h
+// validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kq {
+
+struct KronFactors {
+  float A[16];  // row-major 4x4
+  float B[64];  // row-major 8x8
+};
+
+// Lloyd-Max codebooks for a unit Gaussian, as float32 for the kernels.
+struct LmTables {
+  float t16[7];   // positive thresholds of the 16-level quantizer (ascending)
+  float l16[8];   // positive levels of the 16-level quantizer
+  float t4;       // positive threshold of the 4-level quantizer
+  float l4[2];    // positive levels of the 4-level quantizer
+};
+const LmTables& lm_tables();
+bool lloyd_max_levels(int n, double* out);
+
+// Kronecker transform + MXFP4 for a flat array of nblocks 32-element fp16 blocks.
+hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFactors& f,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+// Row-staged transform + quantize: any transform, optional centring, MXFP4 or LM4.
+// kind: 0 none, 1 kron, 2 rpbh; fmt: 0 MXFP4, 1 LM4.
+hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int64_t M, int64_t K,
+                            const KronFactors& f, const int32_t* perm, const int8_t* sign,
+                            uint8_t* codes, void* scales, __half* mu, hipStream_t s);
+
+// Offline fold: W'^T rows = inverse transform of W^T rows, quantized along K.
+// fmt: 0 MXFP4, 2 LM2.  f holds the INVERSE factors for kind 1.
+hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
+                       const int32_t* perm, const int8_t* sign, uint8_t* wcodes, void* wscales,
+                       hipStream_t s);
+hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
+
+// T[M][r] = fp16(X L1^T), fp32 accumulation.
+hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r,
+                               __half* T, hipStream_t s);
+
+// Y = Xq Wq^T (+ T L2^T) (+ mu wbar^T), MXFP4 x MXFP4.
+hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,
+                            const uint8_t* wcodes, const uint8_t* wscales, int64_t N,
+                            const __half* T, const __half* L2, int r, const __half* mu,
+                            const __half* wbar, __half* Y, hipStream_t s);
+
+// Y = (s_t l16[qx]) (s_g l4[qw])^T, per-token Lloyd-Max activations x 2-bit weights.
+hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t M, int64_t K,
+                            const uint8_t* wcodes, const __half* wscales, int64_t N, __half* Y,
+                            hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace kq
