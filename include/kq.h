@@ -63,9 +63,8 @@ enum {
   KQ_ERR_SHAPE = 2,        /* M, N < 1; K % 32 != 0; descriptor K != K; bad rank; mu without wbar */
   KQ_ERR_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
   KQ_ERR_UNSUPPORTED = 4,  /* unknown enum, or a size outside the supported range */
-  KQ_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than kq_w4a4_linear_workspace_bytes */
-  KQ_ERR_VALUE = 6,        /* a transform factor is singular or not finite */
-  KQ_ERR_HIP = 7           /* a HIP launch failed */
+  KQ_ERR_VALUE = 5,        /* a transform factor is singular or not finite */
+  KQ_ERR_HIP = 6           /* a HIP launch failed */
 };
 
 /* transform kinds */
@@ -135,29 +134,31 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt,
                                        uint8_t* wcodes, void* wscales, void* wbar,
                                        hipStream_t stream);
 
-/* Bytes of device workspace kq_w4a4_linear needs: M * r * 2 (the low-rank
- * intermediate T = X L1^T, held in fp16) rounded up to 256; 0 when r == 0. */
-size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r);
+/* Low-rank down-projection of the 16-bit branch (SVDQuant explainer §3):
+ *   T = fp16(X L1^T), fp32 accumulation on the fp16 matrix cores.
+ * X fp16 [M][K] (the original activations: not centred, not transformed), L1 fp16 [r][K],
+ * T fp16 [M][r] (caller-owned).  r in {16, 32, 64}; K % 32 == 0.  One kernel. */
+kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r,
+                          void* T, hipStream_t stream);
 
-/* The 4-bit linear with its full-precision branches:
- *   Y = Xq . Wq^T  +  (X L1^T) L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
+/* The 4-bit linear with its full-precision branches, one kernel:
+ *   Y = Xq . Wq^T  +  T L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
  * fmt MXFP4: Xq, Wq MXFP4 (xscales u8 [M][K/32], wscales u8 [N][K/32]); products on
  *   the scaled-FP4 matrix cores, each block pair scaled by 2^(ex+ew).  K % 128 == 0.
  * fmt LM2_G32 (W2A4): Xq per-token Lloyd-Max 4-bit (xscales f32 [M]), Wq 2-bit groups
  *   (wcodes u8 [N][K/4], wscales fp16 [N][K/32]); the codebooks are the library's own
  *   (kq_lloyd_max_levels).  K % 32 == 0.  No low-rank or rank-1 branch (r must be 0).
- * Low-rank branch (SVDQuant §3): r in {0, 16, 32, 64}; X fp16 [M][K] is the original
- *   (uncentred, untransformed) activation; T = X L1^T is formed in fp32 and held as
- *   fp16 in `workspace`; T L2^T is added in the fp32 accumulator before the store.
+ * Low-rank branch (SVDQuant §3): T fp16 [M][r] from kq_lowrank_down, L2 fp16 [N][r],
+ *   r in {0, 16, 32, 64} (0: T and L2 ignored); T L2^T enters the fp32 accumulators
+ *   before the 4-bit product, so the branch costs no extra pass over Y.
  * Rank-1 restore (CentriQ): mu fp16 [M] and wbar fp16 [N], both or neither.
- * Y fp16 [M][N]. */
+ * N % 16 == 0.  Y fp16 [M][N]. */
 kq_status kq_w4a4_linear(int32_t fmt,
                          const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
                          const uint8_t* wcodes, const void* wscales, int64_t N,
-                         const void* X, const void* L1, const void* L2, int32_t r,
+                         const void* T, const void* L2, int32_t r,
                          const void* mu, const void* wbar,
-                         void* Y, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         void* Y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

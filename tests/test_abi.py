@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert kq.abi_version() == 1
-    for s in range(0, 8):
+    for s in range(0, 7):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
 
@@ -87,7 +87,7 @@ def test_transform_quantize_validation(lib):
     assert f(ctypes.byref(rp), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 1          # RPBH without perm
     nan = _xf()
     nan.A[0] = float("nan")
-    assert f(ctypes.byref(nan), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 6         # non-finite factor
+    assert f(ctypes.byref(nan), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 5         # non-finite factor
     big = _xf(kind=2, K=65536 + 32)
     big.perm, big.sign = 0x100000, 0x100000
     assert f(ctypes.byref(big), 0, 0, FAKE, 4, 65536 + 32, FAKE, FAKE, None, None) == 4  # row too long
@@ -101,25 +101,23 @@ def test_fold_validation(lib):
     sing = _xf()
     for i in range(16):
         sing.A[i] = 0.0
-    assert f(ctypes.byref(sing), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 6           # singular A
+    assert f(ctypes.byref(sing), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 5           # singular A
     rank1 = _xf()
     for i in range(8):
         for j in range(8):
             rank1.B[8 * i + j] = float(i + 1)                                           # rank-1 B
-    assert f(ctypes.byref(rank1), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 6
+    assert f(ctypes.byref(rank1), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 5
 
 
 def test_linear_validation(lib):
     f = lib.kq_w4a4_linear
-    ws = lib.kq_w4a4_linear_workspace_bytes
-    assert ws(100, 32) == ((100 * 32 * 2 + 255) // 256) * 256 and ws(100, 0) == 0
-    args = dict(fmt=0, xc=FAKE, xs=FAKE, M=16, K=256, wc=FAKE, wsc=FAKE, N=32, X=None, L1=None, L2=None, r=0,
-                mu=None, wbar=None, Y=FAKE, w=None, wb=0)
+    args = dict(fmt=0, xc=FAKE, xs=FAKE, M=16, K=256, wc=FAKE, wsc=FAKE, N=32, T=None, L2=None, r=0,
+                mu=None, wbar=None, Y=FAKE)
 
     def call(**kw):
         a = dict(args, **kw)
-        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["X"], a["L1"], a["L2"],
-                 a["r"], a["mu"], a["wbar"], a["Y"], a["w"], a["wb"], None)
+        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["T"], a["L2"],
+                 a["r"], a["mu"], a["wbar"], a["Y"], None)
     assert call(Y=None) == 1
     assert call(N=0) == 2
     assert call(r=24) == 2
@@ -127,11 +125,19 @@ def test_linear_validation(lib):
     assert call(K=96) == 4                             # MXFP4 needs K % 128
     assert call(N=40) == 4                             # N % 16
     assert call(fmt=5) == 4
-    assert call(r=32) == 1                             # low rank without X/L1/L2
-    assert call(r=32, X=FAKE, L1=FAKE, L2=FAKE) == 5   # no workspace
-    assert call(r=32, X=FAKE, L1=FAKE, L2=FAKE, w=FAKE, wb=16) == 5
-    assert call(fmt=2, r=32, X=FAKE, L1=FAKE, L2=FAKE, w=FAKE, wb=1 << 20) == 4   # W2A4 has no low-rank branch
+    assert call(r=32) == 1                             # low rank without T/L2
+    assert call(fmt=2, r=32, T=FAKE, L2=FAKE) == 4     # W2A4 has no low-rank branch
     assert call(xc=FAKE_ODD) == 3
+    assert call(r=32, T=FAKE_ODD, L2=FAKE) == 3
+
+
+def test_lowrank_validation(lib):
+    f = lib.kq_lowrank_down
+    assert f(None, FAKE, 4, 64, 32, FAKE, None) == 1
+    assert f(FAKE, FAKE, 4, 48, 32, FAKE, None) == 2
+    assert f(FAKE, FAKE, 4, 64, 8, FAKE, None) == 2
+    assert f(FAKE, FAKE, 0, 64, 32, FAKE, None) == 2
+    assert f(FAKE, FAKE_ODD, 4, 64, 32, FAKE, None) == 3
 
 
 def test_binding_rejects_cpu_tensors():

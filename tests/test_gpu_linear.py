@@ -112,11 +112,13 @@ def _linear_case(kq, cfg, layer, M, N=None, rank=None, with_mu=None, K=None, see
     wc, ws, wbar = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
     L1d = None if L1 is None else torch.from_numpy(np.ascontiguousarray(L1)).cuda()
     L2d = None if L2 is None else torch.from_numpy(L2).cuda()
-    Y = kq.w4a4_linear(xc, xs, wc, ws, X=X if r else None, L1=L1d, L2=L2d, mu=mu, wbar=wbar if center else None)
+    T = kq.lowrank_down(X, L1d) if r else None
+    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=L2d, mu=mu, wbar=wbar if center else None)
     torch.cuda.synchronize()
     return dict(X16=X16, W16=W16, L1=L1, L2=L2, xc=xc.cpu().numpy(), xs=xs.cpu().numpy(), wc=wc.cpu().numpy(),
                 ws=ws.cpu().numpy(), mu=None if mu is None else mu.cpu().numpy(),
-                wbar=None if not center else wbar.cpu().numpy(), Y=Y.cpu().numpy(), xf=xf)
+                wbar=None if not center else wbar.cpu().numpy(), Y=Y.cpu().numpy(), xf=xf,
+                T=None if T is None else T.cpu().numpy())
 
 
 def _ref_Y(d, rows=None, cols=None):
@@ -142,6 +144,22 @@ def test_w4a4_branch_variants(kq, rank, with_mu):
     err = linear.rel_frobenius(d["Y"], _ref_Y(d))
     print(f"rank {rank} mu {with_mu}: {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("M,K,r", [(1, 128, 32), (77, 1152, 16), (301, 3072, 32), (40, 12288, 64), (19, 2240, 32)])
+def test_lowrank_down_matches_oracle(kq, M, K, r):
+    """T = fp16(X L1^T): within one fp16 rounding of the exact product (plus the float32
+    accumulation bound)."""
+    import torch
+    X16 = synth.activations(M, K, 7, 2.0)
+    _, L1, _ = synth.weights(K, 16, 7, 0, r)
+    T = kq.lowrank_down(torch.from_numpy(X16).cuda(), torch.from_numpy(L1).cuda())
+    torch.cuda.synchronize()
+    got = T.cpu().numpy().astype(np.float64)
+    exact = X16.astype(np.float64) @ L1.astype(np.float64).T
+    bound = np.abs(X16.astype(np.float64)) @ np.abs(L1.astype(np.float64)).T
+    err = np.abs(got - exact)
+    assert np.all(err <= np.abs(exact) * 2.0 ** -11 + ties.gamma_tau(K // 8 + 16, bound) + 2.0 ** -24)
 
 
 def test_w4a4_small_shapes(kq):

@@ -8,7 +8,8 @@ library is missing: there is no fallback.
     xf = kq.Xform.kron(A, B, K)                     # or Xform.rpbh(perm, sign), Xform.none(K)
     codes, scales, mu = kq.transform_quantize(X, xf, fmt="mxfp4", center=False)
     wcodes, wscales, wbar = kq.fold_inverse_into_weights(W, xf, fmt="mxfp4")
-    Y = kq.w4a4_linear(codes, scales, wcodes, wscales, X=X, L1=L1, L2=L2, mu=mu, wbar=wbar)
+    T = kq.lowrank_down(X, L1)
+    Y = kq.w4a4_linear(codes, scales, wcodes, wscales, T=T, L2=L2, mu=mu, wbar=wbar)
 """
 
 import ctypes
@@ -16,7 +17,7 @@ import os
 
 __all__ = ["load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
            "transform_quantize", "fold_inverse_into_weights", "w4a4_linear",
-           "linear_workspace_bytes", "KQError"]
+           "lowrank_down", "KQError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -63,10 +64,10 @@ def load():
     lib.kq_transform_quantize.argtypes = [ctypes.POINTER(_XformC), i32, i32, vp, i64, i64, vp, vp, vp, vp]
     lib.kq_fold_inverse_into_weights.restype = i32
     lib.kq_fold_inverse_into_weights.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp]
-    lib.kq_w4a4_linear_workspace_bytes.restype = sz
-    lib.kq_w4a4_linear_workspace_bytes.argtypes = [i64, i32]
+    lib.kq_lowrank_down.restype = i32
+    lib.kq_lowrank_down.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     lib.kq_w4a4_linear.restype = i32
-    lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib
     return lib
 
@@ -220,13 +221,24 @@ def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None
     return wcodes, wscales, wbar
 
 
-def linear_workspace_bytes(M, r):
-    return int(load().kq_w4a4_linear_workspace_bytes(int(M), int(r)))
+def lowrank_down(X, L1, T=None, stream=None):
+    """T = fp16(X L1^T): the low-rank branch's down-projection (fp16 [M][r])."""
+    torch = _torch()
+    _check(X, "X", torch.float16)
+    M, K = X.shape
+    r = L1.shape[0]
+    _check(L1, "L1", torch.float16, (r, K))
+    T = torch.empty((M, r), dtype=torch.float16, device=X.device) if T is None else T
+    _check(T, "T", torch.float16, (M, r))
+    s = load().kq_lowrank_down(_ptr(X), _ptr(L1), M, K, r, _ptr(T), _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_lowrank_down")
+    return T
 
 
-def w4a4_linear(xcodes, xscales, wcodes, wscales, X=None, L1=None, L2=None, mu=None, wbar=None,
-                fmt="mxfp4", Y=None, workspace=None, stream=None):
-    """Y = Xq Wq^T + (X L1^T) L2^T + mu wbar^T (fp16 [M][N]).  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4)."""
+def w4a4_linear(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar=None,
+                fmt="mxfp4", Y=None, stream=None):
+    """Y = Xq Wq^T + T L2^T + mu wbar^T (fp16 [M][N]).  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4)."""
     torch = _torch()
     f = _FMT[fmt]
     _check(xcodes, "xcodes", torch.uint8)
@@ -241,24 +253,17 @@ def w4a4_linear(xcodes, xscales, wcodes, wscales, X=None, L1=None, L2=None, mu=N
         _check(xscales, "xscales", torch.float32, (M,))
         _check(wscales, "wscales", torch.float16, (N, K // 32))
     r = 0
-    if L1 is not None:
-        r = L1.shape[0]
-        _check(X, "X", torch.float16, (M, K))
-        _check(L1, "L1", torch.float16, (r, K))
+    if T is not None:
+        r = T.shape[1]
+        _check(T, "T", torch.float16, (M, r))
         _check(L2, "L2", torch.float16, (N, r))
     if mu is not None:
         _check(mu, "mu", torch.float16, (M,))
         _check(wbar, "wbar", torch.float16, (N,))
-    dev = xcodes.device
-    Y = torch.empty((M, N), dtype=torch.float16, device=dev) if Y is None else Y
+    Y = torch.empty((M, N), dtype=torch.float16, device=xcodes.device) if Y is None else Y
     _check(Y, "Y", torch.float16, (M, N))
-    need = linear_workspace_bytes(M, r)
-    if need and workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     s = load().kq_w4a4_linear(f, _ptr(xcodes), _ptr(xscales), M, K, _ptr(wcodes), _ptr(wscales), N,
-                              _ptr(X if r else None), _ptr(L1), _ptr(L2), r, _ptr(mu), _ptr(wbar), _ptr(Y),
-                              _ptr(workspace), wsb, _stream(stream))
+                              _ptr(T), _ptr(L2 if r else None), r, _ptr(mu), _ptr(wbar), _ptr(Y), _stream(stream))
     if s != KQ_OK:
         raise KQError(s, "kq_w4a4_linear")
     return Y

@@ -124,7 +124,6 @@ const char* kq_status_str(kq_status s) {
     case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE: invalid shape (M, N >= 1, K % 32 == 0, descriptor K, rank)";
     case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN: a device pointer is not suitably aligned";
     case KQ_ERR_UNSUPPORTED: return "KQ_ERR_UNSUPPORTED: unknown enum or size outside the supported range";
-    case KQ_ERR_WORKSPACE: return "KQ_ERR_WORKSPACE: workspace missing or too small";
     case KQ_ERR_VALUE: return "KQ_ERR_VALUE: transform factor singular or not finite";
     case KQ_ERR_HIP: return "KQ_ERR_HIP: a HIP launch failed";
     default: return "KQ_ERR_UNKNOWN: unknown status code";
@@ -186,16 +185,20 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const vo
   return hip_status(e);
 }
 
-size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r) {
-  if (M < 1 || r <= 0) return 0;
-  const size_t b = (size_t)M * (size_t)r * 2;
-  return (b + 255) & ~(size_t)255;
+kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r, void* T,
+                          hipStream_t stream) {
+  if (!X || !L1 || !T) return KQ_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if (M > (1LL << 31) - 64 || K > (1LL << 30)) return KQ_ERR_UNSUPPORTED;
+  if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16)) return KQ_ERR_ALIGN;
+  return hip_status(launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r,
+                                        static_cast<__half*>(T), stream));
 }
 
 kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
-                         const uint8_t* wcodes, const void* wscales, int64_t N, const void* X, const void* L1,
-                         const void* L2, int32_t r, const void* mu, const void* wbar, void* Y, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
+                         int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {
   if (!xcodes || !xscales || !wcodes || !wscales || !Y) return KQ_ERR_NULL;
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (r != 0 && r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
@@ -210,26 +213,18 @@ kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales
     return KQ_ERR_UNSUPPORTED;
   }
   if (r > 0) {
-    if (!X || !L1 || !L2) return KQ_ERR_NULL;
-    if (!workspace) return KQ_ERR_WORKSPACE;
-    if (workspace_bytes < kq_w4a4_linear_workspace_bytes(M, r)) return KQ_ERR_WORKSPACE;
-    if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(L2, 16) || !aligned(workspace, 16)) return KQ_ERR_ALIGN;
+    if (!T || !L2) return KQ_ERR_NULL;
+    if (!aligned(T, 16) || !aligned(L2, 16)) return KQ_ERR_ALIGN;
   }
   if (!aligned(xcodes, 16) || !aligned(wcodes, 16) || !aligned(Y, 16)) return KQ_ERR_ALIGN;
   if (!aligned(xscales, 4) || !aligned(wscales, 4)) return KQ_ERR_ALIGN;
   if (mu && (!aligned(mu, 2) || !aligned(wbar, 2))) return KQ_ERR_ALIGN;
   hipError_t e;
   if (fmt == KQ_FMT_MXFP4) {
-    __half* T = nullptr;
-    if (r > 0) {
-      T = static_cast<__half*>(workspace);
-      e = launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r, T, stream);
-      if (e != hipSuccess) return KQ_ERR_HIP;
-    }
     e = launch_w4a4_gemm(xcodes, static_cast<const uint8_t*>(xscales), M, K, wcodes,
-                         static_cast<const uint8_t*>(wscales), N, T, static_cast<const __half*>(L2), r,
-                         static_cast<const __half*>(mu), static_cast<const __half*>(wbar), static_cast<__half*>(Y),
-                         stream);
+                         static_cast<const uint8_t*>(wscales), N, r ? static_cast<const __half*>(T) : nullptr,
+                         static_cast<const __half*>(L2), r, static_cast<const __half*>(mu),
+                         static_cast<const __half*>(wbar), static_cast<__half*>(Y), stream);
   } else {
     e = launch_w2a4_gemm(xcodes, static_cast<const float*>(xscales), M, K, wcodes,
                          static_cast<const __half*>(wscales), N, static_cast<__half*>(Y), stream);

@@ -2,18 +2,21 @@
 // matrix cores with fp32 accumulation, T stored as fp16 [M][r] (the branch is held in
 // 16 bits).  X is the original fp16 activation [M][K], L1 is [r][K].
 //
-// A workgroup of four wavefronts owns 16 rows; wavefront w reduces the 32-wide k-steps
-// w, w+4, ... with v_mfma_f32_16x16x32_f16 (lane l: row l%16, k = 8*(l/16)..+7, one
-// 16-byte load per operand), and the four partial 16 x r tiles are summed through LDS.
+// A workgroup of SPLIT wavefronts owns 16 rows; wavefront w reduces the 32-wide k-steps
+// w, w+SPLIT, ... with v_mfma_f32_16x16x32_f16 (lane l: row l%16, k = 8*(l/16)..+7, one
+// 16-byte load per operand).  Loads are issued in batches of BATCH k-steps ahead of their
+// MFMAs so each wavefront keeps several KiB in flight; the SPLIT partial 16 x r tiles are
+// summed through LDS in a fixed order.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
 namespace kq {
 
-template <int RT>  // RT = r / 16 output tiles
-__global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restrict__ X, const __half* __restrict__ L1,
-                                                           int64_t M, int64_t K, __half* __restrict__ T) {
-  __shared__ float part[4][16][RT * 16];
+template <int RT, int SPLIT, int BATCH>  // RT = r / 16 output tiles
+__global__ __launch_bounds__(64 * SPLIT) void lowrank_down_kernel(const __half* __restrict__ X,
+                                                                  const __half* __restrict__ L1, int64_t M,
+                                                                  int64_t K, __half* __restrict__ T) {
+  __shared__ float part[SPLIT][16][RT * 16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   int64_t row = m0 + (lane & 15);
@@ -24,13 +27,23 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   const __half* xr = X + row * K + 8 * q;
-  for (int64_t s = w; s < nk; s += 4) {
-    const v8h a = *reinterpret_cast<const v8h*>(xr + 32 * s);
+  const __half* lr[RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const v8h b = *reinterpret_cast<const v8h*>(L1 + (int64_t)(16 * t + (lane & 15)) * K + 32 * s + 8 * q);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+  for (int t = 0; t < RT; ++t) lr[t] = L1 + (int64_t)(16 * t + (lane & 15)) * K + 8 * q;
+  for (int64_t s0 = w; s0 < nk; s0 += SPLIT * BATCH) {
+    v8h a[BATCH], b[BATCH][RT];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int64_t s = s0 + (int64_t)u * SPLIT;
+      const bool ok = s < nk;
+      a[u] = ok ? *reinterpret_cast<const v8h*>(xr + 32 * s) : v8h{};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) b[u][t] = ok ? *reinterpret_cast<const v8h*>(lr[t] + 32 * s) : v8h{};
     }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], b[u][t], acc[t], 0, 0, 0);
   }
   // acc[t][i] = partial T[m0 + 4q + i][16t + lane%16]
 #pragma unroll
@@ -38,20 +51,23 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[w][4 * q + i][16 * t + (lane & 15)] = acc[t][i];
   __syncthreads();
-  for (int e = threadIdx.x; e < 16 * RT * 16; e += 256) {
+  for (int e = threadIdx.x; e < 16 * RT * 16; e += 64 * SPLIT) {
     const int r = e / (RT * 16), c = e % (RT * 16);
-    const float v = (part[0][r][c] + part[1][r][c]) + (part[2][r][c] + part[3][r][c]);
+    float v = 0.0f;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) v += part[p][r][c];
     if (m0 + r < M) T[(m0 + r) * (RT * 16) + c] = __float2half_rn(v);
   }
 }
 
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
                                hipStream_t s) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(256);
+  constexpr int SPLIT = 8, BATCH = 6;
+  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * SPLIT);
   switch (r) {
-    case 16: hipLaunchKernelGGL(lowrank_down_kernel<1>, grid, block, 0, s, X, L1, M, K, T); break;
-    case 32: hipLaunchKernelGGL(lowrank_down_kernel<2>, grid, block, 0, s, X, L1, M, K, T); break;
-    case 64: hipLaunchKernelGGL(lowrank_down_kernel<4>, grid, block, 0, s, X, L1, M, K, T); break;
+    case 16: hipLaunchKernelGGL((lowrank_down_kernel<1, SPLIT, BATCH>), grid, block, 0, s, X, L1, M, K, T); break;
+    case 32: hipLaunchKernelGGL((lowrank_down_kernel<2, SPLIT, BATCH>), grid, block, 0, s, X, L1, M, K, T); break;
+    case 64: hipLaunchKernelGGL((lowrank_down_kernel<4, SPLIT, 4>), grid, block, 0, s, X, L1, M, K, T); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
