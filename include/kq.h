@@ -79,7 +79,8 @@ enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
  * RPBH_32 (OrbitQuant §03): y = x . Pi . blockdiag(H32) . D / sqrt(32) with
  *   (x.Pi)_j = x[perm[j]] over all K, H32 the Sylvester Hadamard matrix
  *   (H[i][j] = (-1)^popcount(i&j)), D = diag(sign), sign[j] in {-1, +1}.
- *   perm (int32 [K], a permutation of 0..K-1) and sign (int8 [K]) are device arrays.
+ *   perm (int32 [K], a permutation of 0..K-1) and sign (int8 [K]) are device arrays,
+ *   16- and 4-byte aligned.
  * NONE: identity. */
 typedef struct kq_xform {
   int32_t kind;
@@ -113,8 +114,8 @@ kq_status kq_lloyd_max_levels(int32_t n, double* levels_out);
  *                        (a value on a threshold takes the smaller magnitude).
  * X fp16 [M][K]; codes u8 [M][K/2]; scales u8 [M][K/32] (MXFP4) or f32 [M] (LM4);
  * mu fp16 [M], required iff center != 0 (else ignored).
- * K % 32 == 0; K <= 32768 when centring or LM4 is used, K <= 16384 for RPBH (the row is
- * staged on chip).
+ * K % 32 == 0; K <= 16384 when centring, RPBH or LM4 is used (rows are staged on chip;
+ * K <= 16320 for RPBH).
  * All device pointers 16-byte aligned except mu and scales (4-byte for LM4). */
 kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
                                 const void* X, int64_t M, int64_t K,

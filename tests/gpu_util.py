@@ -7,12 +7,22 @@ from oracle import mxfp4, pipeline, ties, transforms
 
 U = 2.0 ** -24
 
-# Forward-error operation counts of the kernels' float32 arithmetic per output element:
-#  Kronecker: an 8-term FMA chain (x B) feeding a 4-term chain (A^T .), plus the rounding
-#             of the folded inverse factors to float32 in the weight fold;
-#  RPBH: five butterfly stages, the rounded 1/sqrt(32) and the final product;
-#  centring adds one rounding (x - mu in float32).
-N_OPS = {"kron": 13, "rpbh": 8, "none": 1}
+# Forward-error bounds of the kernels' float32 arithmetic per output element, by path:
+#  Kronecker, no centring (matrix cores): A (x) B formed in float32 and split into fp16
+#      hi + lo parts (~2^-21 relative), 64 exact products accumulated in float32;
+#  Kronecker or identity with centring, and Lloyd-Max (vector units): an 8-term FMA chain
+#      feeding a 4-term chain, plus the centring subtraction;
+#  RPBH, MXFP4 (matrix cores): 32 exact +-1 products of the UNCENTRED inputs accumulated in
+#      float32, the centring applied to output 0 of each block afterwards (subtracting
+#      32 mu), then the rounded 1/sqrt(32) and the final product;
+#  RPBH, Lloyd-Max (vector units): five butterfly stages, 1/sqrt(32), the product, and
+#      the centring subtraction.
+def _path(kind, center, fmt):
+    if kind == "kron":
+        return ("uncentred", 80) if (not center and fmt == "mxfp4") else ("centred", 14)
+    if kind == "rpbh":
+        return ("uncentred", 36) if fmt == "mxfp4" else ("centred", 9)
+    return ("uncentred", 2) if (not center and fmt == "mxfp4") else ("centred", 2)
 
 
 def abs_transform(x_abs, xform):
@@ -27,14 +37,22 @@ def abs_transform(x_abs, xform):
     return x_abs
 
 
-def tau_for(x_c, xform, center):
-    n = N_OPS[xform["kind"]] + (1 if center else 0)
-    return ties.gamma_tau(n, abs_transform(np.abs(x_c), xform))
+def tau_for(x_c, xform, center, fmt="mxfp4", x_raw=None, mu=None):
+    """Per-element error bound of the kernel that handles (transform, centring, format).
+    x_c: the centred input (or the raw input when not centring); x_raw, mu: the raw input
+    and the fp16 means, needed for the paths that centre after the transform."""
+    which, n = _path(xform["kind"], center, fmt)
+    if which == "centred" or not center:
+        return ties.gamma_tau(n, abs_transform(np.abs(x_c), xform))
+    base = abs_transform(np.abs(np.asarray(x_raw, dtype=np.float64)), xform)
+    corr = np.zeros_like(base)
+    corr[:, 0::32] = 32.0 * np.abs(np.asarray(mu, dtype=np.float64))[:, None] / np.sqrt(32.0)
+    return ties.gamma_tau(n, base + corr)
 
 
-def oracle_activation_reference(X16, xform, center, mu_gpu=None):
-    """Exact transformed values y (float64) and the error bound tau, using the kernel's mean
-    where it differs from the oracle's only by a rounding tie."""
+def oracle_activation_reference(X16, xform, center, mu_gpu=None, fmt="mxfp4"):
+    """Exact transformed values y (float64) and the kernel's error bound tau, using the
+    kernel's mean where it differs from the oracle's only by a rounding tie."""
     X = X16.astype(np.float64)
     mu = None
     if center:
@@ -45,7 +63,7 @@ def oracle_activation_reference(X16, xform, center, mu_gpu=None):
     else:
         xc = X
     y = pipeline.apply_transform(xc, xform)
-    return y, tau_for(xc, xform, center), mu
+    return y, tau_for(xc, xform, center, fmt, x_raw=X, mu=mu), mu
 
 
 def check_mu(X16, mu_gpu):

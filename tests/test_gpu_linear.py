@@ -53,9 +53,9 @@ def test_fold_mxfp4_matches_oracle(kq, cfg, layer, nrows):
         # w'_b = P^-1 w_b, so the bound scales with sum_k |P^-1[j][k]| |w_k| = (|w| |P^-T|)_j
         inv_t = {"kind": "kron", "A": np.linalg.inv(xf["A"].astype(np.float64)).T,
                  "B": np.linalg.inv(xf["B"].astype(np.float64)).T}
-        tau = gpu_util.tau_for(W16.astype(np.float64), inv_t, False)
-    else:
-        tau = gpu_util.tau_for(W16.astype(np.float64), xf, False)     # W'^T = W^T R
+        tau = ties.gamma_tau(13, gpu_util.abs_transform(np.abs(W16.astype(np.float64)), inv_t))
+    else:   # W'^T = W^T R, five butterfly stages, 1/sqrt(32) and the product
+        tau = ties.gamma_tau(8, gpu_util.abs_transform(np.abs(W16.astype(np.float64)), xf))
     gpu_util.assert_mx_parity(wc.cpu().numpy(), ws.cpu().numpy(), wt, tau, label=f"fold cfg{cfg} layer{layer}")
     _wbar_check(W16, wbar.cpu().numpy())
 
@@ -71,7 +71,7 @@ def test_fold_w2_matches_oracle(kq):
     s_gpu = ws.cpu().numpy()
     wt = pipeline.inverse_fold(W16, xf)
     ref_codes, ref_s = lloyd_max.w2_group_quantize(wt)
-    tau = gpu_util.tau_for(W16.astype(np.float64), xf, False).reshape(wt.shape)
+    tau = ties.gamma_tau(8, gpu_util.abs_transform(np.abs(W16.astype(np.float64)), xf)).reshape(wt.shape)
     # group scales: fp16 of the RMS; differences only at fp16 rounding ties
     g = wt.reshape(wt.shape[0], -1, 32)
     rms = np.sqrt(np.mean(g * g, axis=2))

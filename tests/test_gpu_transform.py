@@ -104,7 +104,7 @@ def test_single_row_and_ragged_block_count(kq):
 
 def _lm4_check(kq, X16, xf, label):
     codes_p, s_gpu, _ = _run(kq, X16, xf, "lm4", False)
-    y, tau, _ = gpu_util.oracle_activation_reference(X16, xf, False)
+    y, tau, _ = gpu_util.oracle_activation_reference(X16, xf, False, fmt="lm4")
     codes = mxfp4.unpack_nibbles(codes_p)
     # relative error bound of the kernel's scale: the float32 sum of squares (per-thread
     # chains of <= 32 terms, a 6-level wave tree, <= 16 wave partials), plus the effect

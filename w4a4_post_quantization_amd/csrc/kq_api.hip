@@ -102,7 +102,7 @@ static kq_status check_xform(const kq_xform* xf, int64_t K) {
   if (xf->K != K) return KQ_ERR_SHAPE;
   if (xf->kind == KQ_XFORM_RPBH_32) {
     if (!xf->perm || !xf->sign) return KQ_ERR_NULL;
-    if (!aligned(xf->perm, 16)) return KQ_ERR_ALIGN;
+    if (!aligned(xf->perm, 16) || !aligned(xf->sign, 4)) return KQ_ERR_ALIGN;
   }
   if (xf->kind == KQ_XFORM_KRON_4X8) {
     for (int i = 0; i < 16; ++i)
@@ -149,16 +149,24 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   KronFactors f;
   std::memcpy(f.A, xf->A, sizeof f.A);
   std::memcpy(f.B, xf->B, sizeof f.B);
-  const bool row_path = center || fmt != KQ_FMT_MXFP4 || xf->kind != KQ_XFORM_KRON_4X8;
-  if (row_path && K > 32768) return KQ_ERR_UNSUPPORTED;
-  if (xf->kind == KQ_XFORM_RPBH_32 && K > 16384) return KQ_ERR_UNSUPPORTED;  // row staged in 32 KiB of LDS
+  // MXFP4 goes through the matrix-core transforms (streaming for Kronecker / identity
+  // without centring, row-staged for RPBH); the per-token Lloyd-Max format and centred
+  // Kronecker / identity use the row-staged vector kernel.
+  const bool mx = fmt == KQ_FMT_MXFP4;
+  const bool stream_path = mx && !center && xf->kind != KQ_XFORM_RPBH_32;
+  const bool rpbh_mfma = mx && xf->kind == KQ_XFORM_RPBH_32;
+  if (!stream_path && K > 16384) return KQ_ERR_UNSUPPORTED;
+  if (xf->kind == KQ_XFORM_RPBH_32 && K > 16320) return KQ_ERR_UNSUPPORTED;  // two rows staged in 64 KiB of LDS
   hipError_t e;
-  if (!row_path) {
-    e = launch_kron_mx_stream(static_cast<const __half*>(X), M * (K / 32), f, codes,
-                              static_cast<uint8_t*>(scales), stream);
+  if (stream_path) {
+    e = launch_kron_mx_mfma(xf->kind == KQ_XFORM_KRON_4X8, static_cast<const __half*>(X), M * (K / 32), f, codes,
+                            static_cast<uint8_t*>(scales), stream);
+  } else if (rpbh_mfma) {
+    e = launch_rpbh_mx_mfma(center != 0, static_cast<const __half*>(X), M, K, xf->perm, xf->sign, codes,
+                            static_cast<uint8_t*>(scales), static_cast<__half*>(mu), stream);
   } else {
-    e = launch_row_quant(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 1, center != 0, static_cast<const __half*>(X), M, K, f,
-                         xf->perm, xf->sign, codes, scales, static_cast<__half*>(mu), stream);
+    e = launch_row_quant(xf->kind, mx ? 0 : 1, center != 0, static_cast<const __half*>(X), M, K, f, xf->perm,
+                         xf->sign, codes, scales, static_cast<__half*>(mu), stream);
   }
   return hip_status(e);
 }

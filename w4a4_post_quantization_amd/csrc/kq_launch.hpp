@@ -27,6 +27,13 @@ bool lloyd_max_levels(int n, double* out);
 hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFactors& f,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// Matrix-core block transforms + MXFP4: streaming Kronecker (or identity) without centring,
+// and row-staged RPBH with optional centring.
+hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, const KronFactors& f, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
+                               const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s);
+
 // Row-staged transform + quantize: any transform, optional centring, MXFP4 or LM4.
 // kind: 0 none, 1 kron, 2 rpbh; fmt: 0 MXFP4, 1 LM4.
 hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int64_t M, int64_t K,

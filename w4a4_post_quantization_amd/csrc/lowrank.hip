@@ -13,7 +13,7 @@
 namespace kq {
 
 template <int RT, int SPLIT, int BATCH>  // RT = r / 16 output tiles
-__global__ __launch_bounds__(64 * SPLIT) void lowrank_down_kernel(const __half* __restrict__ X,
+__global__ __launch_bounds__(64 * SPLIT, 1) void lowrank_down_kernel(const __half* __restrict__ X,
                                                                   const __half* __restrict__ L1, int64_t M,
                                                                   int64_t K, __half* __restrict__ T) {
   __shared__ float part[SPLIT][16][RT * 16];
@@ -60,17 +60,25 @@ __global__ __launch_bounds__(64 * SPLIT) void lowrank_down_kernel(const __half* 
   }
 }
 
-hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
-                               hipStream_t s) {
-  constexpr int SPLIT = 8, BATCH = 6;
+template <int SPLIT>
+static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
+                                 hipStream_t s) {
   const dim3 grid((unsigned)((M + 15) / 16)), block(64 * SPLIT);
   switch (r) {
-    case 16: hipLaunchKernelGGL((lowrank_down_kernel<1, SPLIT, BATCH>), grid, block, 0, s, X, L1, M, K, T); break;
-    case 32: hipLaunchKernelGGL((lowrank_down_kernel<2, SPLIT, BATCH>), grid, block, 0, s, X, L1, M, K, T); break;
+    case 16: hipLaunchKernelGGL((lowrank_down_kernel<1, SPLIT, 8>), grid, block, 0, s, X, L1, M, K, T); break;
+    case 32: hipLaunchKernelGGL((lowrank_down_kernel<2, SPLIT, 8>), grid, block, 0, s, X, L1, M, K, T); break;
     case 64: hipLaunchKernelGGL((lowrank_down_kernel<4, SPLIT, 4>), grid, block, 0, s, X, L1, M, K, T); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
+                               hipStream_t s) {
+  // one batch of 8 k-steps per wavefront for K up to 8 x 32 x SPLIT; long rows use 16
+  // wavefronts so each still issues its loads in one or two batches
+  if (K >= 8192) return lowrank_launch<16>(X, L1, M, K, r, T, s);
+  return lowrank_launch<8>(X, L1, M, K, r, T, s);
 }
 
 }  // namespace kq

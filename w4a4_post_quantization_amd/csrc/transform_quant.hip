@@ -120,74 +120,98 @@ __global__ __launch_bounds__(256) void kron_mx_stream_kernel(const uint4* __rest
 }
 
 // ---------------------------------------------------------------------------------
-// Row-staged kernel: one workgroup per token row (grid-strided).  Thread t owns the
-// 8-element groups g = t + T*j (j < NG); a group's quad holds one 32-element block.
+// Row-staged kernel: each workgroup walks token rows (grid-strided).  Thread t owns the
+// 8-element groups g = t + T*j (j < NG) of a row; a group's quad holds one 32-element
+// block.  The next row's 16-byte chunks are loaded into registers while the current row
+// is transformed, and rows alternate between two LDS buffers, so one barrier per row
+// suffices and two rows per workgroup are in flight.
 // KIND: 0 none, 1 Kronecker, 2 RPBH.  FMT: 0 MXFP4, 1 per-token Lloyd-Max (LM4).
 template <int KIND, int FMT, bool CENTER, int NG>
-__global__ __launch_bounds__(1024) void row_quant_kernel(const __half* __restrict__ X, int64_t M, int K,
-                                                         KronFactors f, const int32_t* __restrict__ perm,
-                                                         const int8_t* __restrict__ sign, LmTables lm,
-                                                         uint8_t* __restrict__ codes, void* __restrict__ scales,
-                                                         __half* __restrict__ mu) {
+__global__ __launch_bounds__(512) void row_quant_kernel(const __half* __restrict__ X, int64_t M, int K,
+                                                        KronFactors f, const int32_t* __restrict__ perm,
+                                                        const int8_t* __restrict__ sign, LmTables lm,
+                                                        uint8_t* __restrict__ codes, void* __restrict__ scales,
+                                                        __half* __restrict__ mu) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __half* srow = reinterpret_cast<__half*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (KIND == 2 ? (size_t)K * 2 : 0));
   const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wid = t >> 6, nw = T >> 6;
   const int G = K >> 3;
   const int qi = lane & 3;
+  // two row buffers of K halves (RPBH only), addressed from the __shared__ base so the
+  // gathers stay LDS reads
+  __half* const srow0 = reinterpret_cast<__half*>(smem);
+  float* red = reinterpret_cast<float*>(smem + (KIND == 2 ? (size_t)K * 4 : 0));   // [2][32]: wave sums
 
   float acol[4];
   if (KIND == 1) kron_acol(f, qi, acol);
-  // RPBH: gather indices and output coefficients d_j * (-1)^popcount(qi) / sqrt(32)
+  // RPBH: gather indices (K <= 16384 uses 14 bits; bit 15 carries the sign d_j of the
+  // output element), and the lane's butterfly sign (-1)^popcount(qi) folded into 1/sqrt(32)
   uint32_t pidx[KIND == 2 ? NG : 1][4];
-  float coef[KIND == 2 ? NG : 1][8];
   const float s1 = (qi & 1) ? -1.0f : 1.0f;
   const float s2 = (qi & 2) ? -1.0f : 1.0f;
+  const float rho = s1 * s2 * KQ_INV_SQRT32;
   if (KIND == 2) {
-    const float rho = s1 * s2 * KQ_INV_SQRT32;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int g = t + T * j;
       const bool v = g < G;
 #pragma unroll
       for (int m = 0; m < 8; m += 2) {
-        const uint32_t p0 = v ? (uint32_t)perm[8 * g + m] : 0u;
-        const uint32_t p1 = v ? (uint32_t)perm[8 * g + m + 1] : 0u;
+        uint32_t p0 = 0, p1 = 0;
+        if (v) {
+          p0 = (uint32_t)perm[8 * g + m] | (sign[8 * g + m] < 0 ? 0x8000u : 0u);
+          p1 = (uint32_t)perm[8 * g + m + 1] | (sign[8 * g + m + 1] < 0 ? 0x8000u : 0u);
+        }
         pidx[j][m >> 1] = p0 | (p1 << 16);
       }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) coef[j][m] = (v && sign[8 * g + m] < 0) ? -rho : rho;
     }
   }
 
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+  uint4 raw[NG];
+  auto load_row = [&](int64_t row) {
     const uint4* xr = reinterpret_cast<const uint4*>(X + row * (int64_t)K);
-    uint4 raw[NG];
-    float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const int g = t + T * j;
-      raw[j] = g < G ? xr[g] : make_uint4(0u, 0u, 0u, 0u);
-      if (KIND == 2 && g < G) reinterpret_cast<uint4*>(srow)[g] = raw[j];
+      raw[j] = (row < M && g < G) ? xr[g] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  int64_t row = blockIdx.x;
+  load_row(row);
+  for (int it = 0; row < M; row += gridDim.x, ++it) {
+    const int buf = it & 1;
+    uint4 cur[NG];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      cur[j] = raw[j];
+      const int g = t + T * j;
+      if (KIND == 2 && g < G) reinterpret_cast<uint4*>(srow0 + buf * K)[g] = cur[j];
       if (CENTER) {
         float x[8];
-        unpack8_f16(raw[j], x);
+        unpack8_f16(cur[j], x);
 #pragma unroll
         for (int m = 0; m < 8; ++m) psum += x[m];
       }
     }
+    load_row(row + gridDim.x);            // prefetch the next row while this one is processed
+    float* rd = red + buf * 32;
+    if (CENTER) {
+      const float sw = wave_sum(psum);
+      if (lane == 0) rd[wid] = sw;
+    }
+    if (CENTER || KIND == 2) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
     float muf = 0.0f;
     if (CENTER) {
-      const float s = wave_sum(psum);
-      if (lane == 0) red[wid] = s;
-      __syncthreads();
       float tot = 0.0f;
-      for (int w = 0; w < nw; ++w) tot += red[w];
+      for (int w = 0; w < nw; ++w) tot += rd[w];
       const __half mh = __float2half_rn(tot / (float)K);
       muf = __half2float(mh);
       if (t == 0) mu[row] = mh;
-    } else if (KIND == 2) {
-      __syncthreads();
     }
 
     float yv[FMT == 1 ? NG : 1][8];
@@ -197,14 +221,16 @@ __global__ __launch_bounds__(1024) void row_quant_kernel(const __half* __restric
       const int g = t + T * j;
       const bool valid = g < G;
       float u[8], y[8];
+      uint32_t sgn = 0;
       if (KIND == 2) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const uint32_t p = (pidx[j][m >> 1] >> (16 * (m & 1))) & 0xFFFFu;
-          u[m] = __half2float(srow[p]);
+          u[m] = __half2float(srow0[buf * K + (int)(p & 0x7FFFu)]);
+          sgn |= (p >> 15) << m;
         }
       } else {
-        unpack8_f16(raw[j], u);
+        unpack8_f16(cur[j], u);
       }
       if (CENTER) {
 #pragma unroll
@@ -214,8 +240,9 @@ __global__ __launch_bounds__(1024) void row_quant_kernel(const __half* __restric
         kron_quad(u, f, acol, y);
       } else if (KIND == 2) {
         hadamard32_quad(u, s1, s2);
+        // y = v d_j / sqrt(32); the fma with +0 turns an exact -0 into +0
 #pragma unroll
-        for (int m = 0; m < 8; ++m) y[m] = __builtin_fmaf(u[m], coef[j][m], 0.0f);
+        for (int m = 0; m < 8; ++m) y[m] = __builtin_fmaf(u[m], ((sgn >> m) & 1) ? -rho : rho, 0.0f);
       } else {
 #pragma unroll
         for (int m = 0; m < 8; ++m) y[m] = u[m] + 0.0f;
@@ -235,19 +262,21 @@ __global__ __launch_bounds__(1024) void row_quant_kernel(const __half* __restric
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           yv[j][m] = y[m];
-          // lanes past the end of the row (K/8 not a multiple of the block size) hold
-          // gathered filler and must not enter the token's sum of squares
+          // lanes past the end of the row hold gathered filler and must not enter the
+          // token's sum of squares
           ssq = valid ? __builtin_fmaf(y[m], y[m], ssq) : ssq;
         }
       }
     }
 
     if (FMT == 1) {
-      const float s = wave_sum(ssq);
-      if (lane == 0) red[32 + wid] = s;
-      __syncthreads();
+      const float sw = wave_sum(ssq);
+      if (lane == 0) rd[16 + wid] = sw;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       float tot = 0.0f;
-      for (int w = 0; w < nw; ++w) tot += red[32 + w];
+      for (int w = 0; w < nw; ++w) tot += rd[16 + w];
       const float sc = sqrtf(tot / (float)K);
       float ts[7];
 #pragma unroll
@@ -273,8 +302,324 @@ __global__ __launch_bounds__(1024) void row_quant_kernel(const __half* __restric
       }
       if (t == 0) reinterpret_cast<float*>(scales)[row] = sc;
     }
-    __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Matrix-core block transform.  A 32-element block transform is a 32x32 matrix product,
+// so 16 blocks at a time go through v_mfma_f32_16x16x32_f16 in the transposed
+// orientation C^T = P^T X^T: the A operand holds 16 output rows of P^T (two 16-row
+// tiles cover the block), the B operand holds the 16 blocks as columns (lane l: block
+// l%16, elements 8(l/16)..+7 as fp16, exact), and lane l ends with outputs
+// 4q..4q+3 and 16+4q..16+4q+3 (q = l/16) of block l%16 -- eight outputs of one block
+// per lane, so the block maximum needs two lane exchanges and the codes pack locally.
+// RPBH: P = H32, entries +-1, exact in fp16.  Kronecker: P = A (x) B formed in float32
+// and split into fp16 hi + lo parts (two MFMAs per tile; the split keeps ~22 bits).
+
+struct MfmaXform {
+  v8h a[2][2];   // [tile][hi, lo] A-operand fragments (P^T rows)
+};
+
+// A-operand fragments of P^T for this lane: tile t rows j = 16t + l%16, k = 8q..8q+7.
+__device__ __forceinline__ MfmaXform mfma_xform_kron(const KronFactors& f, int lane) {
+  MfmaXform x;
+  const int q = lane >> 4, jl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = 16 * t + jl;                 // output index (column of P)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * q + i;                 // input index (row of P)
+      const float p = f.A[4 * (k >> 3) + (j >> 3)] * f.B[8 * (k & 7) + (j & 7)];
+      const _Float16 hi = (_Float16)p;
+      x.a[t][0][i] = hi;
+      x.a[t][1][i] = (_Float16)(p - (float)hi);
+    }
+  }
+  return x;
+}
+
+__device__ __forceinline__ MfmaXform mfma_xform_hadamard(int lane) {
+  MfmaXform x;
+  const int q = lane >> 4, jl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = 16 * t + jl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * q + i;
+      x.a[t][0][i] = (__builtin_popcount(j & k) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      x.a[t][1][i] = (_Float16)0.0f;
+    }
+  }
+  return x;
+}
+
+// y[0..3] = outputs 4q..4q+3, y[4..7] = outputs 16+4q..16+4q+3 of block l%16.
+template <bool LO>
+__device__ __forceinline__ void mfma_block_transform(const MfmaXform& x, const v8h& b, float* y) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(x.a[t][0], b, acc, 0, 0, 0);
+    if (LO) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(x.a[t][1], b, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[4 * t + i] = acc[i];
+  }
+}
+
+// MXFP4 of the lane's eight outputs: block maximum over the four lanes l, l^16, l^32,
+// l^48, E8M0 byte, and the packed codes as one dword per lane at byte offset
+// {0, 8, 4, 12}[q] of the block's 16 code bytes (lanes q and q^1 swap halves).
+// Inputs must not be -0.0.
+__device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& dword, int& byte_off,
+                                              uint32_t& scale_byte) {
+  float a = fmaxf(fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))),
+                  fmaxf(fmaxf(fabsf(y[4]), fabsf(y[5])), fmaxf(fabsf(y[6]), fabsf(y[7]))));
+  // maximum with lanes l^16 and l^32 through the register lane swaps: each swap returns,
+  // per lane, its own value in one result and its partner's in the other, so the maximum
+  // of both results is the pairwise maximum whichever way round the swap goes
+  {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(a, fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1])));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(a, fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])));
+  }
+  const uint32_t sb = e8m0_byte(a);
+  const float sc = e8m0_as_cvt_scale(sb);
+  uint32_t h0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], sc, 0);
+  h0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h0, y[2], y[3], sc, 1);      // bytes 2q, 2q+1
+  uint32_t h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[4], y[5], sc, 0);
+  h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h1, y[6], y[7], sc, 1);      // bytes 8+2q, 8+2q+1
+  const bool odd = q & 1;
+  const uint32_t r = (uint32_t)__shfl_xor((int)(odd ? h0 : h1), 16, 64);
+  dword = odd ? (r | (h1 << 16)) : (h0 | (r << 16));
+  byte_off = odd ? 8 + 2 * (q - 1) : 2 * q;
+  scale_byte = sb;
+}
+
+// Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
+// flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
+// one 16-byte load per lane and writes 256 contiguous code bytes.
+template <int U, bool KRON>
+__global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* __restrict__ X, int64_t nblocks,
+                                                                  KronFactors f, uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15;
+  MfmaXform xf;
+  if (KRON) {
+    xf = mfma_xform_kron(f, lane);
+  } else {   // identity: P^T rows are unit vectors
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xf.a[t][0][i] = (16 * t + bl == 8 * q + i) ? (_Float16)1.0f : (_Float16)0.0f;
+        xf.a[t][1][i] = (_Float16)0.0f;
+      }
+  }
+  const int64_t nchunks = (nblocks + 15) >> 4;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  for (int64_t c0 = wave; c0 < nchunks; c0 += nwaves * U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * nwaves;
+      const int64_t blk = c * 16 + bl;
+      raw[u] = (c < nchunks && blk < nblocks) ? X[blk * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float y[8];
+      mfma_block_transform<KRON>(xf, __builtin_bit_cast(v8h, raw[u]), y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] += 0.0f;      // an exact zero leaves as +0
+      uint32_t w, sb;
+      int off;
+      mx_pack_block(y, q, w, off, sb);
+      const int64_t c = c0 + u * nwaves;
+      const int64_t blk = c * 16 + bl;
+      if (c < nchunks && blk < nblocks) {
+        *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
+        if (q == 0) scales[blk] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// Row-staged RPBH + MXFP4 on the matrix cores, optional centring.  A workgroup walks token
+// rows; each row is staged in LDS (two buffers, ping-pong) for the full-K permutation
+// gather, and wavefront w transforms the 16-block chunks w, w+W, ... of the row.
+// Centring is applied after the rotation: (x - mu 1) H32 = x H32 - 32 mu e_0 for the
+// Sylvester matrix (every column but the first sums to zero), so only output 0 of each
+// block is corrected; the result is the same linear map as centring first.
+template <bool CENTER, int CW>
+__global__ __launch_bounds__(512) void rpbh_mx_mfma_row_kernel(const __half* __restrict__ X, int64_t M, int K,
+                                                               const int32_t* __restrict__ perm,
+                                                               const int8_t* __restrict__ sign,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales, __half* __restrict__ mu) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __half* const srow0 = reinterpret_cast<__half*>(smem);             // [2][K]
+  float* red = reinterpret_cast<float*>(smem + (size_t)K * 4);      // [2][16] wave partial sums
+  const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wid = t >> 6, nw = T >> 6;
+  const int q = lane >> 4, bl = lane & 15;
+  const int G = K >> 3, nb = K >> 5, nchunk = (nb + 15) >> 4;
+  const MfmaXform xf = mfma_xform_hadamard(lane);
+
+  // per chunk of this wave: the gather indices of the lane's eight inputs (two per dword)
+  // and the output coefficients d_j / sqrt(32) of its eight outputs
+  uint32_t pidx[CW][4];
+  float coef[CW][8];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const int ch = wid + nw * c;
+    const int blk = 16 * ch + bl;
+    const bool v = ch < nchunk && blk < nb;
+    // inputs 8q..8q+7 of block blk: 32 contiguous bytes of perm; outputs 4q..4q+3 and
+    // 16+4q..16+4q+3: two groups of 4 contiguous sign bytes
+    uint4 p0 = make_uint4(0u, 0u, 0u, 0u), p1 = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t sg0 = 0x01010101u, sg1 = 0x01010101u;
+    if (v) {
+      p0 = *reinterpret_cast<const uint4*>(perm + 32 * blk + 8 * q);
+      p1 = *reinterpret_cast<const uint4*>(perm + 32 * blk + 8 * q + 4);
+      sg0 = *reinterpret_cast<const uint32_t*>(sign + 32 * blk + 4 * q);
+      sg1 = *reinterpret_cast<const uint32_t*>(sign + 32 * blk + 16 + 4 * q);
+    }
+    pidx[c][0] = p0.x | (p0.y << 16);
+    pidx[c][1] = p0.z | (p0.w << 16);
+    pidx[c][2] = p1.x | (p1.y << 16);
+    pidx[c][3] = p1.z | (p1.w << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      coef[c][i] = ((sg0 >> (8 * i)) & 0x80u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
+      coef[c][4 + i] = ((sg1 >> (8 * i)) & 0x80u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
+    }
+  }
+
+  constexpr int NL = 4;   // row chunks of 16 bytes per thread, at most
+  uint4 raw[NL];
+  const int nl = (G + T - 1) / T;
+  auto load_row = [&](int64_t row) {
+    const uint4* xr = reinterpret_cast<const uint4*>(X + row * (int64_t)K);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int g = t + T * j;
+      raw[j] = (j < nl && row < M && g < G) ? xr[g] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  int64_t row = blockIdx.x;
+  load_row(row);
+  for (int it = 0; row < M; row += gridDim.x, ++it) {
+    const int buf = it & 1;
+    __half* const sr = srow0 + buf * K;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int g = t + T * j;
+      if (j < nl && g < G) {
+        reinterpret_cast<uint4*>(sr)[g] = raw[j];
+        if (CENTER) {
+          float x[8];
+          unpack8_f16(raw[j], x);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) psum += x[m];
+        }
+      }
+    }
+    load_row(row + gridDim.x);            // prefetch the next row while this one is processed
+    float* rd = red + buf * 16;
+    if (CENTER) {
+      const float sw = wave_sum(psum);
+      if (lane == 0) rd[wid] = sw;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    float m32 = 0.0f;
+    if (CENTER) {
+      float tot = 0.0f;
+      for (int w = 0; w < nw; ++w) tot += rd[w];
+      const __half mh = __float2half_rn(tot / (float)K);
+      m32 = 32.0f * __half2float(mh);
+      if (t == 0) mu[row] = mh;
+    }
+    uint8_t* crow = codes + row * (int64_t)(K >> 1);
+    uint8_t* srow_sc = scales + row * (int64_t)nb;
+    // straight-line over the wave's chunks (a chunk past the row's end gathers element 0
+    // and is not stored), so the gathers, MFMAs and lane exchanges of different chunks
+    // can overlap
+    float y[CW][8];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      v8h b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t pi = (pidx[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        b[i] = __builtin_bit_cast(_Float16, sr[pi]);
+      }
+      mfma_block_transform<false>(xf, b, y[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int ch = wid + nw * c;
+      const int blk = 16 * ch + bl;
+      if (CENTER && q == 0) y[c][0] -= m32;     // output 0 of the block
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[c][i] = __builtin_fmaf(y[c][i], coef[c][i], 0.0f);   // +0 for an exact zero
+      uint32_t w, sb;
+      int off;
+      mx_pack_block(y[c], q, w, off, sb);
+      if (ch < nchunk && blk < nb) {
+        *reinterpret_cast<uint32_t*>(crow + 16 * blk + off) = w;
+        if (q == 0) srow_sc[blk] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, const KronFactors& f, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
+  constexpr int U = 4;
+  const int64_t nchunks = (nblocks + 15) / 16;
+  const int64_t waves = (nchunks + U - 1) / U;
+  int64_t grid = (waves + 3) / 4;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (kron)
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, true>), dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(X), nblocks, f, codes, scales);
+  else
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, false>), dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(X), nblocks, f, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
+                               const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
+  // waves per row: enough that each handles at most 3 chunks of 16 blocks; threads must
+  // also cover the row's 16-byte chunks in at most 4 loads each
+  const int nb = (int)(K / 32), nchunk = (nb + 15) / 16, G = (int)(K / 8);
+  int waves = (nchunk + 2) / 3;
+  while (waves * 64 * 4 < G) ++waves;
+  if (waves > 8) return hipErrorInvalidValue;
+  const int cw = (nchunk + waves - 1) / waves;
+  const size_t lds = (size_t)K * 4 + 2 * 16 * sizeof(float);
+  int64_t grid = M;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (grid > cap) grid = cap;
+  const dim3 g((unsigned)grid), b((unsigned)(64 * waves));
+#define KQ_RPBH_CASE(C, CWV)                                                                                       \
+  hipLaunchKernelGGL((rpbh_mx_mfma_row_kernel<C, CWV>), g, b, lds, s, X, M, (int)K, perm, sign, codes, scales, mu)
+  if (center) {
+    if (cw <= 1) KQ_RPBH_CASE(true, 1); else if (cw == 2) KQ_RPBH_CASE(true, 2); else KQ_RPBH_CASE(true, 3);
+  } else {
+    if (cw <= 1) KQ_RPBH_CASE(false, 1); else if (cw == 2) KQ_RPBH_CASE(false, 2); else KQ_RPBH_CASE(false, 3);
+  }
+#undef KQ_RPBH_CASE
+  return hipGetLastError();
 }
 
 int device_cu_count() {
@@ -306,12 +651,21 @@ static hipError_t row_launch_ng(int ng, unsigned grid, unsigned threads, size_t 
                                 int K, const KronFactors& f, const int32_t* perm, const int8_t* sign,
                                 uint8_t* codes, void* scales, __half* mu, hipStream_t s) {
   const LmTables& lm = lm_tables();
+#define KQ_ROW_CASE(NGV)                                                                                        \
+  case NGV:                                                                                                     \
+    hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, NGV>), dim3(grid), dim3(threads), lds, s, X, M, K, f, \
+                       perm, sign, lm, codes, scales, mu);                                                      \
+    break;
   switch (ng) {
-    case 1: hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 1>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm, sign, lm, codes, scales, mu); break;
-    case 2: hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 2>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm, sign, lm, codes, scales, mu); break;
-    case 3: hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 3>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm, sign, lm, codes, scales, mu); break;
-    default: hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 4>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm, sign, lm, codes, scales, mu); break;
+    KQ_ROW_CASE(1)
+    KQ_ROW_CASE(2)
+    KQ_ROW_CASE(3)
+    default:
+      hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 4>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm,
+                         sign, lm, codes, scales, mu);
+      break;
   }
+#undef KQ_ROW_CASE
   return hipGetLastError();
 }
 
@@ -330,13 +684,16 @@ static hipError_t row_launch_kind(int fmt, bool center, int ng, unsigned grid, u
 hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int64_t M, int64_t K,
                             const KronFactors& f, const int32_t* perm, const int8_t* sign, uint8_t* codes,
                             void* scales, __half* mu, hipStream_t s) {
+  // threads per row: the smallest multiple of 64 (at most 512) that leaves each thread at
+  // most 4 groups of 8 elements; small workgroups keep many rows resident per CU
   const int G = (int)(K / 8);
-  int threads = ((G + 63) / 64) * 64;
-  if (threads > 1024) threads = 1024;
-  const int ng = (G + threads - 1) / threads;       // <= 4 for K <= 32768
-  const size_t lds = (kind == 2 ? (size_t)K * 2 : 0) + 64 * sizeof(float);
+  int threads = 64;
+  while (threads < 512 && (G + threads - 1) / threads > 4) threads += 64;
+  const int ng = (G + threads - 1) / threads;
+  if (ng > 4) return hipErrorInvalidValue;          // K > 16384 on the row path is rejected by the caller
+  const size_t lds = (kind == 2 ? (size_t)K * 4 : 0) + 2 * 32 * sizeof(float);
   int64_t grid = M;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
   if (grid > cap) grid = cap;
   switch (kind) {
     case 1: return row_launch_kind<1>(fmt, center, ng, (unsigned)grid, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
