@@ -114,8 +114,8 @@ kq_status kq_lloyd_max_levels(int32_t n, double* levels_out);
  *                        (a value on a threshold takes the smaller magnitude).
  * X fp16 [M][K]; codes u8 [M][K/2]; scales u8 [M][K/32] (MXFP4) or f32 [M] (LM4);
  * mu fp16 [M], required iff center != 0 (else ignored).
- * K % 32 == 0; K <= 16384 when centring, RPBH or LM4 is used (rows are staged on chip;
- * K <= 16320 for RPBH).
+ * K % 32 == 0; K <= 16384 when centring, RPBH or LM4 is used (rows are staged on
+ * chip).
  * All device pointers 16-byte aligned except mu and scales (4-byte for LM4). */
 kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
                                 const void* X, int64_t M, int64_t K,

@@ -156,7 +156,6 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   const bool stream_path = mx && !center && xf->kind != KQ_XFORM_RPBH_32;
   const bool rpbh_mfma = mx && xf->kind == KQ_XFORM_RPBH_32;
   if (!stream_path && K > 16384) return KQ_ERR_UNSUPPORTED;
-  if (xf->kind == KQ_XFORM_RPBH_32 && K > 16320) return KQ_ERR_UNSUPPORTED;  // two rows staged in 64 KiB of LDS
   hipError_t e;
   if (stream_path) {
     e = launch_kron_mx_mfma(xf->kind == KQ_XFORM_KRON_4X8, static_cast<const __half*>(X), M * (K / 32), f, codes,

@@ -11,6 +11,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));   // 16 raw bytes (a native vector: copies stay in registers)
 
 // DPP quad_perm control word: lane i of each quad reads lane sel[i] of the same quad.
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
@@ -68,6 +69,20 @@ __device__ __forceinline__ void unpack8_f16(const uint4& raw, float* x) {
     x[2 * i] = f.x;
     x[2 * i + 1] = f.y;
   }
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it does not
+// wait for this wave's outstanding global loads, so prefetches stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void unpack8_f16(const v4u& raw, float* x) {
+  const v8h h = __builtin_bit_cast(v8h, raw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
 }
 
 // Sum over a wavefront (every lane gets the result).

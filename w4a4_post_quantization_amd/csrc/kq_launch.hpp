@@ -63,5 +63,7 @@ hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t
                             hipStream_t s);
 
 int device_cu_count();
+// Workgroups of `kernel` that can be resident on one compute unit at once.
+int resident_blocks_per_cu(const void* kernel, int threads, size_t lds);
 
 }  // namespace kq

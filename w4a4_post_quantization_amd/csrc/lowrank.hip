@@ -30,15 +30,20 @@ __global__ __launch_bounds__(64 * SPLIT, 1) void lowrank_down_kernel(const __hal
   const __half* lr[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) lr[t] = L1 + (int64_t)(16 * t + (lane & 15)) * K + 8 * q;
+  // workgroups start at different k-steps so that they do not all read the same lines of
+  // L1 at the same moment (a rotation of the k order; the sum is over the same terms)
+  const int64_t rot = ((int64_t)blockIdx.x * 7 * SPLIT) % nk;
   for (int64_t s0 = w; s0 < nk; s0 += SPLIT * BATCH) {
     v8h a[BATCH], b[BATCH][RT];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int64_t s = s0 + (int64_t)u * SPLIT;
       const bool ok = s < nk;
-      a[u] = ok ? *reinterpret_cast<const v8h*>(xr + 32 * s) : v8h{};
+      int64_t ks = s + rot;
+      ks = ks >= nk ? ks - nk : ks;
+      a[u] = ok ? *reinterpret_cast<const v8h*>(xr + 32 * ks) : v8h{};
 #pragma unroll
-      for (int t = 0; t < RT; ++t) b[u][t] = ok ? *reinterpret_cast<const v8h*>(lr[t] + 32 * s) : v8h{};
+      for (int t = 0; t < RT; ++t) b[u][t] = ok ? *reinterpret_cast<const v8h*>(lr[t] + 32 * ks) : v8h{};
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)

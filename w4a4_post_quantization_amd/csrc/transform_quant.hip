@@ -15,6 +15,10 @@
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 namespace kq {
 
 // 1/sqrt(32) rounded to float.
@@ -391,10 +395,12 @@ __device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& d
   h0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h0, y[2], y[3], sc, 1);      // bytes 2q, 2q+1
   uint32_t h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[4], y[5], sc, 0);
   h1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h1, y[6], y[7], sc, 1);      // bytes 8+2q, 8+2q+1
-  const bool odd = q & 1;
-  const uint32_t r = (uint32_t)__shfl_xor((int)(odd ? h0 : h1), 16, 64);
-  dword = odd ? (r | (h1 << 16)) : (h0 | (r << 16));
-  byte_off = odd ? 8 + 2 * (q - 1) : 2 * q;
+  // lanes of an even row (q even) keep h0 and receive the odd partner's h0; lanes of an
+  // odd row receive the even partner's h1 and keep h1 -- one row swap of the two registers
+  // (the odd rows of the first with the even rows of the second)
+  const auto sw = __builtin_amdgcn_permlane16_swap(h0, h1, false, false);
+  dword = sw[0] | (sw[1] << 16);
+  byte_off = (q & 1) ? 8 + 2 * (q - 1) : 2 * q;
   scale_byte = sb;
 }
 
@@ -448,132 +454,177 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
   }
 }
 
-// Row-staged RPBH + MXFP4 on the matrix cores, optional centring.  A workgroup walks token
-// rows; each row is staged in LDS (two buffers, ping-pong) for the full-K permutation
-// gather, and wavefront w transforms the 16-block chunks w, w+W, ... of the row.
+// Row-staged RPBH + MXFP4 on the matrix cores, optional centring.  Workgroups are
+// persistent (one launch fills the chip once) and build, once, an LDS gather table of
+// the permutation (u16 per element) and a sign bitmask per block, so the per-row work
+// is only the row itself.  WPR wavefronts share a row (NR = 8 / WPR rows in flight per
+// workgroup, each in its own LDS slot); with WPR = 1 every wavefront owns its rows and
+// needs no workgroup barrier.  A wavefront loads its share of the next row into
+// registers while it transforms the current one.
 // Centring is applied after the rotation: (x - mu 1) H32 = x H32 - 32 mu e_0 for the
 // Sylvester matrix (every column but the first sums to zero), so only output 0 of each
 // block is corrected; the result is the same linear map as centring first.
-template <bool CENTER, int CW>
-__global__ __launch_bounds__(512) void rpbh_mx_mfma_row_kernel(const __half* __restrict__ X, int64_t M, int K,
-                                                               const int32_t* __restrict__ perm,
-                                                               const int8_t* __restrict__ sign,
-                                                               uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ scales, __half* __restrict__ mu) {
+constexpr int RPBH_WAVES = 8;
+constexpr int RPBH_LMAX = 6;   // 16-byte row chunks per lane per row, at most
+
+__host__ __device__ constexpr size_t rpbh_lds_bytes(int wpr, int K) {
+  return (size_t)(RPBH_WAVES / wpr) * K * 2 + (size_t)K * 2 + (size_t)(K / 32) * 4 + RPBH_WAVES * 4;
+}
+
+struct RowChunks {
+  v4u v[RPBH_LMAX];
+};
+
+// The lane's 16-byte chunks cidx[] of row `row` (rows past M read row M-1).
+__device__ __forceinline__ RowChunks rpbh_load_row(const __half* __restrict__ X, int64_t row, int64_t M, int K,
+                                                   const int* cidx) {
+  const v4u* xr = reinterpret_cast<const v4u*>(X + (row < M ? row : M - 1) * (int64_t)K);
+  RowChunks r;
+#pragma unroll
+  for (int j = 0; j < RPBH_LMAX; ++j) r.v[j] = xr[cidx[j]];
+  return r;
+}
+
+template <bool CENTER, int WPR>
+__global__ __launch_bounds__(64 * RPBH_WAVES) void rpbh_mx_mfma_rows_kernel(
+    const __half* __restrict__ X, int64_t M, int K, const int32_t* __restrict__ perm,
+    const int8_t* __restrict__ sign, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    __half* __restrict__ mu) {
+  constexpr int NR = RPBH_WAVES / WPR;
   extern __shared__ __align__(16) unsigned char smem[];
-  __half* const srow0 = reinterpret_cast<__half*>(smem);             // [2][K]
-  float* red = reinterpret_cast<float*>(smem + (size_t)K * 4);      // [2][16] wave partial sums
-  const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wid = t >> 6, nw = T >> 6;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int rs = wid / WPR, wr = wid % WPR;   // row slot of this wave, its index within the row
   const int q = lane >> 4, bl = lane & 15;
   const int G = K >> 3, nb = K >> 5, nchunk = (nb + 15) >> 4;
-  const MfmaXform xf = mfma_xform_hadamard(lane);
+  __half* const rows = reinterpret_cast<__half*>(smem);                                        // [NR][K]
+  uint16_t* const tab = reinterpret_cast<uint16_t*>(smem + (size_t)NR * K * 2);               // [K]
+  uint32_t* const smask = reinterpret_cast<uint32_t*>(smem + (size_t)NR * K * 2 + (size_t)K * 2);   // [nb]
+  float* const red = reinterpret_cast<float*>(smask + nb);                                    // [8]
 
-  // per chunk of this wave: the gather indices of the lane's eight inputs (two per dword)
-  // and the output coefficients d_j / sqrt(32) of its eight outputs
-  uint32_t pidx[CW][4];
-  float coef[CW][8];
+  __half* const slot = rows + (size_t)rs * K;
+  const int nl = (G + 64 * WPR - 1) / (64 * WPR);
+  // Loads and LDS writes use clamped indices instead of conditions (a lane past the end
+  // repeats the last chunk, rows past M repeat row M-1, chunks j >= nl -- only when
+  // K < 3072 WPR -- repeat chunk nl - 1, and the duplicate writes carry identical data),
+  // so no load is placed in a branch together with its consumer.
+  int cidx[RPBH_LMAX];
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    const int ch = wid + nw * c;
-    const int blk = 16 * ch + bl;
-    const bool v = ch < nchunk && blk < nb;
-    // inputs 8q..8q+7 of block blk: 32 contiguous bytes of perm; outputs 4q..4q+3 and
-    // 16+4q..16+4q+3: two groups of 4 contiguous sign bytes
-    uint4 p0 = make_uint4(0u, 0u, 0u, 0u), p1 = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t sg0 = 0x01010101u, sg1 = 0x01010101u;
-    if (v) {
-      p0 = *reinterpret_cast<const uint4*>(perm + 32 * blk + 8 * q);
-      p1 = *reinterpret_cast<const uint4*>(perm + 32 * blk + 8 * q + 4);
-      sg0 = *reinterpret_cast<const uint32_t*>(sign + 32 * blk + 4 * q);
-      sg1 = *reinterpret_cast<const uint32_t*>(sign + 32 * blk + 16 + 4 * q);
-    }
-    pidx[c][0] = p0.x | (p0.y << 16);
-    pidx[c][1] = p0.z | (p0.w << 16);
-    pidx[c][2] = p1.x | (p1.y << 16);
-    pidx[c][3] = p1.z | (p1.w << 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      coef[c][i] = ((sg0 >> (8 * i)) & 0x80u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
-      coef[c][4 + i] = ((sg1 >> (8 * i)) & 0x80u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
-    }
+  for (int j = 0; j < RPBH_LMAX; ++j) {
+    const int c = wr * 64 + lane + 64 * WPR * (j < nl ? j : nl - 1);
+    cidx[j] = c < G ? c : G - 1;
   }
+  RowChunks raw;
+  const int64_t stride = (int64_t)gridDim.x * NR;
+  int64_t base = (int64_t)blockIdx.x * NR;
 
-  constexpr int NL = 4;   // row chunks of 16 bytes per thread, at most
-  uint4 raw[NL];
-  const int nl = (G + T - 1) / T;
-  auto load_row = [&](int64_t row) {
-    const uint4* xr = reinterpret_cast<const uint4*>(X + row * (int64_t)K);
+  // gather table (u16 per element) and sign masks (bit j of smask[b]: d_{32b+j} < 0).
+  // Every load of the set-up and of the first row is issued before any is waited for.
+  // 16-byte perm chunks per thread: K <= 3072 WPR (so that G <= 384 WPR) and K <= 16384
+  constexpr int PV = WPR == 1 ? 2 : WPR == 2 ? 3 : WPR == 4 ? 6 : 8;
+  uint4 pv[PV];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int g = t + T * j;
-      raw[j] = (j < nl && row < M && g < G) ? xr[g] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  int64_t row = blockIdx.x;
-  load_row(row);
-  for (int it = 0; row < M; row += gridDim.x, ++it) {
-    const int buf = it & 1;
-    __half* const sr = srow0 + buf * K;
+  for (int i = 0; i < PV; ++i) {
+    const int c = min(t + 64 * RPBH_WAVES * i, (K >> 2) - 1);
+    pv[i] = reinterpret_cast<const uint4*>(perm)[c];
+  }
+  const int sb_ = min(t, nb - 1);                      // this thread's block of sign bytes (nb <= 512)
+  uint32_t sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = reinterpret_cast<const uint32_t*>(sign + 32 * sb_)[i];
+  raw = rpbh_load_row(X, base + rs, M, K, cidx);
+#pragma unroll
+  for (int i = 0; i < PV; ++i) {
+    const int c = min(t + 64 * RPBH_WAVES * i, (K >> 2) - 1);
+    reinterpret_cast<uint2*>(tab)[c] = make_uint2((pv[i].x & 0xFFFFu) | (pv[i].y << 16),
+                                                    (pv[i].z & 0xFFFFu) | (pv[i].w << 16));
+  }
+  {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m |= ((sv[i] >> (8 * k + 7)) & 1u) << (4 * i + k);
+    smask[sb_] = m;
+  }
+  const MfmaXform xf = mfma_xform_hadamard(lane);
+  lds_barrier();     // the table is visible; the row loads stay in flight
+
+  for (; base < M; base += stride) {
+    const int64_t row = base + rs;
+    if (WPR > 1) lds_barrier();          // the previous row's gathers are done
     float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int g = t + T * j;
-      if (j < nl && g < G) {
-        reinterpret_cast<uint4*>(sr)[g] = raw[j];
-        if (CENTER) {
-          float x[8];
-          unpack8_f16(raw[j], x);
+    for (int j = 0; j < RPBH_LMAX; ++j) {
+      reinterpret_cast<v4u*>(slot)[cidx[j]] = raw.v[j];    // repeated chunks rewrite identical data
+      if (CENTER) {
+        float x[8];
+        unpack8_f16(raw.v[j], x);
+        float ps = 0.0f;
 #pragma unroll
-          for (int m = 0; m < 8; ++m) psum += x[m];
-        }
+        for (int m = 0; m < 8; ++m) ps += x[m];
+        const bool counted = j < nl && wr * 64 + lane + 64 * WPR * j < G;   // a repeated chunk is not
+        psum += counted ? ps : 0.0f;
       }
     }
-    load_row(row + gridDim.x);            // prefetch the next row while this one is processed
-    float* rd = red + buf * 16;
-    if (CENTER) {
-      const float sw = wave_sum(psum);
-      if (lane == 0) rd[wid] = sw;
+    raw = rpbh_load_row(X, row + stride, M, K, cidx);   // prefetch this wave's next row
+    float tot = 0.0f;
+    if (CENTER) tot = wave_sum(psum);
+    if (WPR > 1) {
+      if (CENTER && lane == 0) red[wid] = tot;
+      lds_barrier();
+      if (CENTER) {
+        tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) tot += red[rs * WPR + w];
+      }
+    } else {
+      // the row slot is private to this wavefront: its LDS writes complete before its
+      // later LDS reads, so no barrier is needed, only no reordering by the compiler
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     float m32 = 0.0f;
     if (CENTER) {
-      float tot = 0.0f;
-      for (int w = 0; w < nw; ++w) tot += rd[w];
       const __half mh = __float2half_rn(tot / (float)K);
       m32 = 32.0f * __half2float(mh);
-      if (t == 0) mu[row] = mh;
+      if (row < M && wr == 0 && lane == 0) mu[row] = mh;
     }
-    uint8_t* crow = codes + row * (int64_t)(K >> 1);
-    uint8_t* srow_sc = scales + row * (int64_t)nb;
-    // straight-line over the wave's chunks (a chunk past the row's end gathers element 0
-    // and is not stored), so the gathers, MFMAs and lane exchanges of different chunks
-    // can overlap
-    float y[CW][8];
+    uint8_t* const crow = codes + row * (int64_t)(K >> 1);
+    uint8_t* const srow_sc = scales + row * (int64_t)nb;
+    // chunks wr, wr + WPR, ... of the row, two at a time
+    for (int ch0 = wr; ch0 < nchunk; ch0 += 2 * WPR) {
+      float y[2][8];
+      int blk[2];
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      v8h b;
+      for (int u = 0; u < 2; ++u) {
+        blk[u] = 16 * (ch0 + u * WPR) + bl;
+        const int bb = blk[u] < nb ? blk[u] : 0;    // lanes past the row's end gather block 0, not stored
+        const uint4 ix = *reinterpret_cast<const uint4*>(tab + 32 * bb + 8 * q);
+        const uint32_t iw[4] = {ix.x, ix.y, ix.z, ix.w};
+        v8h b;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t pi = (pidx[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        b[i] = __builtin_bit_cast(_Float16, sr[pi]);
+        for (int i = 0; i < 8; ++i)
+          b[i] = __builtin_bit_cast(_Float16, slot[(iw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu]);
+        mfma_block_transform<false>(xf, b, y[u]);
+        const uint32_t sm = smask[bb];
+        if (CENTER && q == 0) y[u][0] -= m32;     // output 0 of the block
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
+          const float c = ((sm >> j) & 1u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
+          y[u][i] = __builtin_fmaf(y[u][i], c, 0.0f);   // +0 for an exact zero
+        }
       }
-      mfma_block_transform<false>(xf, b, y[c]);
-    }
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int ch = wid + nw * c;
-      const int blk = 16 * ch + bl;
-      if (CENTER && q == 0) y[c][0] -= m32;     // output 0 of the block
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[c][i] = __builtin_fmaf(y[c][i], coef[c][i], 0.0f);   // +0 for an exact zero
-      uint32_t w, sb;
-      int off;
-      mx_pack_block(y[c], q, w, off, sb);
-      if (ch < nchunk && blk < nb) {
-        *reinterpret_cast<uint32_t*>(crow + 16 * blk + off) = w;
-        if (q == 0) srow_sc[blk] = (uint8_t)sb;
+      for (int u = 0; u < 2; ++u) {
+        uint32_t w, sb;
+        int off;
+        mx_pack_block(y[u], q, w, off, sb);
+        if (row < M && ch0 + u * WPR < nchunk && blk[u] < nb) {
+          *reinterpret_cast<uint32_t*>(crow + 16 * blk[u] + off) = w;
+          if (q == 0) srow_sc[blk[u]] = (uint8_t)sb;
+        }
       }
     }
   }
@@ -597,29 +648,53 @@ hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, cons
   return hipGetLastError();
 }
 
+template <bool CENTER, int WPR>
+static hipError_t rpbh_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
+                              uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
+  const size_t lds = rpbh_lds_bytes(WPR, K);
+  // one resident wave of workgroups: as many as fit on the chip at once, at most one
+  // per group of NR rows
+  constexpr int NR = RPBH_WAVES / WPR;
+  int64_t grid = (M + NR - 1) / NR;
+  const int64_t cap = (int64_t)device_cu_count() *
+                      resident_blocks_per_cu(reinterpret_cast<const void*>(&rpbh_mx_mfma_rows_kernel<CENTER, WPR>),
+                                             64 * RPBH_WAVES, lds);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((rpbh_mx_mfma_rows_kernel<CENTER, WPR>), dim3((unsigned)grid), dim3(64 * RPBH_WAVES), lds, s, X,
+                     M, K, perm, sign, codes, scales, mu);
+  return hipGetLastError();
+}
+
+template <bool CENTER>
+static hipError_t rpbh_launch_wpr(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
+                                  uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
+  // waves per row: the fewest that keep each lane at <= RPBH_LMAX 16-byte chunks of a row
+  const int G = K / 8;
+  if (G <= 64 * RPBH_LMAX) return rpbh_launch<CENTER, 1>(X, M, K, perm, sign, codes, scales, mu, s);
+  if (G <= 128 * RPBH_LMAX) return rpbh_launch<CENTER, 2>(X, M, K, perm, sign, codes, scales, mu, s);
+  if (G <= 256 * RPBH_LMAX) return rpbh_launch<CENTER, 4>(X, M, K, perm, sign, codes, scales, mu, s);
+  if (G <= 512 * RPBH_LMAX) return rpbh_launch<CENTER, 8>(X, M, K, perm, sign, codes, scales, mu, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
-  // waves per row: enough that each handles at most 3 chunks of 16 blocks; threads must
-  // also cover the row's 16-byte chunks in at most 4 loads each
-  const int nb = (int)(K / 32), nchunk = (nb + 15) / 16, G = (int)(K / 8);
-  int waves = (nchunk + 2) / 3;
-  while (waves * 64 * 4 < G) ++waves;
-  if (waves > 8) return hipErrorInvalidValue;
-  const int cw = (nchunk + waves - 1) / waves;
-  const size_t lds = (size_t)K * 4 + 2 * 16 * sizeof(float);
-  int64_t grid = M;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
-  if (grid > cap) grid = cap;
-  const dim3 g((unsigned)grid), b((unsigned)(64 * waves));
-#define KQ_RPBH_CASE(C, CWV)                                                                                       \
-  hipLaunchKernelGGL((rpbh_mx_mfma_row_kernel<C, CWV>), g, b, lds, s, X, M, (int)K, perm, sign, codes, scales, mu)
-  if (center) {
-    if (cw <= 1) KQ_RPBH_CASE(true, 1); else if (cw == 2) KQ_RPBH_CASE(true, 2); else KQ_RPBH_CASE(true, 3);
-  } else {
-    if (cw <= 1) KQ_RPBH_CASE(false, 1); else if (cw == 2) KQ_RPBH_CASE(false, 2); else KQ_RPBH_CASE(false, 3);
-  }
-#undef KQ_RPBH_CASE
-  return hipGetLastError();
+  if (K > 65536) return hipErrorInvalidValue;    // u16 gather indices
+  return center ? rpbh_launch_wpr<true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
+                : rpbh_launch_wpr<false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+}
+
+int resident_blocks_per_cu(const void* kernel, int threads, size_t lds) {
+  static std::mutex mtx;
+  static std::map<std::tuple<const void*, int, size_t>, int> cache;
+  const auto key = std::make_tuple(kernel, threads, lds);
+  std::lock_guard<std::mutex> lock(mtx);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
+  cache.emplace(key, n);
+  return n;
 }
 
 int device_cu_count() {
@@ -646,39 +721,44 @@ hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFac
   return hipGetLastError();
 }
 
-template <int KIND, int FMT, bool CENTER>
-static hipError_t row_launch_ng(int ng, unsigned grid, unsigned threads, size_t lds, const __half* X, int64_t M,
-                                int K, const KronFactors& f, const int32_t* perm, const int8_t* sign,
-                                uint8_t* codes, void* scales, __half* mu, hipStream_t s) {
-  const LmTables& lm = lm_tables();
-#define KQ_ROW_CASE(NGV)                                                                                        \
-  case NGV:                                                                                                     \
-    hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, NGV>), dim3(grid), dim3(threads), lds, s, X, M, K, f, \
-                       perm, sign, lm, codes, scales, mu);                                                      \
-    break;
-  switch (ng) {
-    KQ_ROW_CASE(1)
-    KQ_ROW_CASE(2)
-    KQ_ROW_CASE(3)
-    default:
-      hipLaunchKernelGGL((row_quant_kernel<KIND, FMT, CENTER, 4>), dim3(grid), dim3(threads), lds, s, X, M, K, f, perm,
-                         sign, lm, codes, scales, mu);
-      break;
-  }
-#undef KQ_ROW_CASE
+template <int KIND, int FMT, bool CENTER, int NG>
+static hipError_t row_launch(unsigned threads, size_t lds, const __half* X, int64_t M, int K, const KronFactors& f,
+                             const int32_t* perm, const int8_t* sign, uint8_t* codes, void* scales, __half* mu,
+                             hipStream_t s) {
+  // persistent workgroups (one resident wave of them): the per-row gather indices are
+  // set up once per workgroup
+  const auto kern = row_quant_kernel<KIND, FMT, CENTER, NG>;
+  int64_t grid = M;
+  const int64_t cap = (int64_t)device_cu_count() *
+                      resident_blocks_per_cu(reinterpret_cast<const void*>(kern), (int)threads, lds);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, f, perm, sign, lm_tables(), codes,
+                     scales, mu);
   return hipGetLastError();
 }
 
-template <int KIND>
-static hipError_t row_launch_kind(int fmt, bool center, int ng, unsigned grid, unsigned threads, size_t lds,
-                                  const __half* X, int64_t M, int K, const KronFactors& f, const int32_t* perm,
-                                  const int8_t* sign, uint8_t* codes, void* scales, __half* mu, hipStream_t s) {
-  if (fmt == 0) {
-    return center ? row_launch_ng<KIND, 0, true>(ng, grid, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s)
-                  : row_launch_ng<KIND, 0, false>(ng, grid, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+template <int KIND, int FMT, bool CENTER>
+static hipError_t row_launch_ng(int ng, unsigned threads, size_t lds, const __half* X, int64_t M, int K,
+                                const KronFactors& f, const int32_t* perm, const int8_t* sign, uint8_t* codes,
+                                void* scales, __half* mu, hipStream_t s) {
+  switch (ng) {
+    case 1: return row_launch<KIND, FMT, CENTER, 1>(threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+    case 2: return row_launch<KIND, FMT, CENTER, 2>(threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+    case 3: return row_launch<KIND, FMT, CENTER, 3>(threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+    default: return row_launch<KIND, FMT, CENTER, 4>(threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
   }
-  return center ? row_launch_ng<KIND, 1, true>(ng, grid, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s)
-                : row_launch_ng<KIND, 1, false>(ng, grid, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+}
+
+template <int KIND>
+static hipError_t row_launch_kind(int fmt, bool center, int ng, unsigned threads, size_t lds, const __half* X,
+                                  int64_t M, int K, const KronFactors& f, const int32_t* perm, const int8_t* sign,
+                                  uint8_t* codes, void* scales, __half* mu, hipStream_t s) {
+  if (fmt == 0) {
+    return center ? row_launch_ng<KIND, 0, true>(ng, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s)
+                  : row_launch_ng<KIND, 0, false>(ng, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
+  }
+  return center ? row_launch_ng<KIND, 1, true>(ng, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s)
+                : row_launch_ng<KIND, 1, false>(ng, threads, lds, X, M, K, f, perm, sign, codes, scales, mu, s);
 }
 
 hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int64_t M, int64_t K,
@@ -687,18 +767,15 @@ hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int
   // threads per row: the smallest multiple of 64 (at most 512) that leaves each thread at
   // most 4 groups of 8 elements; small workgroups keep many rows resident per CU
   const int G = (int)(K / 8);
-  int threads = 64;
+  unsigned threads = 64;
   while (threads < 512 && (G + threads - 1) / threads > 4) threads += 64;
-  const int ng = (G + threads - 1) / threads;
+  const int ng = (int)((G + threads - 1) / threads);
   if (ng > 4) return hipErrorInvalidValue;          // K > 16384 on the row path is rejected by the caller
   const size_t lds = (kind == 2 ? (size_t)K * 4 : 0) + 2 * 32 * sizeof(float);
-  int64_t grid = M;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
-  if (grid > cap) grid = cap;
   switch (kind) {
-    case 1: return row_launch_kind<1>(fmt, center, ng, (unsigned)grid, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
-    case 2: return row_launch_kind<2>(fmt, center, ng, (unsigned)grid, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
-    default: return row_launch_kind<0>(fmt, center, ng, (unsigned)grid, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
+    case 1: return row_launch_kind<1>(fmt, center, ng, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
+    case 2: return row_launch_kind<2>(fmt, center, ng, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
+    default: return row_launch_kind<0>(fmt, center, ng, threads, lds, X, M, (int)K, f, perm, sign, codes, scales, mu, s);
   }
 }
 

@@ -27,12 +27,6 @@ namespace kq {
 // MFMA fragment reads (16 rows x one chunk) and the staging writes hit distinct banks.
 __device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [base, base + bytes): loads past the end return zeros and stores
