@@ -29,6 +29,16 @@ __device__ __forceinline__ float quad_bcast(float v) { return dpp_f<quad_perm(I,
 __device__ __forceinline__ float quad_xor1(float v) { return dpp_f<quad_perm(1, 0, 3, 2)>(v); }
 __device__ __forceinline__ float quad_xor2(float v) { return dpp_f<quad_perm(2, 3, 0, 1)>(v); }
 
+// Sum over the 16 lanes of a DPP row (every lane of the row gets the result): rotations
+// by 8 and 4 within the row, then the two quad exchanges.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);   // row_ror:8
+  v += dpp_f<0x124>(v);   // row_ror:4
+  v += quad_xor2(v);
+  v += quad_xor1(v);
+  return v;
+}
+
 // Max over the four lanes of a quad (every lane gets the result).
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, quad_xor1(v));
@@ -84,6 +94,23 @@ __device__ __forceinline__ void unpack8_f16(const v4u& raw, float* x) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
 }
+
+// acc + (lo half + hi half) of a packed fp16 pair, in fp32 (the products by 1 are exact).
+// The pair is taken by value: a bit cast applied directly to an element of a vector
+// variable has been seen to read element 0 for every index.
+__device__ __forceinline__ float add_f16x2(uint32_t pair, float acc) {
+  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pair), (h2){1.0f, 1.0f}, acc, false);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros and stores
+// past the end are dropped, which handles ragged tiles and masked lanes without branches
+// (a masked lane uses an offset of at least KQ_OOB).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+#define KQ_OOB 0x7FFFFFF0
 
 // Sum over a wavefront (every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {

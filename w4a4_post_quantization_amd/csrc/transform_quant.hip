@@ -454,177 +454,262 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
   }
 }
 
-// Row-staged RPBH + MXFP4 on the matrix cores, optional centring.  Workgroups are
-// persistent (one launch fills the chip once) and build, once, an LDS gather table of
-// the permutation (u16 per element) and a sign bitmask per block, so the per-row work
-// is only the row itself.  WPR wavefronts share a row (NR = 8 / WPR rows in flight per
-// workgroup, each in its own LDS slot); with WPR = 1 every wavefront owns its rows and
-// needs no workgroup barrier.  A wavefront loads its share of the next row into
-// registers while it transforms the current one.
+// Row-group RPBH + MXFP4 on the matrix cores, optional centring.  R consecutive token
+// rows are staged together in LDS, interleaved element by element ([k][r]: R halves per
+// position), so one LDS read of 2R bytes gathers a permuted position for all R rows, and
+// the gather table and sign masks (built once per persistent workgroup) serve R rows per
+// read.  A workgroup of NW wavefronts holds one group: lane t loads 16-byte columns
+// t, t + 64 NW of each of the R rows, transposes them in registers and writes them
+// interleaved; the next group's columns are loaded while the current group is
+// transformed.  Wavefront w transforms the 16-block chunks w and w + NW of all R rows.
 // Centring is applied after the rotation: (x - mu 1) H32 = x H32 - 32 mu e_0 for the
 // Sylvester matrix (every column but the first sums to zero), so only output 0 of each
 // block is corrected; the result is the same linear map as centring first.
-constexpr int RPBH_WAVES = 8;
-constexpr int RPBH_LMAX = 6;   // 16-byte row chunks per lane per row, at most
+constexpr int RG_MAXW = 16;   // wavefronts per workgroup, at most
+constexpr int RG_COLS = 2;    // 16-byte columns of a row per lane, at most (64 NW >= K / 16)
+constexpr int RG_PV = 4;      // 16-byte perm chunks per lane in the set-up, at most
 
-__host__ __device__ constexpr size_t rpbh_lds_bytes(int wpr, int K) {
-  return (size_t)(RPBH_WAVES / wpr) * K * 2 + (size_t)K * 2 + (size_t)(K / 32) * 4 + RPBH_WAVES * 4;
+__host__ __device__ constexpr size_t rg_red_offset(int R, int K) {
+  return ((size_t)R * K * 2 + (size_t)K * 2 + (size_t)(K / 32) * 4 + 15) & ~(size_t)15;
 }
+__host__ __device__ constexpr size_t rg_lds_bytes(int R, int K) { return rg_red_offset(R, K) + RG_MAXW * 16; }
 
-struct RowChunks {
-  v4u v[RPBH_LMAX];
+template <int R>
+struct GroupChunks {
+  v4u v[RG_COLS][R];
 };
 
-// The lane's 16-byte chunks cidx[] of row `row` (rows past M read row M-1).
-__device__ __forceinline__ RowChunks rpbh_load_row(const __half* __restrict__ X, int64_t row, int64_t M, int K,
-                                                   const int* cidx) {
-  const v4u* xr = reinterpret_cast<const v4u*>(X + (row < M ? row : M - 1) * (int64_t)K);
-  RowChunks r;
+// Columns col[] of rows row0 .. row0 + R - 1 (rows past M read row M - 1).
+template <int R>
+__device__ __forceinline__ GroupChunks<R> rg_load(const __half* X, int64_t row0, int64_t M, int K,
+                                                  const int* col) {
+  GroupChunks<R> g;
 #pragma unroll
-  for (int j = 0; j < RPBH_LMAX; ++j) r.v[j] = xr[cidx[j]];
-  return r;
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < M ? row0 + r : M - 1;
+    const v4u* xr = reinterpret_cast<const v4u*>(X + row * (int64_t)K);
+#pragma unroll
+    for (int j = 0; j < RG_COLS; ++j) g.v[j][r] = xr[col[j]];
+  }
+  return g;
 }
 
-template <bool CENTER, int WPR>
-__global__ __launch_bounds__(64 * RPBH_WAVES) void rpbh_mx_mfma_rows_kernel(
-    const __half* __restrict__ X, int64_t M, int K, const int32_t* __restrict__ perm,
+#define KQ_PERM_LO 0x05040100u   // (lo16 of s1, lo16 of s0)
+#define KQ_PERM_HI 0x07060302u   // (hi16 of s1, hi16 of s0)
+
+template <int R, bool CENTER>
+__global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
+    const __half* X, int64_t M, int K, const int32_t* __restrict__ perm,
     const int8_t* __restrict__ sign, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     __half* __restrict__ mu) {
-  constexpr int NR = RPBH_WAVES / WPR;
+  static_assert(R == 2 || R == 4, "rows per group");
   extern __shared__ __align__(16) unsigned char smem[];
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int rs = wid / WPR, wr = wid % WPR;   // row slot of this wave, its index within the row
+  const int t = threadIdx.x, T = blockDim.x, NW = T >> 6, lane = t & 63, wid = t >> 6;
   const int q = lane >> 4, bl = lane & 15;
-  const int G = K >> 3, nb = K >> 5, nchunk = (nb + 15) >> 4;
-  __half* const rows = reinterpret_cast<__half*>(smem);                                        // [NR][K]
-  uint16_t* const tab = reinterpret_cast<uint16_t*>(smem + (size_t)NR * K * 2);               // [K]
-  uint32_t* const smask = reinterpret_cast<uint32_t*>(smem + (size_t)NR * K * 2 + (size_t)K * 2);   // [nb]
-  float* const red = reinterpret_cast<float*>(smask + nb);                                    // [8]
+  const int cols = K >> 3, nb = K >> 5, nchunk = (nb + 15) >> 4;
+  unsigned char* const slot = smem;                                                       // [K][R] halves
+  uint16_t* const tab = reinterpret_cast<uint16_t*>(smem + (size_t)R * K * 2);            // [K]
+  uint32_t* const smask = reinterpret_cast<uint32_t*>(smem + (size_t)R * K * 2 + (size_t)K * 2);   // [nb]
+  float* const red = reinterpret_cast<float*>(smem + rg_red_offset(R, K));                // [NW][4]
 
-  __half* const slot = rows + (size_t)rs * K;
-  const int nl = (G + 64 * WPR - 1) / (64 * WPR);
-  // Loads and LDS writes use clamped indices instead of conditions (a lane past the end
-  // repeats the last chunk, rows past M repeat row M-1, chunks j >= nl -- only when
-  // K < 3072 WPR -- repeat chunk nl - 1, and the duplicate writes carry identical data),
-  // so no load is placed in a branch together with its consumer.
-  int cidx[RPBH_LMAX];
+  // this lane's columns (clamped: a lane past the end repeats the last column, whose
+  // duplicate LDS writes carry identical data)
+  int col[RG_COLS];
+  bool colv[RG_COLS];
 #pragma unroll
-  for (int j = 0; j < RPBH_LMAX; ++j) {
-    const int c = wr * 64 + lane + 64 * WPR * (j < nl ? j : nl - 1);
-    cidx[j] = c < G ? c : G - 1;
+  for (int j = 0; j < RG_COLS; ++j) {
+    const int c = t + T * j;
+    colv[j] = c < cols;
+    col[j] = colv[j] ? c : cols - 1;
   }
-  RowChunks raw;
-  const int64_t stride = (int64_t)gridDim.x * NR;
-  int64_t base = (int64_t)blockIdx.x * NR;
+  const int64_t ngroups = (M + R - 1) / R;
+  int64_t g = blockIdx.x;
 
-  // gather table (u16 per element) and sign masks (bit j of smask[b]: d_{32b+j} < 0).
-  // Every load of the set-up and of the first row is issued before any is waited for.
-  // 16-byte perm chunks per thread: K <= 3072 WPR (so that G <= 384 WPR) and K <= 16384
-  constexpr int PV = WPR == 1 ? 2 : WPR == 2 ? 3 : WPR == 4 ? 6 : 8;
-  uint4 pv[PV];
+  // set-up loads (perm chunks, the sign bytes of block t), then the first group's loads,
+  // all in flight together; then the gather table and sign masks
+  // (workgroups start the table at different chunks so that they do not all read the same
+  // lines at the same moment)
+  const int npc = K >> 2, rot = (int)((blockIdx.x * 61u) % (unsigned)npc);
+  v4u pv[RG_PV];
+  int pc[RG_PV];
 #pragma unroll
-  for (int i = 0; i < PV; ++i) {
-    const int c = min(t + 64 * RPBH_WAVES * i, (K >> 2) - 1);
-    pv[i] = reinterpret_cast<const uint4*>(perm)[c];
+  for (int i = 0; i < RG_PV; ++i) {
+    const int c = min(t + T * i, npc - 1);
+    pc[i] = c + rot < npc ? c + rot : c + rot - npc;
+    pv[i] = reinterpret_cast<const v4u*>(perm)[pc[i]];
   }
-  const int sb_ = min(t, nb - 1);                      // this thread's block of sign bytes (nb <= 512)
+  const int sbk = (int)((min(t, nb - 1) + blockIdx.x * 7u) % (unsigned)nb);
   uint32_t sv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sv[i] = reinterpret_cast<const uint32_t*>(sign + 32 * sb_)[i];
-  raw = rpbh_load_row(X, base + rs, M, K, cidx);
+  for (int i = 0; i < 8; ++i) sv[i] = reinterpret_cast<const uint32_t*>(sign + 32 * sbk)[i];
+  GroupChunks<R> raw = rg_load<R>(X, g * R, M, K, col);
+  // keep the group's loads ahead of the set-up's waits (X is not declared restrict, so
+  // the compiler may not move its loads across this point)
+  asm volatile("" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < PV; ++i) {
-    const int c = min(t + 64 * RPBH_WAVES * i, (K >> 2) - 1);
-    reinterpret_cast<uint2*>(tab)[c] = make_uint2((pv[i].x & 0xFFFFu) | (pv[i].y << 16),
-                                                    (pv[i].z & 0xFFFFu) | (pv[i].w << 16));
-  }
+  for (int i = 0; i < RG_PV; ++i)
+    reinterpret_cast<uint2*>(tab)[pc[i]] = make_uint2((pv[i].x & 0xFFFFu) | (pv[i].y << 16),
+                                                      (pv[i].z & 0xFFFFu) | (pv[i].w << 16));
   {
-    uint32_t m = 0;
+    uint32_t m = 0;      // bit j: d_{32 b + j} < 0
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int k = 0; k < 4; ++k) m |= ((sv[i] >> (8 * k + 7)) & 1u) << (4 * i + k);
-    smask[sb_] = m;
+    smask[sbk] = m;
   }
   const MfmaXform xf = mfma_xform_hadamard(lane);
-  lds_barrier();     // the table is visible; the row loads stay in flight
 
-  for (; base < M; base += stride) {
-    const int64_t row = base + rs;
-    if (WPR > 1) lds_barrier();          // the previous row's gathers are done
-    float psum = 0.0f;
+  for (; g < ngroups; g += gridDim.x) {
+    lds_barrier();       // the previous group's gathers are done (and the table is written)
+    float ps[R];
 #pragma unroll
-    for (int j = 0; j < RPBH_LMAX; ++j) {
-      reinterpret_cast<v4u*>(slot)[cidx[j]] = raw.v[j];    // repeated chunks rewrite identical data
+    for (int r = 0; r < R; ++r) ps[r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < RG_COLS; ++j) {
+      const GroupChunks<R>& c = raw;
+      v4u* dst = reinterpret_cast<v4u*>(slot) + (size_t)col[j] * (R * 8 * 2 / 16);
+      if (R == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4u a = c.v[j][0], b = c.v[j][1], cc = c.v[j][R - 2], d = c.v[j][R - 1];
+          dst[i] = v4u{__builtin_amdgcn_perm(b[i], a[i], KQ_PERM_LO), __builtin_amdgcn_perm(d[i], cc[i], KQ_PERM_LO),
+                       __builtin_amdgcn_perm(b[i], a[i], KQ_PERM_HI), __builtin_amdgcn_perm(d[i], cc[i], KQ_PERM_HI)};
+        }
+      } else {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const v4u a = c.v[j][0], b = c.v[j][1];
+          dst[m2] = v4u{__builtin_amdgcn_perm(b[2 * m2], a[2 * m2], KQ_PERM_LO),
+                        __builtin_amdgcn_perm(b[2 * m2], a[2 * m2], KQ_PERM_HI),
+                        __builtin_amdgcn_perm(b[2 * m2 + 1], a[2 * m2 + 1], KQ_PERM_LO),
+                        __builtin_amdgcn_perm(b[2 * m2 + 1], a[2 * m2 + 1], KQ_PERM_HI)};
+        }
+      }
       if (CENTER) {
-        float x[8];
-        unpack8_f16(raw.v[j], x);
-        float ps = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) ps += x[m];
-        const bool counted = j < nl && wr * 64 + lane + 64 * WPR * j < G;   // a repeated chunk is not
-        psum += counted ? ps : 0.0f;
+        for (int r = 0; r < R; ++r) {
+          float s8 = 0.0f;     // sum of the 8 halves
+#pragma unroll
+          for (int m = 0; m < 4; ++m) s8 = add_f16x2(c.v[j][r][m], s8);
+          ps[r] += colv[j] ? s8 : 0.0f;     // a repeated column is not counted
+        }
       }
     }
-    raw = rpbh_load_row(X, row + stride, M, K, cidx);   // prefetch this wave's next row
-    float tot = 0.0f;
-    if (CENTER) tot = wave_sum(psum);
-    if (WPR > 1) {
-      if (CENTER && lane == 0) red[wid] = tot;
-      lds_barrier();
-      if (CENTER) {
-        tot = 0.0f;
-#pragma unroll
-        for (int w = 0; w < WPR; ++w) tot += red[rs * WPR + w];
-      }
-    } else {
-      // the row slot is private to this wavefront: its LDS writes complete before its
-      // later LDS reads, so no barrier is needed, only no reordering by the compiler
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    }
-    float m32 = 0.0f;
+    if (g + gridDim.x < ngroups) raw = rg_load<R>(X, (g + gridDim.x) * R, M, K, col);   // prefetch the next group
     if (CENTER) {
-      const __half mh = __float2half_rn(tot / (float)K);
-      m32 = 32.0f * __half2float(mh);
-      if (row < M && wr == 0 && lane == 0) mu[row] = mh;
+      // wave sums of the R partial sums in registers: each lane-half / lane-row swap adds
+      // the partner's copy of one value while halving the set (the swap returns, per lane,
+      // its own value in one result and the partner's in the other), then a row sum;
+      // lanes of 16-lane row j end with the sum of row j (R = 4) or j / 2 (R = 2)
+      float v;
+      if (R == 4) {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps[0]), __float_as_uint(ps[2]), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps[1]), __float_as_uint(ps[R - 1]), false, false);
+        const float k0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // rows 0 (lanes < 32) / 2
+        const float k1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // rows 1 / 3
+        const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+        v = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      } else {
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps[0]), __float_as_uint(ps[1]), false, false);
+        const float k = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+        const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(k), __float_as_uint(k), false, false);
+        v = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      }
+      v = row16_sum(v);
+      if ((lane & 15) == 0 && (R == 4 || (lane & 16) == 0)) red[wid * 4 + (R == 4 ? (lane >> 4) : (lane >> 5))] = v;
     }
-    uint8_t* const crow = codes + row * (int64_t)(K >> 1);
-    uint8_t* const srow_sc = scales + row * (int64_t)nb;
-    // chunks wr, wr + WPR, ... of the row, two at a time
-    for (int ch0 = wr; ch0 < nchunk; ch0 += 2 * WPR) {
-      float y[2][8];
-      int blk[2];
+    lds_barrier();       // the group is staged (and the partial sums are visible)
+    float m32[R];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        blk[u] = 16 * (ch0 + u * WPR) + bl;
-        const int bb = blk[u] < nb ? blk[u] : 0;    // lanes past the row's end gather block 0, not stored
-        const uint4 ix = *reinterpret_cast<const uint4*>(tab + 32 * bb + 8 * q);
-        const uint32_t iw[4] = {ix.x, ix.y, ix.z, ix.w};
-        v8h b;
+    for (int r = 0; r < R; ++r) m32[r] = 0.0f;
+    if (CENTER) {
+      float tot[R];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          b[i] = __builtin_bit_cast(_Float16, slot[(iw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu]);
-        mfma_block_transform<false>(xf, b, y[u]);
-        const uint32_t sm = smask[bb];
-        if (CENTER && q == 0) y[u][0] -= m32;     // output 0 of the block
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int j = (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
-          const float c = ((sm >> j) & 1u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
-          y[u][i] = __builtin_fmaf(y[u][i], c, 0.0f);   // +0 for an exact zero
+      for (int r = 0; r < R; ++r) tot[r] = 0.0f;
+      for (int w = 0; w < NW; ++w) {
+        const float4 rw = reinterpret_cast<const float4*>(red)[w];
+        tot[0] += rw.x;
+        tot[1] += rw.y;
+        if (R == 4) {
+          tot[2 % R] += rw.z;
+          tot[3 % R] += rw.w;
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint32_t w, sb;
-        int off;
-        mx_pack_block(y[u], q, w, off, sb);
-        if (row < M && ch0 + u * WPR < nchunk && blk[u] < nb) {
-          *reinterpret_cast<uint32_t*>(crow + 16 * blk[u] + off) = w;
-          if (q == 0) srow_sc[blk[u]] = (uint8_t)sb;
+      for (int r = 0; r < R; ++r) {
+        const __half mh = __float2half_rn(tot[r] / (float)K);
+        m32[r] = 32.0f * __half2float(mh);
+        if (t == r && g * R + r < M) mu[g * R + r] = mh;
+      }
+    }
+    // the group's rows of codes and scales (rows past M are outside both ranges)
+    const int64_t nrows = M - g * R < R ? M - g * R : R;
+    const __amdgpu_buffer_rsrc_t rcodes = make_rsrc(codes + g * R * (int64_t)(K >> 1), nrows * (K >> 1));
+    const __amdgpu_buffer_rsrc_t rscales = make_rsrc(scales + g * R * (int64_t)nb, nrows * nb);
+#pragma unroll 1
+    for (int it = 0; it < 2; ++it) {
+      const int ch = wid + NW * it;
+      if (ch >= nchunk) break;
+      const int blk = 16 * ch + bl;
+      const bool bv = blk < nb;
+      const int bb = bv ? blk : nb - 1;          // lanes past the row's end gather a real block, not stored
+      const v4u ix = *reinterpret_cast<const v4u*>(tab + 32 * bb + 8 * q);
+      uint32_t pos[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pos[2 * i] = ix[i] & 0xFFFFu;
+        pos[2 * i + 1] = ix[i] >> 16;
+      }
+      v4u bop[R];      // B operands (8 fp16 inputs of block bb) of the R rows
+      if (R == 4) {
+        uint2 gv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = *reinterpret_cast<const uint2*>(slot + (size_t)pos[i] * 8);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          bop[0][m] = __builtin_amdgcn_perm(gv[2 * m + 1].x, gv[2 * m].x, KQ_PERM_LO);
+          bop[1][m] = __builtin_amdgcn_perm(gv[2 * m + 1].x, gv[2 * m].x, KQ_PERM_HI);
+          bop[2][m] = __builtin_amdgcn_perm(gv[2 * m + 1].y, gv[2 * m].y, KQ_PERM_LO);
+          bop[R - 1][m] = __builtin_amdgcn_perm(gv[2 * m + 1].y, gv[2 * m].y, KQ_PERM_HI);
         }
+      } else {
+        uint32_t gv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = *reinterpret_cast<const uint32_t*>(slot + (size_t)pos[i] * 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          bop[0][m] = __builtin_amdgcn_perm(gv[2 * m + 1], gv[2 * m], KQ_PERM_LO);
+          bop[1][m] = __builtin_amdgcn_perm(gv[2 * m + 1], gv[2 * m], KQ_PERM_HI);
+        }
+      }
+      const uint32_t sm = smask[bb];
+      float coef[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = (i < 4 ? 4 * q + i : 16 + 4 * q + (i - 4));
+        coef[i] = ((sm >> j) & 1u) ? -KQ_INV_SQRT32 : KQ_INV_SQRT32;
+      }
+      // all R transforms first, then the packing, then branch-free stores (masked lanes
+      // and rows past M fall outside the buffer ranges), so the R rows' chains interleave
+      float y[R][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) mfma_block_transform<false>(xf, __builtin_bit_cast(v8h, bop[r]), y[r]);
+      uint32_t w[R], sb[R];
+      int off = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (CENTER && q == 0) y[r][0] -= m32[r];      // output 0 of the block
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[r][i] = __builtin_fmaf(y[r][i], coef[i], 0.0f);   // +0 for an exact zero
+        mx_pack_block(y[r], q, w[r], off, sb[r]);
+      }
+      const int coff = bv ? 16 * blk + off : KQ_OOB;
+      const int soff = (bv && q == 0) ? blk : KQ_OOB;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        __builtin_amdgcn_raw_buffer_store_b32(w[r], rcodes, coff + (coff == KQ_OOB ? 0 : r * (K >> 1)), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[r], rscales, soff + (soff == KQ_OOB ? 0 : r * nb), 0, 0);
       }
     }
   }
@@ -648,40 +733,35 @@ hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, cons
   return hipGetLastError();
 }
 
-template <bool CENTER, int WPR>
-static hipError_t rpbh_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
-                              uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
-  const size_t lds = rpbh_lds_bytes(WPR, K);
-  // one resident wave of workgroups: as many as fit on the chip at once, at most one
-  // per group of NR rows
-  constexpr int NR = RPBH_WAVES / WPR;
-  int64_t grid = (M + NR - 1) / NR;
-  const int64_t cap = (int64_t)device_cu_count() *
-                      resident_blocks_per_cu(reinterpret_cast<const void*>(&rpbh_mx_mfma_rows_kernel<CENTER, WPR>),
-                                             64 * RPBH_WAVES, lds);
+template <int R, bool CENTER>
+static hipError_t rpbh_group_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
+                                    uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
+  // wavefronts: enough that each transforms at most two 16-block chunks of the group
+  // (this also keeps the set-up at <= 4 perm chunks and the staging at <= 2 columns per
+  // lane); persistent workgroups, as many as are resident at once
+  const int nchunk = (K / 32 + 15) / 16;
+  const int nw = (nchunk + 1) / 2;
+  if (nw > RG_MAXW) return hipErrorInvalidValue;
+  const unsigned threads = 64u * (unsigned)nw;
+  const size_t lds = rg_lds_bytes(R, K);
+  const auto kern = rpbh_mx_group_kernel<R, CENTER>;
+  int64_t grid = (M + R - 1) / R;
+  const int64_t cap =
+      (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), (int)threads, lds);
   if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((rpbh_mx_mfma_rows_kernel<CENTER, WPR>), dim3((unsigned)grid), dim3(64 * RPBH_WAVES), lds, s, X,
-                     M, K, perm, sign, codes, scales, mu);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, perm, sign, codes, scales, mu);
   return hipGetLastError();
-}
-
-template <bool CENTER>
-static hipError_t rpbh_launch_wpr(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
-                                  uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
-  // waves per row: the fewest that keep each lane at <= RPBH_LMAX 16-byte chunks of a row
-  const int G = K / 8;
-  if (G <= 64 * RPBH_LMAX) return rpbh_launch<CENTER, 1>(X, M, K, perm, sign, codes, scales, mu, s);
-  if (G <= 128 * RPBH_LMAX) return rpbh_launch<CENTER, 2>(X, M, K, perm, sign, codes, scales, mu, s);
-  if (G <= 256 * RPBH_LMAX) return rpbh_launch<CENTER, 4>(X, M, K, perm, sign, codes, scales, mu, s);
-  if (G <= 512 * RPBH_LMAX) return rpbh_launch<CENTER, 8>(X, M, K, perm, sign, codes, scales, mu, s);
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
-  if (K > 65536) return hipErrorInvalidValue;    // u16 gather indices
-  return center ? rpbh_launch_wpr<true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
-                : rpbh_launch_wpr<false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+  if (K > 16384) return hipErrorInvalidValue;
+  // four rows per group while their staging fits beside the table (K <= 12288), else two
+  if (K <= 12288)
+    return center ? rpbh_group_launch<4, true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
+                  : rpbh_group_launch<4, false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+  return center ? rpbh_group_launch<2, true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
+                : rpbh_group_launch<2, false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
 }
 
 int resident_blocks_per_cu(const void* kernel, int threads, size_t lds) {

@@ -29,12 +29,6 @@ __device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >>
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Buffer resource over [base, base + bytes): loads past the end return zeros and stores
-// past the end are dropped, which handles the ragged last tiles without clamping.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)(bytes < 0 ? 0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
 
 // Tile configuration: BN weight rows x BM activation rows per workgroup, WN x WM
 // wavefronts, each owning a (BN/WN) x (BM/WM) block of 32x32 MFMA tiles.  PF = how many
