@@ -8,7 +8,7 @@
  *     transform P applied to the activations online, its inverse folded into the
  *     weights offline; §02: P = A (x) B (A 4x4, B 8x8) on every 32-element block of
  *     the activation vector; §03: 4-bit MXFP4 target format.
- *   - OrbitQuant (Data-Free Quantization for Image and Video DiTs), §03:
+ *   - OrbitQuant (data-independent quantization for image and video DiTs), §03:
  *     RPBH(X) = X.P.H.D (random permutation, block Hadamard, random signs), the
  *     inverse folded offline as W' = R^-1 W, one Lloyd-Max codebook for all
  *     rotated coordinates.
@@ -80,7 +80,8 @@ enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
  *   (x.Pi)_j = x[perm[j]] over all K, H32 the Sylvester Hadamard matrix
  *   (H[i][j] = (-1)^popcount(i&j)), D = diag(sign), sign[j] in {-1, +1}.
  *   perm (int32 [K], a permutation of 0..K-1) and sign (int8 [K]) are device arrays,
- *   16- and 4-byte aligned.
+ *   16- and 4-byte aligned.  perm is not checked on the device: an entry outside
+ *   0..K-1 gives unspecified codes for that call (the on-chip gather cannot fault).
  * NONE: identity. */
 typedef struct kq_xform {
   int32_t kind;

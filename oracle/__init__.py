@@ -13,7 +13,7 @@ the pages (cited per function):
   Quantization of Diffusion Transformers (iselia-ai.com/papers/2607-21446):
   §01 (the identity Y = (XP)(P^-1 W)), §02 (P = A (x) B on 32-element blocks),
   §03 (MXFP4 target format).
-* OrbitQuant: Data-Free Quantization for Image and Video DiTs
+* OrbitQuant: data-independent quantization for image and video DiTs
   (iselia-ai.com/papers/2607-02461): §03 (RPBH(X) = X.P.H.D, W' = R^-1 W,
   one Lloyd-Max codebook).
 * CentriQ: Calibration-Free Quantization of DiTs via Exact Mean Centering
