@@ -13,13 +13,17 @@ resident in HBM; the activation buffers rotate over enough copies (>= 1 GiB) tha
 reads them from the 256 MB last-level cache.
 
 Prints ONE JSON line (rank 0).  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on.
+stream the kernels run on, around batches of back-to-back launches of one kernel.  The
+"traffic" fields come from the HBM byte counters recorded in profiles/ for the same
+kernel source (null when the source has changed since).
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -51,6 +55,41 @@ def transform_bytes(M, K, center, fmt="mxfp4"):
     """Algorithmic HBM bytes of transform+quantize: fp16 in, 4-bit codes + E8M0 scales out
     (2 + 0.5 + 1/32 bytes per element), plus the fp16 mean per token when centring."""
     return M * K * 2 + M * K // 2 + M * K // 32 + (2 * M if center else 0)
+
+
+def gemm_bytes(M, K, N, r, center):
+    """Algorithmic HBM bytes of one W4A4 launch: both packed operands with their E8M0
+    scales, T, L2, mu, wbar, and the fp16 output."""
+    return (M + N) * (K // 2 + K // 32) + 2 * M * r + 2 * N * r + (2 * M + 2 * N if center else 0) + 2 * M * N
+
+
+# source files whose kernels the recorded counters describe
+_TRAFFIC_SOURCES = {
+    "w4a4_gemm": ["w4a4_gemm.hip", "kq_device.hpp"],
+    "transform": ["transform_quant.hip", "kq_device.hpp"],
+}
+
+
+def source_digest(kind):
+    h = hashlib.sha256()
+    for f in _TRAFFIC_SOURCES[kind]:
+        with open(os.path.join(ROOT, "w4a4_post_quantization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kind):
+    """HBM bytes per launch by layer, from the counter summary in profiles/, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_flux.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"\s*traffic-record:\s+kind=(\S+)\s+source=(\S+)\s+(.*)$", line)
+            if m and m.group(1) == kind and m.group(2) == source_digest(kind):
+                return {k: float(v) for k, v in (kv.split("=") for kv in m.group(3).split())}
+    return None
 
 
 def cpu_baseline(cfg_idx, rows, col_frac=4):
@@ -93,6 +132,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="activation buffer sets (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="tokens per linear in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10, help="back-to-back launches per kernel timing batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -137,23 +179,15 @@ def main():
             Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
 
-    def step(s, ev=None):
+    def step(s):
         Xs = Xsets[s % R]
-        for li, L in enumerate(layers):
+        for L in layers:
             X = Xs[L["K"]]
-            if ev is not None:
-                ev[li][0].record()
             kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],
                                   mu=L["mu"])
-            if ev is not None:
-                ev[li][1].record()
             kq.lowrank_down(X, L["L1"], T=L["T"])
-            if ev is not None:
-                ev[li][2].record()
             kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
                            wbar=L["wbar"], Y=L["Y"])
-            if ev is not None:
-                ev[li][3].record()
 
     for s in range(args.warmup):
         step(s)
@@ -170,16 +204,43 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
-    # ---- per-kernel durations: HIP events around each launch on the launch stream
-    dur = [[0.0, 0.0, 0.0] for _ in layers]
-    for s in range(args.steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
-        step(args.warmup + args.steps + s, ev)
+    # ---- per-kernel durations: HIP events (on the launch stream) around a batch of
+    # back-to-back launches of one kernel; the average includes the launch gaps
+    def batch_ms(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn(0)
+        a.record()
+        for i in range(n):
+            fn(i + 1)
+        b.record()
         torch.cuda.synchronize()
-        for li in range(len(layers)):
-            for k in range(3):
-                dur[li][k] += ev[li][k].elapsed_time(ev[li][k + 1]) / args.steps   # ms
+        return a.elapsed_time(b) / n
 
+    dur = []
+    for L in layers:
+        def tq(i, L=L):
+            kq.transform_quantize(Xsets[i % R][L["K"]], L["xf"], fmt="mxfp4", center=center, codes=L["codes"],
+                                  scales=L["scales"], mu=L["mu"])
+
+        def lr(i, L=L):
+            kq.lowrank_down(Xsets[i % R][L["K"]], L["L1"], T=L["T"])
+
+        def gm(i, L=L):
+            kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
+                           wbar=L["wbar"], Y=L["Y"])
+        dur.append([batch_ms(tq, args.kernel_reps), batch_ms(lr, args.kernel_reps), batch_ms(gm, args.kernel_reps)])
+
+    if args.copy_calibration:
+        # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference
+        # dispatch for scaling the HBM byte counters
+        src = torch.empty((1 << 27,), dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic_gemm = recorded_traffic("w4a4_gemm")
+    traffic_tq = recorded_traffic("transform")
     per_layer = []
     tot_flops = tot_gemm_flops = tot_tq_bytes = 0
     tot_tq_ms = tot_lr_ms = tot_gemm_ms = 0.0
@@ -201,6 +262,9 @@ def main():
             "lowrank_down_us": round(lr_ms * 1e3, 2),
             "w4a4_gemm_us": round(gm_ms * 1e3, 2),
             "w4a4_gemm_TFLOPs": round(gfl / gm_ms / 1e9, 1),
+            "w4a4_gemm_algorithmic_bytes": gemm_bytes(M, K, N, r, center),
+            "w4a4_gemm_traffic_bytes": traffic_gemm.get(L["name"]) if traffic_gemm else None,
+            "transform_quant_traffic_bytes": traffic_tq.get(L["name"]) if traffic_tq else None,
             "linear_TFLOPs": round(fl / (lr_ms + gm_ms) / 1e9, 1),
         })
         log(f"{L['name']:>4}: transform+quant {tq_ms*1e3:8.2f} us {tb/tq_ms/1e6:8.1f} GB/s | lowrank-down "
@@ -222,12 +286,20 @@ def main():
                                "qkv 3072->9216, fc1 3072->12288, fc2 12288->3072; centred RPBH-32 + MXFP4 "
                                "activations and weights, rank-32 fp16 branch, rank-1 mean restore",
                    "tokens": M, "rotated_input_sets": R},
-        "roofline": {"bound": "mfma", "kernel": "kq_w4a4_linear (W4A4 GEMM + fused low-rank/rank-1 epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "kq_w4a4_linear (W4A4 GEMM + fused low-rank/rank-1 epilogue), "
+                                                "the three launches of one step",
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4), "traffic": None},
-        "roofline_transform": {"bound": "hbm", "kernel": "kq_transform_quantize (centre + RPBH-32 + MXFP4)",
+                     "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": (round(sum(traffic_gemm.get(L["name"], 0.0) for L in layers))
+                                 if traffic_gemm else None),
+                     "algorithmic_bytes": sum(gemm_bytes(M, L["K"], L["N"], r, center) for L in layers)},
+        "roofline_transform": {"bound": "hbm", "kernel": "kq_transform_quantize (centre + RPBH-32 + MXFP4), "
+                                                         "the three launches of one step",
                                "achieved": round(tq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(tq_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                               "frac": round(tq_gbs / PEAK_HBM_GBS, 4),
+                               "traffic": (round(sum(traffic_tq.get(L["name"], 0.0) for L in layers))
+                                           if traffic_tq else None),
+                               "algorithmic_bytes": tot_tq_bytes},
         "transform_quant_GBps": round(tq_gbs, 1),
         "w4a4_gemm_TFLOPs": round(gemm_tflops, 1),
         "linear_TFLOPs": round(tot_flops / ((tot_lr_ms + tot_gemm_ms) * 1e-3) / 1e12, 1),
