@@ -13,9 +13,10 @@ resident in HBM; the activation buffers rotate over enough copies (>= 1 GiB) tha
 reads them from the 256 MB last-level cache.
 
 Prints ONE JSON line (rank 0).  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on, around batches of back-to-back launches of one kernel.  The
-"traffic" fields come from the HBM byte counters recorded in profiles/ for the same
-kernel source (null when the source has changed since).
+stream the kernels run on, one after every launch of the timed steps (a launch's duration
+runs from the event before it to its own, so it includes the dispatch gap; averaged over
+the steps).  The "traffic" fields come from the HBM byte counters recorded in profiles/ for
+the same kernel source (null when the source has changed since).
 """
 
 import argparse
@@ -130,9 +131,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=0, help="activation buffer sets (0: enough for >= 1 GiB)")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="tokens per linear in the CPU-oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=10, help="back-to-back launches per kernel timing batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -179,56 +179,53 @@ def main():
             Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
 
-    def step(s):
+    # one event after every launch of the timed steps, recorded on the current stream (the
+    # one the kernels run on); a launch's duration is the span from the event before it
+    # (the previous launch's, or the start of the timed region) to its own.  Per layer the
+    # order is low-rank projection, transform, GEMM (the first two are independent).
+    nl = len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
+
+    def step(s, ev=None):
         Xs = Xsets[s % R]
-        for L in layers:
+        for li, L in enumerate(layers):
             X = Xs[L["K"]]
+            kq.lowrank_down(X, L["L1"], T=L["T"])
+            if ev:
+                ev[3 * li].record()
             kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],
                                   mu=L["mu"])
-            kq.lowrank_down(X, L["L1"], T=L["T"])
+            if ev:
+                ev[3 * li + 1].record()
             kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
                            wbar=L["wbar"], Y=L["Y"])
+            if ev:
+                ev[3 * li + 2].record()
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # ---- timed region: whole steps, no per-kernel events inside
+    # ---- timed region: K whole steps between two events, with one event after each launch
     t0 = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_start.record()
     for s in range(args.steps):
-        step(args.warmup + s)
+        step(args.warmup + s, evs[s])
     e_end.record()
+    host_submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
-    # ---- per-kernel durations: HIP events (on the launch stream) around a batch of
-    # back-to-back launches of one kernel; the average includes the launch gaps
-    def batch_ms(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn(0)
-        a.record()
-        for i in range(n):
-            fn(i + 1)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
-
-    dur = []
-    for L in layers:
-        def tq(i, L=L):
-            kq.transform_quantize(Xsets[i % R][L["K"]], L["xf"], fmt="mxfp4", center=center, codes=L["codes"],
-                                  scales=L["scales"], mu=L["mu"])
-
-        def lr(i, L=L):
-            kq.lowrank_down(Xsets[i % R][L["K"]], L["L1"], T=L["T"])
-
-        def gm(i, L=L):
-            kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
-                           wbar=L["wbar"], Y=L["Y"])
-        dur.append([batch_ms(tq, args.kernel_reps), batch_ms(lr, args.kernel_reps), batch_ms(gm, args.kernel_reps)])
+    # average duration of each launch over the timed steps: [transform, low-rank, GEMM] per layer
+    flat = [e_start] + [e for ev in evs for e in ev]
+    span = [flat[i].elapsed_time(flat[i + 1]) for i in range(len(flat) - 1)]
+    per = [[0.0, 0.0, 0.0] for _ in range(nl)]
+    for i, t in enumerate(span):
+        li, k = (i % (3 * nl)) // 3, i % 3
+        per[li][k] += t / args.steps
+    dur = [[p[1], p[0], p[2]] for p in per]
 
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference
@@ -275,7 +272,8 @@ def main():
     tq_gbs = tot_tq_bytes / (tot_tq_ms * 1e-3) / 1e9
     log(f"step {ms_per_step*1e3:.1f} us; whole-step linear throughput {value:.1f} TFLOP/s; "
         f"GEMM {gemm_tflops:.1f} TFLOP/s ({gemm_tflops/PEAK_FP4_TFLOPS:.1%} of MXFP4 peak); "
-        f"transform+quant {tq_gbs:.1f} GB/s ({tq_gbs/PEAK_HBM_GBS:.1%} of HBM peak); wall {wall:.2f} s")
+        f"transform+quant {tq_gbs:.1f} GB/s ({tq_gbs/PEAK_HBM_GBS:.1%} of HBM peak); wall {wall:.2f} s; "
+        f"host submission {host_submit / args.steps * 1e6:.1f} us per step")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

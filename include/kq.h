@@ -139,7 +139,12 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt,
 /* Low-rank down-projection of the 16-bit branch (SVDQuant explainer §3):
  *   T = fp16(X L1^T), fp32 accumulation on the fp16 matrix cores.
  * X fp16 [M][K] (the original activations: not centred, not transformed), L1 fp16 [r][K],
- * T fp16 [M][r] (caller-owned).  r in {16, 32, 64}; K % 32 == 0.  One kernel. */
+ * T fp16 [M][r] (caller-owned).  r in {16, 32, 64}; K % 32 == 0, K <= 2^20.
+ * When M is small against the device, K is split over several workgroups whose fp32
+ * partials go to a library-owned workspace (32 MiB per device, allocated on the first
+ * such call and kept until the process ends) and a second kernel sums them in a fixed
+ * order, so results do not depend on scheduling.  Calls that use the workspace must not
+ * overlap on one device (issue them on one stream, or synchronize between them). */
 kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r,
                           void* T, hipStream_t stream);
 
@@ -154,7 +159,7 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
  *   r in {0, 16, 32, 64} (0: T and L2 ignored); T L2^T enters the fp32 accumulators
  *   before the 4-bit product, so the branch costs no extra pass over Y.
  * Rank-1 restore (CentriQ): mu fp16 [M] and wbar fp16 [N], both or neither.
- * N % 16 == 0.  Y fp16 [M][N]. */
+ * N % 16 == 0; M <= 2^30, N and K <= 2^20.  Y fp16 [M][N]. */
 kq_status kq_w4a4_linear(int32_t fmt,
                          const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
                          const uint8_t* wcodes, const void* wscales, int64_t N,

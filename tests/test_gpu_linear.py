@@ -146,13 +146,13 @@ def test_w4a4_branch_variants(kq, rank, with_mu):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("M,K,r", [(1, 128, 32), (77, 1152, 16), (301, 3072, 32), (40, 12288, 64), (19, 2240, 32)])
-def test_lowrank_down_matches_oracle(kq, M, K, r):
+def _check_lowrank(kq, M, K, r, seed=7):
     """T = fp16(X L1^T): within one fp16 rounding of the exact product (plus the float32
-    accumulation bound)."""
+    accumulation bound: K / 8 sequential additions per lane and MFMA block, then the
+    split-K partials)."""
     import torch
-    X16 = synth.activations(M, K, 7, 2.0)
-    _, L1, _ = synth.weights(K, 16, 7, 0, r)
+    X16 = synth.activations(M, K, seed, 2.0)
+    _, L1, _ = synth.weights(K, 16, seed, 0, r)
     T = kq.lowrank_down(torch.from_numpy(X16).cuda(), torch.from_numpy(L1).cuda())
     torch.cuda.synchronize()
     got = T.cpu().numpy().astype(np.float64)
@@ -160,6 +160,19 @@ def test_lowrank_down_matches_oracle(kq, M, K, r):
     bound = np.abs(X16.astype(np.float64)) @ np.abs(L1.astype(np.float64)).T
     err = np.abs(got - exact)
     assert np.all(err <= np.abs(exact) * 2.0 ** -11 + ties.gamma_tau(K // 8 + 16, bound) + 2.0 ** -24)
+
+
+@pytest.mark.parametrize("M,K,r", [(1, 128, 32), (77, 1152, 16), (301, 3072, 32), (40, 12288, 64), (19, 2240, 32),
+                                   (1000, 3072, 64), (4608, 3072, 16), (4608, 12288, 32)])
+def test_lowrank_down_matches_oracle(kq, M, K, r):
+    _check_lowrank(kq, M, K, r)
+
+
+def test_lowrank_down_repeated_calls(kq):
+    """Split-K calls in a row with different shapes: each call leaves the per-row-block
+    arrival counters at zero for the next."""
+    for i, (M, K, r) in enumerate(((300, 3072, 32), (130, 12288, 32), (300, 3072, 32), (64, 5120, 16))):
+        _check_lowrank(kq, M, K, r, seed=11 + i)
 
 
 def test_w4a4_small_shapes(kq):
@@ -207,4 +220,33 @@ def test_w4a4_full_size_sampled(kq):
     ref = _ref_Y(d, rows=rows)
     err = linear.rel_frobenius(d["Y"][rows], ref)
     print(f"full-size sampled rel frobenius {err:.3e}")
+    assert err <= TOL
+
+
+def _sampled_rows(M):
+    """Rows spread over the matrix plus both edges of every 256-row tile boundary near the
+    ends (the large-tile kernel form works on 256 x 256 output tiles)."""
+    rows = set(range(0, M, 97)) | {0, 1, 255, 256, M - 257, M - 256, M - 2, M - 1}
+    return np.array(sorted(r for r in rows if 0 <= r < M))
+
+
+@pytest.mark.parametrize("rank,with_mu", [(0, False), (16, True), (64, False), (32, True)])
+def test_w4a4_large_tile_form_ragged(kq, rank, with_mu):
+    """Enough 256 x 256 tiles for the large-tile kernel form (K a multiple of 512), with M
+    and N not multiples of the tile; oracle on sampled rows and all columns."""
+    M, N, K = 1800, 4624, 1024
+    d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=rank, with_mu=with_mu)
+    rows = _sampled_rows(M)
+    err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
+    print(f"M={M} N={N} K={K} rank {rank} mu {with_mu}: {err:.3e}")
+    assert err <= TOL
+
+
+def test_w4a4_full_size_fc2_sampled(kq):
+    """FLUX-like fc2 at full size (M = 4608, K = 12288, N = 3072): oracle on sampled rows and
+    all columns."""
+    d = _linear_case(kq, 3, 2, 4608)
+    rows = _sampled_rows(4608)
+    err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
+    print(f"fc2 full-size sampled rel frobenius {err:.3e}")
     assert err <= TOL

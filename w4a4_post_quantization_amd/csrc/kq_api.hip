@@ -197,7 +197,7 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
   if (!X || !L1 || !T) return KQ_ERR_NULL;
   if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
-  if (M > (1LL << 31) - 64 || K > (1LL << 30)) return KQ_ERR_UNSUPPORTED;
+  if (M > (1LL << 31) - 64 || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16)) return KQ_ERR_ALIGN;
   return hip_status(launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r,
                                         static_cast<__half*>(T), stream));
@@ -210,7 +210,7 @@ kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (r != 0 && r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
   if ((mu == nullptr) != (wbar == nullptr)) return KQ_ERR_SHAPE;
-  if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return KQ_ERR_UNSUPPORTED;
+  if (M > (1LL << 30) || N > (1LL << 20) || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (N % 16 != 0) return KQ_ERR_UNSUPPORTED;
   if (fmt == KQ_FMT_MXFP4) {
     if (K % 128 != 0) return KQ_ERR_UNSUPPORTED;

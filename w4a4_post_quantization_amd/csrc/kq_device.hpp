@@ -112,6 +112,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 #define KQ_OOB 0x7FFFFFF0
 
+// ---- loads from global memory straight into LDS (buffer loads with the LDS destination)
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations
+// of this wave are outstanding and does not wait on the other counters.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Buffer resource words for [base, base + bytes) (raw buffer, no stride, as make_rsrc).
+__device__ __forceinline__ v4i rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int32_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int32_t)(bytes < 0 ? 0 : bytes);
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), n, 0x00020000};
+}
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 64 lanes x 16 bytes from rsrc at byte offset voff (per lane, range-checked) into LDS
+// at lds + 16 x lane.  The LDS address must be wave-uniform (it goes to M0): it is passed
+// through readfirstlane so that it lives in a scalar register.
+__device__ __forceinline__ void lds_load16(const v4i& rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
 // Sum over a wavefront (every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

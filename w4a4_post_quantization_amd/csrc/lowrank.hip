@@ -2,88 +2,217 @@
 // matrix cores with fp32 accumulation, T stored as fp16 [M][r] (the branch is held in
 // 16 bits).  X is the original fp16 activation [M][K], L1 is [r][K].
 //
-// A workgroup of SPLIT wavefronts owns 16 rows; wavefront w reduces the 32-wide k-steps
-// w, w+SPLIT, ... with v_mfma_f32_16x16x32_f16 (lane l: row l%16, k = 8*(l/16)..+7, one
-// 16-byte load per operand).  Loads are issued in batches of BATCH k-steps ahead of their
-// MFMAs so each wavefront keeps several KiB in flight; the SPLIT partial 16 x r tiles are
-// summed through LDS in a fixed order.
+// The projection only streams X (r is small), so the kernel is built for HBM bandwidth:
+//   - a workgroup owns 64 rows and a slice of K (split-K), so L1 is re-read once per 64
+//     rows and the grid has enough workgroups to keep every compute unit streaming;
+//   - X and L1 go from global memory straight into LDS in 128-wide k-chunks (buffer loads
+//     with the LDS destination, full 128-byte lines), NS chunks deep;
+//   - each of the four wavefronts owns 16 rows and all r columns: v_mfma_f32_16x16x32_f16
+//     (lane l: row l%16, eight consecutive k of the 16-byte piece 4 s + l/16 of the chunk);
+//   - with several K slices the fp32 partial tiles go to a workspace and a second, small
+//     kernel sums them in slice order (deterministic) and stores T.  (Summing them in the
+//     last workgroup to finish a row block would need device-scope fences, which on this
+//     chip write back and invalidate the whole L2 of the compute die: far slower.)
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
+#include <map>
+#include <mutex>
+
 namespace kq {
 
-template <int RT, int SPLIT, int BATCH>  // RT = r / 16 output tiles
-__global__ __launch_bounds__(64 * SPLIT, 1) void lowrank_down_kernel(const __half* __restrict__ X,
-                                                                  const __half* __restrict__ L1, int64_t M,
-                                                                  int64_t K, __half* __restrict__ T) {
-  __shared__ float part[SPLIT][16][RT * 16];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  int64_t row = m0 + (lane & 15);
-  if (row >= M) row = M - 1;  // clamp: the tail rows compute duplicates that are not stored
-  const int q = lane >> 4;
-  const int64_t nk = K >> 5;
-  v4f acc[RT];
+constexpr int LR_ROWS = 64;      // rows per workgroup
+constexpr int LR_KC = 128;       // k per chunk (256 bytes of a row)
+
+// 16-byte piece c of a 256-byte LDS row sits at slot c ^ (row % 16): the fragment reads
+// (16 rows x one piece) then touch 16 distinct bank groups.
+__device__ __forceinline__ int lr_slot(int row, int piece) { return piece ^ (row & 15); }
+
+template <int RR, int NS>
+struct LrCfg {
+  static constexpr int RT = RR / 16;                    // 16-column output tiles
+  static constexpr int X_BYTES = LR_ROWS * 256;         // one chunk of X
+  static constexpr int STAGE = X_BYTES + RR * 256;      // ... and of L1
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int LPW = 4 + RR / 16;               // load instructions per wave per chunk
+};
+
+template <int RR, int NS>
+__global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restrict__ X,
+                                                           const __half* __restrict__ L1, int M, int K,
+                                                           int slices, int cps, float* __restrict__ part,
+                                                           __half* __restrict__ T) {
+  using C = LrCfg<RR, NS>;
+  __shared__ __align__(16) uint8_t lds[C::LDS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rb = blockIdx.x / slices, sl = blockIdx.x % slices;
+  const int m0 = rb * LR_ROWS;
+  const int nch = (K + LR_KC - 1) / LR_KC;
+  const int c0 = sl * cps;                                   // first chunk of the slice
+  const int nc = max(0, min(cps, nch - c0));                 // chunks in the slice
+
+  const v4i rX = rsrc_words(X + (int64_t)m0 * K, (int64_t)(M - m0) * K * 2);   // rows past M read zeros
+  const v4i rL = rsrc_words(L1, (int64_t)RR * K * 2);
+  const uint32_t lds0 = lds_addr(lds);
+
+  // load instruction j of this wave covers 4 rows x 256 bytes: row 4 j' + lane / 16 of
+  // its operand (j' numbering the instruction within the operand), LDS slot lane % 16,
+  // which holds the global piece slot ^ (row % 16)
+  int xoff[4], loff[RR / 16];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  const __half* xr = X + row * K + 8 * q;
-  const __half* lr[RT];
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * w + 4 * j + (lane >> 4);
+    const int piece = (lane & 15) ^ (row & 15);
+    xoff[j] = (row * K + 8 * piece) * 2;
+  }
 #pragma unroll
-  for (int t = 0; t < RT; ++t) lr[t] = L1 + (int64_t)(16 * t + (lane & 15)) * K + 8 * q;
-  // workgroups start at different k-steps so that they do not all read the same lines of
-  // L1 at the same moment (a rotation of the k order; the sum is over the same terms)
-  const int64_t rot = ((int64_t)blockIdx.x * 7 * SPLIT) % nk;
-  for (int64_t s0 = w; s0 < nk; s0 += SPLIT * BATCH) {
-    v8h a[BATCH], b[BATCH][RT];
+  for (int j = 0; j < RR / 16; ++j) {
+    const int row = (RR / 4) * w + 4 * j + (lane >> 4);      // RR / 4 rows of L1 per wave
+    const int piece = (lane & 15) ^ (row & 15);
+    loff[j] = (row * K + 8 * piece) * 2;
+  }
+  auto issue = [&](int f) {                                  // chunk f of the slice into stage f % NS
+    const uint32_t st = lds0 + (uint32_t)((f % NS) * C::STAGE);
+    const int kbase = (c0 + f) * LR_KC;
+    const bool live = f < nc;
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int64_t s = s0 + (int64_t)u * SPLIT;
-      const bool ok = s < nk;
-      int64_t ks = s + rot;
-      ks = ks >= nk ? ks - nk : ks;
-      a[u] = ok ? *reinterpret_cast<const v8h*>(xr + 32 * ks) : v8h{};
-#pragma unroll
-      for (int t = 0; t < RT; ++t) b[u][t] = ok ? *reinterpret_cast<const v8h*>(lr[t] + 32 * ks) : v8h{};
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * w + 4 * j + (lane >> 4);
+      const int k = kbase + 8 * ((lane & 15) ^ (row & 15));
+      lds_load16(rX, st + (16 * w + 4 * j) * 256, live && k < K ? xoff[j] + kbase * 2 : KQ_OOB);
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
+    for (int j = 0; j < RR / 16; ++j) {
+      const int row = (RR / 4) * w + 4 * j + (lane >> 4);
+      const int k = kbase + 8 * ((lane & 15) ^ (row & 15));
+      lds_load16(rL, st + C::X_BYTES + ((RR / 4) * w + 4 * j) * 256, live && k < K ? loff[j] + kbase * 2 : KQ_OOB);
+    }
+  };
+
+  v4f acc[C::RT];
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[u], b[u][t], acc[t], 0, 0, 0);
+  for (int t = 0; t < C::RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p);
+  const int arow = 16 * w + (lane & 15);
+  for (int f = 0; f < nc; ++f) {
+    // chunk f has landed once at most the NS - 2 younger chunks' loads are outstanding
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * C::LPW));
+    lds_barrier();                                           // ... for every wave; stage (f - 1) % NS is free
+    issue(f + NS - 1);
+    const uint8_t* st = lds + (f % NS) * C::STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int piece = 4 * s + (lane >> 4);
+      const v8h a = *reinterpret_cast<const v8h*>(st + arow * 256 + 16 * lr_slot(arow, piece));
+#pragma unroll
+      for (int t = 0; t < C::RT; ++t) {
+        const int n = 16 * t + (lane & 15);
+        const v8h b = *reinterpret_cast<const v8h*>(st + C::X_BYTES + n * 256 + 16 * lr_slot(n, piece));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+      }
+    }
   }
-  // acc[t][i] = partial T[m0 + 4q + i][16t + lane%16]
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                 // no load may land after the workgroup ends
+
+  // acc[t][i] = (partial) T[m0 + 16 w + 4 (lane / 16) + i][16 t + lane % 16]
+  const int orow = 16 * w + 4 * (lane >> 4);
+  if (slices == 1) {
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < C::RT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[w][4 * q + i][16 * t + (lane & 15)] = acc[t][i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * RT * 16; e += 64 * SPLIT) {
-    const int r = e / (RT * 16), c = e % (RT * 16);
-    float v = 0.0f;
-#pragma unroll
-    for (int p = 0; p < SPLIT; ++p) v += part[p][r][c];
-    if (m0 + r < M) T[(m0 + r) * (RT * 16) + c] = __float2half_rn(v);
+      for (int i = 0; i < 4; ++i)
+        if (m0 + orow + i < M) T[(int64_t)(m0 + orow + i) * RR + 16 * t + (lane & 15)] = __float2half_rn(acc[t][i]);
+    return;
   }
+  float* const mine = part + ((int64_t)sl * M + m0) * RR;
+#pragma unroll
+  for (int t = 0; t < C::RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (m0 + orow + i < M) mine[(orow + i) * RR + 16 * t + (lane & 15)] = acc[t][i];
 }
 
-template <int SPLIT>
-static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
-                                 hipStream_t s) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * SPLIT);
-  switch (r) {
-    case 16: hipLaunchKernelGGL((lowrank_down_kernel<1, SPLIT, 8>), grid, block, 0, s, X, L1, M, K, T); break;
-    case 32: hipLaunchKernelGGL((lowrank_down_kernel<2, SPLIT, 8>), grid, block, 0, s, X, L1, M, K, T); break;
-    case 64: hipLaunchKernelGGL((lowrank_down_kernel<4, SPLIT, 4>), grid, block, 0, s, X, L1, M, K, T); break;
-    default: return hipErrorInvalidValue;
+// T[m][c] = fp16(sum over slices s, in order, of part[s][m][c]); four columns per thread.
+template <int RR>
+__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ part, int M, int slices,
+                                                             __half* __restrict__ T) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // first of four elements
+  if (e >= (int64_t)M * RR) return;
+  v4f v = *reinterpret_cast<const v4f*>(part + e);
+  for (int s = 1; s < slices; ++s) v += *reinterpret_cast<const v4f*>(part + (int64_t)s * M * RR + e);
+  const __half2 h0 = __floats2half2_rn(v[0], v[1]), h1 = __floats2half2_rn(v[2], v[3]);
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<v2u*>(T + e) = v2u{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+}
+
+// ---- split-K workspace: fp32 partial tiles, one per device, allocated on first use and
+// kept until the process ends.
+constexpr int64_t LR_PART_BYTES = 32ll << 20;
+
+static hipError_t lr_workspace(float*& part) {
+  static std::mutex mu;
+  static std::map<int, float*> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) {
+    part = it->second;
+    return hipSuccess;
+  }
+  e = hipMalloc(&part, LR_PART_BYTES);
+  if (e != hipSuccess) return e;
+  per_device[dev] = part;
+  return hipSuccess;
+}
+
+// Slices of K per 64-row block: enough workgroups for every compute unit to hold a few,
+// a slice of at least four chunks, and partials that fit the workspace.
+static int lr_slices(int64_t M, int64_t K, int r) {
+  const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
+  const int64_t nch = (K + LR_KC - 1) / LR_KC;
+  const int64_t want = 4 * (int64_t)device_cu_count();
+  int64_t s = (want + blocks - 1) / blocks;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nch / 4));
+  while (s > 1 && s * M * r * 4 > LR_PART_BYTES) --s;
+  return (int)std::max<int64_t>(s, 1);
+}
+
+template <int RR>
+static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, __half* T, hipStream_t s,
+                                 int slices) {
+  constexpr int NS = RR == 64 ? 2 : 3;
+  const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
+  const int64_t nch = (K + LR_KC - 1) / LR_KC;
+  const int cps = (int)((nch + slices - 1) / slices);
+  slices = (int)((nch + cps - 1) / cps);                     // no empty slice
+  float* part = nullptr;
+  if (slices > 1) {
+    const hipError_t e = lr_workspace(part);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((lowrank_down_kernel<RR, NS>), dim3((unsigned)(blocks * slices)), dim3(256), 0, s, X, L1,
+                     (int)M, (int)K, slices, cps, part, T);
+  if (slices > 1) {
+    const int64_t threads = M * RR / 4;
+    hipLaunchKernelGGL((lowrank_reduce_kernel<RR>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       part, (int)M, slices, T);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
                                hipStream_t s) {
-  // one batch of 8 k-steps per wavefront for K up to 8 x 32 x SPLIT; long rows use 16
-  // wavefronts so each still issues its loads in one or two batches
-  if (K >= 8192) return lowrank_launch<16>(X, L1, M, K, r, T, s);
-  return lowrank_launch<8>(X, L1, M, K, r, T, s);
+  const int slices = lr_slices(M, K, r);
+  switch (r) {
+    case 16: return lowrank_launch<16>(X, L1, M, K, T, s, slices);
+    case 32: return lowrank_launch<32>(X, L1, M, K, T, s, slices);
+    case 64: return lowrank_launch<64>(X, L1, M, K, T, s, slices);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kq

@@ -3,9 +3,8 @@
 // KroQuant §01 / OrbitQuant §03: both operands are already in the transformed basis
 // ((XP) and (P^-1 W)), so the 4-bit product needs no transform of its own.  Each pair
 // of 32-element blocks contributes 2^(ex + ew) sum_k e2m1(qx) e2m1(qw), which is exactly
-// what gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 computes with FP4 operands and E8M0
-// scale bytes: lane l holds row l%16 and the 32 codes of k-block l/16 (16 bytes,
-// element 2i in the low nibble), plus that block's scale byte.
+// what gfx950's scaled FP4 MFMA computes from E2M1 codes (element 2i in the low nibble of
+// byte i) and E8M0 scale bytes.
 // SVDQuant explainer §3: the low-rank branch is fused into the same kernel: the
 // accumulators start from T L2^T (fp16 MFMA), so no separate pass touches Y.
 // CentriQ abstract: the rank-1 term mu wbar^T restores the token means before the store.
@@ -13,11 +12,12 @@
 // The MFMA computes C^T tiles (weight rows as the A operand, activation rows as B), so a
 // lane ends with four consecutive output columns of one output row: one 8-byte store.
 //
-// Pipeline per 128-wide k-step (64 code bytes + 4 scale bytes per row):
-//   global -> registers two k-steps ahead (two staging sets, ping-pong),
-//   registers -> LDS one k-step ahead (two LDS buffers),
-//   LDS -> MFMA fragments for the current k-step.
-// Barriers fence only LDS, so the global prefetch stays in flight across them.
+// Two kernel forms share that arithmetic:
+//   - a configurable-tile form that stages the operands global -> registers -> LDS, for
+//     small grids and for K not a multiple of 512;
+//   - a 256x256-tile form whose operands go from global memory straight into LDS (buffer
+//     loads with the LDS destination), four stages deep, for the large shapes.
+// Per 128-wide k-step a row contributes 64 code bytes and 4 scale bytes.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -27,12 +27,13 @@ namespace kq {
 // MFMA fragment reads (16 rows x one chunk) and the staging writes hit distinct banks.
 __device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 
-// Tile configuration: BN weight rows x BM activation rows per workgroup, WN x WM
+// Configurable-tile form.  BN weight rows x BM activation rows per workgroup, WN x WM
 // wavefronts, each owning a (BN/WN) x (BM/WM) block of 32x32 MFMA tiles.  PF = how many
-// k-steps ahead the global loads run (1 or 2 register staging sets).
+// k-steps ahead the global loads run (1 or 2 register staging sets); registers go to LDS
+// one k-step ahead (two LDS buffers), and barriers fence only LDS, so the global
+// prefetch stays in flight across them.
 //
 // The 32x32x64 form of the scaled FP4 MFMA is the one that runs at the doubled FP4 rate
 // on gfx950 (the 16x16x128 form issues at the FP8 rate).  Its operand layout: lane l
@@ -122,13 +123,16 @@ __global__ __launch_bounds__(C::NT) void w4a4_gemm_kernel(
   const int lsb = tid < BM ? C::BS_OFF + 4 * tid : C::DUMMY_OFF + 4 * tid;
   const int sa_ok = tid < BN, sb_ok = tid < BM;
 
+  // every offset goes through the range-checked vector offset; k-steps past the last one
+  // (prefetched by the pipeline, never consumed) read as zeros
   auto gload = [&](S& st, int ks) {
+    const bool kv = ks < nk;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, oa[i], 64 * ks, 0);
+    for (int i = 0; i < ACH; ++i) st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, kv ? oa[i] + 64 * ks : KQ_OOB, 0, 0);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, ob[i], 64 * ks, 0);
-    st.sa = __builtin_amdgcn_raw_buffer_load_b32(rAS, sa_ok ? osa : 0x7FFFFFF0, 4 * ks, 0);
-    st.sb = __builtin_amdgcn_raw_buffer_load_b32(rBS, sb_ok ? osb : 0x7FFFFFF0, 4 * ks, 0);
+    for (int i = 0; i < BCH; ++i) st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, kv ? ob[i] + 64 * ks : KQ_OOB, 0, 0);
+    st.sa = __builtin_amdgcn_raw_buffer_load_b32(rAS, (sa_ok && kv) ? osa + 4 * ks : KQ_OOB, 0, 0);
+    st.sb = __builtin_amdgcn_raw_buffer_load_b32(rBS, (sb_ok && kv) ? osb + 4 * ks : KQ_OOB, 0, 0);
   };
   auto lstore = [&](const S& st, int buf) {
     uint8_t* base = lds + buf * C::BUF;
@@ -206,8 +210,8 @@ __global__ __launch_bounds__(C::NT) void w4a4_gemm_kernel(
 
   // The scheduling fences keep the order load-issue / MFMAs / LDS stores: the stores wait
   // for their global loads, and hoisting them above the MFMAs would expose the whole
-  // load latency on every k-step.  Loads past the last k-step read past the operand window
-  // or into the next row and are never consumed.
+  // load latency on every k-step.  Loads past the last k-step take the out-of-range offset
+  // (they return zeros) and are never consumed.
   if (C::PF == 2) {
     // two k-steps per trip so the staging sets alternate without register copies:
     // entering a trip, LDS buffer 0 holds k-step ks and st1 holds ks+1 (possibly in flight)
@@ -270,6 +274,335 @@ __global__ __launch_bounds__(C::NT) void w4a4_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Large-tile form: 256x256 tiles on 4 wavefronts (2 x 2), each owning a 128 x 128 block of
+// 4 x 4 MFMA tiles (256 fp32 accumulators per lane, held in the accumulation registers),
+// which halves the LDS bytes read per MFMA against 128 x 64 wave tiles.  Per 128-wide
+// k-step the workgroup stages 32 KiB of codes; the fragments of the next 64-wide slice
+// are read while the current slice's MFMAs run, so a single barrier per k-step suffices.
+// Scale bytes are read as one dword per row and k-step: lane l shifts it by 8 (l / 32)
+// and the MFMA's byte select picks block 2 s + l / 32.
+struct Tile256 {
+  static constexpr int BN = 256, BM = 256, NT = 256, TN = 4, TM = 4;
+};
+
+// FP4 MFMA operand from 16 code bytes: the FP4 form reads only the first four registers.
+__device__ __forceinline__ v8i fp4_operand(const v4i& v) { return v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
+
+// ---------------------------------------------------------------------------------
+// The operands go from HBM straight into LDS (buffer loads with the LDS
+// destination), so staging needs no registers and no LDS store instructions; four code
+// stages keep three k-steps of loads in flight.  A load instruction writes 64 lanes x 16
+// bytes to consecutive LDS bytes; lane L of the instruction that fills rows
+// 16 q .. 16 q + 15 fetches the global chunk that the swizzled layout expects at slot L
+// (row 16 q + L / 4, chunk (L % 4) ^ swizzle(row)).  Scales come in groups of four
+// k-steps: one 16-byte load per row (a lane per row) into a double-buffered scale area,
+// so their loads touch a fraction of the cache lines that per-k-step dword loads would.
+// All offsets go in the range-checked vector offset.
+// The loads are issued from inline assembly: the compiler's wait insertion would
+// otherwise wait for every outstanding LDS load before each LDS read.  The kernel waits
+// itself (at k-step ks, for the code loads of ks + 1; at most 16 younger loads of this
+// wave are then outstanding), and one barrier per k-step makes every wave's loads visible
+// and frees the stage that the next loads refill.
+constexpr int DMA_STAGES = 4;
+constexpr int DMA_CODE_LOADS = 8;   // code load instructions per wave per k-step
+constexpr int DMA_STAGE_BYTES = Tile256::BN * 64 + Tile256::BM * 64;                  // 32 KiB of codes
+constexpr int DMA_SC_OFF = DMA_STAGES * DMA_STAGE_BYTES;                       // scale groups
+constexpr int DMA_SC_BYTES = (Tile256::BN + Tile256::BM) * 16;                        // one group, both operands
+constexpr int DMA_MU_OFF = DMA_SC_OFF + 2 * DMA_SC_BYTES;                     // wbar, mu of the tile
+constexpr int DMA_LDS = DMA_MU_OFF + 2048;                                    // 149504 bytes
+
+template <bool LR, bool MU>
+__global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, const uint8_t* __restrict__ xcodes,
+    const uint8_t* __restrict__ xscales, int M, int N, int K, const __half* __restrict__ T,
+    const __half* __restrict__ L2, int r, const __half* __restrict__ mu, const __half* __restrict__ wbar,
+    __half* __restrict__ Y) {
+  constexpr int BN = Tile256::BN, BM = Tile256::BM, TN = Tile256::TN, TM = Tile256::TM, NS = DMA_STAGES, SB = DMA_STAGE_BYTES;
+  constexpr int A_OFF = 0, B_OFF = BN * 64;                       // within a code stage
+  constexpr int SA_OFF = 0, SBM_OFF = BN * 16;                    // within a scale group
+  __shared__ __align__(16) uint8_t lds[DMA_LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, wm = wid >> 1;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  const int ntiles = tiles_n * tiles_m;
+  int pid = blockIdx.x;
+  {
+    const int per = ntiles / 8;
+    if (pid < 8 * per) pid = (pid % 8) * per + pid / 8;
+  }
+  constexpr int GM = 8;
+  const int group = pid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tile_m = first_m + (pid % (GM * tiles_n)) % gsize;
+  const int tile_n = (pid % (GM * tiles_n)) / gsize;
+  const int n0 = tile_n * BN, m0 = tile_m * BM;
+
+  const int KB = K >> 1, KS = K >> 5, nk = K >> 7;
+  const v4i rA = rsrc_words(wcodes + (int64_t)n0 * KB, (int64_t)(N - n0) * KB);
+  const v4i rB = rsrc_words(xcodes + (int64_t)m0 * KB, (int64_t)(M - m0) * KB);
+  const v4i rAS = rsrc_words(wscales + (int64_t)n0 * KS, (int64_t)(N - n0) * KS);
+  const v4i rBS = rsrc_words(xscales + (int64_t)m0 * KS, (int64_t)(M - m0) * KS);
+  // low-rank operands: L2 rows go with the weight rows (A side), T rows with the tokens
+  const v4i rL = rsrc_words(L2 + (int64_t)n0 * r, LR ? (int64_t)(N - n0) * r * 2 : 0);
+  const v4i rT = rsrc_words(T + (int64_t)m0 * r, LR ? (int64_t)(M - m0) * r * 2 : 0);
+
+  // wave w fills code rows 64 w .. 64 w + 63 of both operands (four instructions each)
+  // and the scale groups of rows 64 w + lane
+  int og[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 64 * wid + 16 * q + (lane >> 2);
+    og[q] = row * KB + 16 * ((lane & 3) ^ chunk_swz(row));
+  }
+  const int osc = (64 * wid + lane) * KS;
+  const uint32_t lds0 = lds_addr(lds);
+  auto code_load = [&](int ks, int g) {     // code load g (0..7) of k-step ks into stage ks % NS
+    const uint32_t st = lds0 + (uint32_t)((ks % NS) * SB);
+    const int off = ks < nk ? og[g & 3] + 64 * ks : KQ_OOB;
+    if (g < 4) lds_load16(rA, st + A_OFF + (64 * wid + 16 * g) * 64, off);
+    else lds_load16(rB, st + B_OFF + (64 * wid + 16 * (g - 4)) * 64, off);
+  };
+  // scale group grp (k-steps 4 grp .. 4 grp + 3), issued only when skip is zero: 16 bytes
+  // per row (K is a multiple of 512, so a group never straddles two rows).  The skip is a
+  // branch inside the assembly so that the loop body stays one block for the instruction
+  // scheduler (a compiler branch here lets it move MFMAs across the barrier).
+  auto scale_loads = [&](int grp, int skip) {
+    const uint32_t sc = lds0 + (uint32_t)(DMA_SC_OFF + (grp & 1) * DMA_SC_BYTES + 16 * 64 * wid);
+    const int off = 4 * grp < nk ? osc + 16 * grp : KQ_OOB;
+    asm volatile(
+        "s_cmp_lg_u32 %0, 0\n\t"
+        "s_cbranch_scc1 1f\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %3, %4, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "buffer_load_dwordx4 %3, %5, 0 offen lds\n"
+        "1:"
+        :: "s"(__builtin_amdgcn_readfirstlane(skip)), "s"(__builtin_amdgcn_readfirstlane(sc + SA_OFF)),
+           "s"(__builtin_amdgcn_readfirstlane(sc + SBM_OFF)), "v"(off), "s"(rAS), "s"(rBS)
+        : "memory", "m0", "scc");
+  };
+
+  const int wrow_a = wn * 128, wrow_b = wm * 128;
+  auto read_frags = [&](const uint8_t* base, int sl, v8i* fa, v8i* fb) {
+    const int ch = 2 * sl + h;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int row = wrow_a + 32 * i + l32;
+      fa[i] = fp4_operand(*reinterpret_cast<const v4i*>(base + A_OFF + row * 64 + 16 * (ch ^ chunk_swz(row))));
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = wrow_b + 32 * j + l32;
+      fb[j] = fp4_operand(*reinterpret_cast<const v4i*>(base + B_OFF + row * 64 + 16 * (ch ^ chunk_swz(row))));
+    }
+  };
+  auto read_scales = [&](int ks, int* sa, int* sb) {   // the scale dwords of k-step ks
+    const uint8_t* sc = lds + DMA_SC_OFF + ((ks >> 2) & 1) * DMA_SC_BYTES + 4 * (ks & 3);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + SA_OFF + 16 * (wrow_a + 32 * i + l32)) >> (8 * h));
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+      sb[j] = (int)(*reinterpret_cast<const uint32_t*>(sc + SBM_OFF + 16 * (wrow_b + 32 * j + l32)) >> (8 * h));
+  };
+
+  v16f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Prologue: scale group 0 and code stages 0..2, behind the first 32 columns of the
+  // low-rank operands, which borrow code stage 3 (16-byte pieces in the same swizzled
+  // 64-byte rows as the codes; pieces past column r read as zeros).  The low-rank product
+  // enters the accumulators first; r = 64 takes a second pass through the same stage.
+  auto lr_load = [&](int rc) {
+    const uint32_t st = lds0 + (uint32_t)((NS - 1) * SB);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 64 * wid + 16 * q + (lane >> 2);
+      const int piece = 8 * ((lane & 3) ^ chunk_swz(row));     // column of the piece
+      const int off = rc + piece < r ? (row * r + rc + piece) * 2 : KQ_OOB;
+      lds_load16(rL, st + A_OFF + (64 * wid + 16 * q) * 64, off);
+      lds_load16(rT, st + B_OFF + (64 * wid + 16 * q) * 64, off);
+    }
+  };
+  auto lr_mfma = [&]() {
+    const uint8_t* base = lds + (NS - 1) * SB;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      v8h lt[TM], ll[TN];
+      const int ch = 2 * c2 + h;
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int row = wrow_a + 32 * i + l32;
+        ll[i] = *reinterpret_cast<const v8h*>(base + A_OFF + row * 64 + 16 * (ch ^ chunk_swz(row)));
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int row = wrow_b + 32 * j + l32;
+        lt[j] = *reinterpret_cast<const v8h*>(base + B_OFF + row * 64 + 16 * (ch ^ chunk_swz(row)));
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ll[i], lt[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  if (MU && wid == 0) {
+    // the tile's 256 column sums and 256 token means: one load each, lanes 0..31 carry
+    // 16 bytes (8 values) apiece, lanes 32..63 read past the range and write zeros
+    const v4i rW = rsrc_words(wbar + n0, (int64_t)(N - n0) * 2);
+    const v4i rM = rsrc_words(mu + m0, (int64_t)(M - m0) * 2);
+    const int off = lane < 32 ? 16 * lane : KQ_OOB;
+    lds_load16(rW, lds0 + DMA_MU_OFF, off);
+    lds_load16(rM, lds0 + DMA_MU_OFF + 1024, off);
+  }
+  if (LR) lr_load(0);
+  scale_loads(0, 0);
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+#pragma unroll
+    for (int g = 0; g < DMA_CODE_LOADS; ++g) code_load(p, g);
+  if (LR) {
+    // the low-rank pieces and everything before the 16 youngest loads (scale group 0,
+    // code stage 0) have landed once at most 16 loads of this wave are outstanding
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS));
+    lds_barrier();
+    lr_mfma();
+    for (int rc = 32; rc < r; rc += 32) {
+      lds_barrier();                              // every wave has read the previous chunk
+      lr_load(rc);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+      lr_mfma();
+    }
+    lds_barrier();                                // stage 3 is free for the k-loop's loads
+  }
+
+  // k-loop.  The loads of k-steps past the last one write zeros into stages that are
+  // never computed; they are drained before the epilogue.
+  //   slice-1 fragment reads of stage ks;
+  //   slice-0 MFMAs, with the eight code loads of k-step ks + 3 issued between them (the
+  //     address unit is shared by the workgroup's four waves: issued in a burst, the
+  //     loads would stall the wave -- and its matrix core -- for their whole issue time);
+  //   wait for this wave's code loads of k-step ks + 1, barrier;
+  //   at the start of a group of four k-steps, the next group's scale loads;
+  //   scale and slice-0 fragment reads of stage ks + 1;
+  //   slice-1 MFMAs of ks.
+  // Waiting for the 16 youngest loads to be the only ones outstanding covers the code
+  // loads of ks + 1 and every scale group issued before them.
+  if (!LR) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS));
+    lds_barrier();
+  }
+  v8i a0[TN], b0[TM];
+  int sa[TN], sb[TM];
+  read_scales(0, sa, sb);
+  read_frags(lds, 0, a0, b0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const uint8_t* const cur = lds + (ks % NS) * SB;
+    const uint8_t* const nxt = lds + ((ks + 1) % NS) * SB;
+    v8i a1[TN], b1[TM];
+    read_frags(cur, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[i], b0[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
+        // code load g after MFMA m for (m, g) = (0,0) (1,1) (3,2) (4,3) (6,4) (7,5) (9,6) (10,7)
+        const int m = TM * i + j;
+        const int g = (m % 3 == 2 || m > 10) ? -1 : m - m / 3;
+        if (g >= 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          code_load(ks + NS - 1, g);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS));
+    lds_barrier();
+    scale_loads((ks >> 2) + 1, ks & 3);
+    int nsa[TN], nsb[TM];
+    read_scales(ks + 1, nsa, nsb);
+    read_frags(nxt, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[i], b1[j], acc[i][j], 4, 4, 2, sa[i], 2, sb[j]);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) sa[i] = nsa[i];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) sb[j] = nsb[j];
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no load may land in LDS after the workgroup ends
+
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(Y + (int64_t)m0 * N, (int64_t)(M - m0) * N * 2);
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  const __half* const wbar_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF);
+  const __half* const mu_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF + 1024);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int ml = wrow_b + 32 * j + l32;
+    const float mm = MU ? __half2float(mu_t[ml]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = wrow_a + 32 * i + 8 * g + 4 * h;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+        if (MU) {
+          // halves unpacked from scalar dwords (a bit cast of a vector element inside an
+          // unrolled loop is mis-compiled to read element 0)
+          const uint32_t* const wp = reinterpret_cast<const uint32_t*>(wbar_t + nl);
+          const uint32_t w01 = wp[0], w23 = wp[1];
+          v[0] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 & 0xFFFFu))), v[0]);
+          v[1] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 >> 16))), v[1]);
+          v[2] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 & 0xFFFFu))), v[2]);
+          v[3] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 >> 16))), v[3]);
+        }
+        const __half2 h0 = __floats2half2_rn(v[0], v[1]);
+        const __half2 h1 = __floats2half2_rn(v[2], v[3]);
+        const int off = n0 + nl < N ? (ml * N + n0 + nl) * 2 : KQ_OOB;
+        const v2u outv = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+        __builtin_amdgcn_raw_buffer_store_b64(outv, rY, off, 0, 0);
+      }
+    }
+  }
+}
+
+static hipError_t gemm_dma_launch(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,
+                                 const uint8_t* wcodes, const uint8_t* wscales, int64_t N, const __half* T,
+                                 const __half* L2, int r, const __half* mu, const __half* wbar, __half* Y,
+                                 hipStream_t s) {
+  const int64_t tiles = ((N + Tile256::BN - 1) / Tile256::BN) * ((M + Tile256::BM - 1) / Tile256::BM);
+  const dim3 g((unsigned)tiles), b(Tile256::NT);
+  if (r > 0 && mu)
+    hipLaunchKernelGGL((w4a4_gemm_dma_kernel<true, true>), g, b, 0, s, wcodes, wscales, xcodes, xscales, (int)M,
+                       (int)N, (int)K, T, L2, r, mu, wbar, Y);
+  else if (r > 0)
+    hipLaunchKernelGGL((w4a4_gemm_dma_kernel<true, false>), g, b, 0, s, wcodes, wscales, xcodes, xscales, (int)M,
+                       (int)N, (int)K, T, L2, r, mu, wbar, Y);
+  else if (mu)
+    hipLaunchKernelGGL((w4a4_gemm_dma_kernel<false, true>), g, b, 0, s, wcodes, wscales, xcodes, xscales, (int)M,
+                       (int)N, (int)K, T, L2, r, mu, wbar, Y);
+  else
+    hipLaunchKernelGGL((w4a4_gemm_dma_kernel<false, false>), g, b, 0, s, wcodes, wscales, xcodes, xscales, (int)M,
+                       (int)N, (int)K, T, L2, r, mu, wbar, Y);
+  return hipGetLastError();
+}
+
 template <class C>
 static hipError_t gemm_launch(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,
                               const uint8_t* wcodes, const uint8_t* wscales, int64_t N, const __half* T,
@@ -300,6 +633,8 @@ hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64
   using Big = GemmCfg<256, 256, 2, 4, 1>;
   using Small = GemmCfg<128, 128, 2, 2, 1>;
   const int64_t big_tiles = ((N + 255) / 256) * ((M + 255) / 256);
+  if (big_tiles >= device_cu_count() / 2 && K % 512 == 0)
+    return gemm_dma_launch(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
   if (big_tiles >= device_cu_count() / 2)
     return gemm_launch<Big>(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
   return gemm_launch<Small>(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
