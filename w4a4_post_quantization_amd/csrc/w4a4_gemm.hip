@@ -351,18 +351,16 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
   const v4i rT = rsrc_words(T + (int64_t)m0 * r, LR ? (int64_t)(M - m0) * r * 2 : 0);
 
   // wave w fills code rows 64 w .. 64 w + 63 of both operands (four instructions each)
-  // and the scale groups of rows 64 w + lane
-  int og[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 64 * wid + 16 * q + (lane >> 2);
-    og[q] = row * KB + 16 * ((lane & 3) ^ chunk_swz(row));
-  }
+  // and the scale groups of rows 64 w + lane.  Instruction q covers rows 64 w + 16 q ..
+  // + 15; the chunk swizzle depends on row bits 1..3 only, so the four instructions share
+  // the lane's chunk and differ by 16 rows (a uniform offset).
+  const int lrow = 64 * wid + (lane >> 2);
+  const int og0 = lrow * KB + 16 * ((lane & 3) ^ chunk_swz(lrow));
   const int osc = (64 * wid + lane) * KS;
   const uint32_t lds0 = lds_addr(lds);
   auto code_load = [&](int ks, int g) {     // code load g (0..7) of k-step ks into stage ks % NS
     const uint32_t st = lds0 + (uint32_t)((ks % NS) * SB);
-    const int off = ks < nk ? og[g & 3] + 64 * ks : KQ_OOB;
+    const int off = ks < nk ? og0 + (16 * (g & 3) * KB + 64 * ks) : KQ_OOB;
     if (g < 4) lds_load16(rA, st + A_OFF + (64 * wid + 16 * g) * 64, off);
     else lds_load16(rB, st + B_OFF + (64 * wid + 16 * (g - 4)) * 64, off);
   };
@@ -387,27 +385,25 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
   };
 
   const int wrow_a = wn * 128, wrow_b = wm * 128;
+  // Fragment i of a wave reads row wrow + 32 i + l32; the chunk swizzle depends on row bits
+  // 1..3 only, so it is the same for every i and the four reads of an operand differ by a
+  // constant 2 KiB.
+  const int sw = chunk_swz(l32);
+  const int fa_base[2] = {A_OFF + (wrow_a + l32) * 64 + 16 * (h ^ sw), A_OFF + (wrow_a + l32) * 64 + 16 * ((2 + h) ^ sw)};
+  const int fb_base[2] = {B_OFF + (wrow_b + l32) * 64 + 16 * (h ^ sw), B_OFF + (wrow_b + l32) * 64 + 16 * ((2 + h) ^ sw)};
   auto read_frags = [&](const uint8_t* base, int sl, v8i* fa, v8i* fb) {
-    const int ch = 2 * sl + h;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int row = wrow_a + 32 * i + l32;
-      fa[i] = fp4_operand(*reinterpret_cast<const v4i*>(base + A_OFF + row * 64 + 16 * (ch ^ chunk_swz(row))));
-    }
+    for (int i = 0; i < TN; ++i) fa[i] = fp4_operand(*reinterpret_cast<const v4i*>(base + fa_base[sl] + 2048 * i));
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int row = wrow_b + 32 * j + l32;
-      fb[j] = fp4_operand(*reinterpret_cast<const v4i*>(base + B_OFF + row * 64 + 16 * (ch ^ chunk_swz(row))));
-    }
+    for (int j = 0; j < TM; ++j) fb[j] = fp4_operand(*reinterpret_cast<const v4i*>(base + fb_base[sl] + 2048 * j));
   };
+  const int sa_base = SA_OFF + 16 * (wrow_a + l32), sb_base = SBM_OFF + 16 * (wrow_b + l32);
   auto read_scales = [&](int ks, int* sa, int* sb) {   // the scale dwords of k-step ks
     const uint8_t* sc = lds + DMA_SC_OFF + ((ks >> 2) & 1) * DMA_SC_BYTES + 4 * (ks & 3);
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
-      sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + SA_OFF + 16 * (wrow_a + 32 * i + l32)) >> (8 * h));
+    for (int i = 0; i < TN; ++i) sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + sa_base + 512 * i) >> (8 * h));
 #pragma unroll
-    for (int j = 0; j < TM; ++j)
-      sb[j] = (int)(*reinterpret_cast<const uint32_t*>(sc + SBM_OFF + 16 * (wrow_b + 32 * j + l32)) >> (8 * h));
+    for (int j = 0; j < TM; ++j) sb[j] = (int)(*reinterpret_cast<const uint32_t*>(sc + sb_base + 512 * j) >> (8 * h));
   };
 
   v16f acc[TN][TM];
@@ -547,7 +543,6 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no load may land in LDS after the workgroup ends
 
   const __amdgpu_buffer_rsrc_t rY = make_rsrc(Y + (int64_t)m0 * N, (int64_t)(M - m0) * N * 2);
-  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
   const __half* const wbar_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF);
   const __half* const mu_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF + 1024);
 #pragma unroll
@@ -557,26 +552,36 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wrow_a + 32 * i + 8 * g + 4 * h;
-        float v[4];
+      for (int p = 0; p < 2; ++p) {
+        uint32_t pk[2][2];                                   // [group of the pair][dword]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-        if (MU) {
-          // halves unpacked from scalar dwords (a bit cast of a vector element inside an
-          // unrolled loop is mis-compiled to read element 0)
-          const uint32_t* const wp = reinterpret_cast<const uint32_t*>(wbar_t + nl);
-          const uint32_t w01 = wp[0], w23 = wp[1];
-          v[0] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 & 0xFFFFu))), v[0]);
-          v[1] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 >> 16))), v[1]);
-          v[2] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 & 0xFFFFu))), v[2]);
-          v[3] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 >> 16))), v[3]);
+        for (int u = 0; u < 2; ++u) {
+          const int g = 2 * p + u;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          if (MU) {
+            // halves unpacked from scalar dwords (a bit cast of a vector element inside an
+            // unrolled loop is mis-compiled to read element 0)
+            const uint32_t* const wp = reinterpret_cast<const uint32_t*>(wbar_t + wrow_a + 32 * i + 8 * g + 4 * h);
+            const uint32_t w01 = wp[0], w23 = wp[1];
+            v[0] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 & 0xFFFFu))), v[0]);
+            v[1] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w01 >> 16))), v[1]);
+            v[2] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 & 0xFFFFu))), v[2]);
+            v[3] = __builtin_fmaf(mm, __half2float(__ushort_as_half((unsigned short)(w23 >> 16))), v[3]);
+          }
+          pk[u][0] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v[0], v[1]));
+          pk[u][1] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v[2], v[3]));
         }
-        const __half2 h0 = __floats2half2_rn(v[0], v[1]);
-        const __half2 h1 = __floats2half2_rn(v[2], v[3]);
-        const int off = n0 + nl < N ? (ml * N + n0 + nl) * 2 : KQ_OOB;
-        const v2u outv = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
-        __builtin_amdgcn_raw_buffer_store_b64(outv, rY, off, 0, 0);
+        // a lane holds columns 8 g + 4 h .. + 3 of groups g = 2p, 2p + 1; one lane-half swap
+        // per dword leaves lanes 0..31 with the eight columns of group 2p and lanes 32..63
+        // with those of group 2p + 1: one 16-byte store per lane
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+        const v4u outv = {s0[0], s1[0], s0[1], s1[1]};
+        const int col = wrow_a + 32 * i + 8 * (2 * p + h);
+        const int off = n0 + col < N ? (ml * N + n0 + col) * 2 : KQ_OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, outv), rY, off, 0, 0);
       }
     }
   }
