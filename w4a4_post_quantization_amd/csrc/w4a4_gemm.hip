@@ -483,17 +483,15 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
   }
 
   // k-loop.  The loads of k-steps past the last one write zeros into stages that are
-  // never computed; they are drained before the epilogue.
-  //   slice-1 fragment reads of stage ks;
-  //   slice-0 MFMAs, with the eight code loads of k-step ks + 3 issued between them (the
-  //     address unit is shared by the workgroup's four waves: issued in a burst, the
-  //     loads would stall the wave -- and its matrix core -- for their whole issue time);
-  //   wait for this wave's code loads of k-step ks + 1, barrier;
+  // never computed; they are drained before the epilogue.  Per k-step:
+  //   slice-0 MFMAs, interleaved with the slice-1 fragment reads of ks and the first four
+  //     code loads of ks + 3 (the address unit is shared by the workgroup's four waves:
+  //     issued in a burst, the loads would stall the wave -- and its matrix core -- for
+  //     their whole issue time);
+  //   wait for this wave's loads of ks + 1, barrier;
   //   at the start of a group of four k-steps, the next group's scale loads;
-  //   scale and slice-0 fragment reads of stage ks + 1;
-  //   slice-1 MFMAs of ks.
-  // Waiting for the 16 youngest loads to be the only ones outstanding covers the code
-  // loads of ks + 1 and every scale group issued before them.
+  //   slice-1 MFMAs, interleaved with the scale and slice-0 fragment reads of ks + 1 and
+  //     the last four code loads of ks + 3.
   if (!LR) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS));
     lds_barrier();
@@ -506,35 +504,57 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
     const uint8_t* const cur = lds + (ks % NS) * SB;
     const uint8_t* const nxt = lds + ((ks + 1) % NS) * SB;
     v8i a1[TN], b1[TM];
-    read_frags(cur, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
+    // slice 0: MFMA m is preceded by slice-1 fragment m (m < 8: four A, then four B) and
+    // followed, for m = 1, 5, 9, 13, by code load (m - 1) / 4 of k-step ks + 3
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[i], b0[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
-        // code load g after MFMA m for (m, g) = (0,0) (1,1) (3,2) (4,3) (6,4) (7,5) (9,6) (10,7)
         const int m = TM * i + j;
-        const int g = (m % 3 == 2 || m > 10) ? -1 : m - m / 3;
-        if (g >= 0) {
+        if (m < 8) {
           __builtin_amdgcn_sched_barrier(0);
-          code_load(ks + NS - 1, g);
+          if (m < 4) a1[m] = fp4_operand(*reinterpret_cast<const v4i*>(cur + fa_base[1] + 2048 * m));
+          else b1[m - 4] = fp4_operand(*reinterpret_cast<const v4i*>(cur + fb_base[1] + 2048 * (m - 4)));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0[i], b0[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
+        if (m % 4 == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          code_load(ks + NS - 1, m / 4);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS));
+    // k-step ks + 1 has landed once at most 12 of this wave's loads are outstanding: those
+    // of ks + 2 and the first half of ks + 3 (the second half of ks + 1 went out before
+    // any of them)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * DMA_CODE_LOADS - DMA_CODE_LOADS / 2));
     lds_barrier();
     scale_loads((ks >> 2) + 1, ks & 3);
     int nsa[TN], nsb[TM];
-    read_scales(ks + 1, nsa, nsb);
-    read_frags(nxt, 0, a0, b0);
+    const uint8_t* const sc = lds + DMA_SC_OFF + (((ks + 1) >> 2) & 1) * DMA_SC_BYTES + 4 * ((ks + 1) & 3);
     __builtin_amdgcn_sched_barrier(0);
+    // slice 1: MFMA m is followed by read m of the next k-step (four A scales, four B
+    // scales, four A fragments, four B fragments of slice 0) and, for m = 1, 5, 9, 13, by
+    // code load 4 + (m - 1) / 4 of k-step ks + 3 (its stage was freed by the barrier above)
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
+      for (int j = 0; j < TM; ++j) {
+        const int m = TM * i + j;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[i], b1[j], acc[i][j], 4, 4, 2, sa[i], 2, sb[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m < 4) nsa[m] = (int)(*reinterpret_cast<const uint32_t*>(sc + sa_base + 512 * m) >> (8 * h));
+        else if (m < 8) nsb[m - 4] = (int)(*reinterpret_cast<const uint32_t*>(sc + sb_base + 512 * (m - 4)) >> (8 * h));
+        else if (m < 12) a0[m - 8] = fp4_operand(*reinterpret_cast<const v4i*>(nxt + fa_base[0] + 2048 * (m - 8)));
+        else b0[m - 12] = fp4_operand(*reinterpret_cast<const v4i*>(nxt + fb_base[0] + 2048 * (m - 12)));
+        __builtin_amdgcn_sched_barrier(0);
+        if (m % 4 == 1) {
+          code_load(ks + NS - 1, 4 + m / 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
 #pragma unroll
     for (int i = 0; i < TN; ++i) sa[i] = nsa[i];
 #pragma unroll
