@@ -176,6 +176,7 @@ def main():
             scales=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
             mu=torch.empty((M,), dtype=torch.float16, device=dev),
             T=torch.empty((M, r), dtype=torch.float16, device=dev),
+            lrws=torch.empty((max(kq.lowrank_down_workspace_bytes(M, K, r), 16),), dtype=torch.uint8, device=dev),
             Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
 
@@ -190,7 +191,7 @@ def main():
         Xs = Xsets[s % R]
         for li, L in enumerate(layers):
             X = Xs[L["K"]]
-            kq.lowrank_down(X, L["L1"], T=L["T"])
+            kq.lowrank_down(X, L["L1"], T=L["T"], workspace=L["lrws"])
             if ev:
                 ev[3 * li].record()
             kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 1
+#define KQ_ABI_VERSION 2
 
 typedef int32_t kq_status;
 enum {
@@ -140,13 +140,16 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt,
  *   T = fp16(X L1^T), fp32 accumulation on the fp16 matrix cores.
  * X fp16 [M][K] (the original activations: not centred, not transformed), L1 fp16 [r][K],
  * T fp16 [M][r] (caller-owned).  r in {16, 32, 64}; K % 32 == 0, K <= 2^20.
- * When M is small against the device, K is split over several workgroups whose fp32
- * partials go to a library-owned workspace (32 MiB per device, allocated on the first
- * such call and kept until the process ends) and a second kernel sums them in a fixed
- * order, so results do not depend on scheduling.  Calls that use the workspace must not
- * overlap on one device (issue them on one stream, or synchronize between them). */
+ * workspace (optional, caller-owned device memory, 16-byte aligned): when M is small
+ *   against the device, K is split over several workgroups whose fp32 partials go to the
+ *   workspace, and a second kernel sums them in a fixed order (results do not depend on
+ *   scheduling).  kq_lowrank_down_workspace_bytes gives the size that enables the full
+ *   split; a smaller workspace gives fewer slices, and NULL / 0 runs unsplit (same
+ *   results up to fp32 summation order, slower for small M).  The library allocates
+ *   nothing.  Calls that share a workspace must not overlap. */
+size_t kq_lowrank_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
 kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r,
-                          void* T, hipStream_t stream);
+                          void* T, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The 4-bit linear with its full-precision branches, one kernel:
  *   Y = Xq . Wq^T  +  T L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 1
+    assert kq.abi_version() == 2
     for s in range(0, 7):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
@@ -133,11 +133,21 @@ def test_linear_validation(lib):
 
 def test_lowrank_validation(lib):
     f = lib.kq_lowrank_down
-    assert f(None, FAKE, 4, 64, 32, FAKE, None) == 1
-    assert f(FAKE, FAKE, 4, 48, 32, FAKE, None) == 2
-    assert f(FAKE, FAKE, 4, 64, 8, FAKE, None) == 2
-    assert f(FAKE, FAKE, 0, 64, 32, FAKE, None) == 2
-    assert f(FAKE, FAKE_ODD, 4, 64, 32, FAKE, None) == 3
+    assert f(None, FAKE, 4, 64, 32, FAKE, None, 0, None) == 1
+    assert f(FAKE, FAKE, 4, 48, 32, FAKE, None, 0, None) == 2
+    assert f(FAKE, FAKE, 4, 64, 8, FAKE, None, 0, None) == 2
+    assert f(FAKE, FAKE, 0, 64, 32, FAKE, None, 0, None) == 2
+    assert f(FAKE, FAKE_ODD, 4, 64, 32, FAKE, None, 0, None) == 3
+    assert f(FAKE, FAKE, 4, 64, 32, FAKE, None, 1024, None) == 1      # size without a workspace
+    assert f(FAKE, FAKE, 4, 64, 32, FAKE, FAKE_ODD, 1024, None) == 3
+
+
+def test_lowrank_workspace_size(lib):
+    """The split only pays for small M; the size is slices x M x r x 4 bytes, 0 when unsplit."""
+    n = kq.lowrank_down_workspace_bytes(4608, 3072, 32)
+    assert n > 0 and n % (4608 * 32 * 4) == 0
+    assert kq.lowrank_down_workspace_bytes(4608, 128, 32) == 0          # one chunk of K: nothing to split
+    assert kq.lowrank_down_workspace_bytes(4608, 3072, 8) == 0          # invalid rank
 
 
 def test_binding_rejects_cpu_tensors():

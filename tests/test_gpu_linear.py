@@ -146,14 +146,15 @@ def test_w4a4_branch_variants(kq, rank, with_mu):
     assert err <= TOL
 
 
-def _check_lowrank(kq, M, K, r, seed=7):
+def _check_lowrank(kq, M, K, r, seed=7, workspace="default"):
     """T = fp16(X L1^T): within one fp16 rounding of the exact product (plus the float32
     accumulation bound: K / 8 sequential additions per lane and MFMA block, then the
     split-K partials)."""
     import torch
     X16 = synth.activations(M, K, seed, 2.0)
     _, L1, _ = synth.weights(K, 16, seed, 0, r)
-    T = kq.lowrank_down(torch.from_numpy(X16).cuda(), torch.from_numpy(L1).cuda())
+    kw = {} if isinstance(workspace, str) else {"workspace": workspace}
+    T = kq.lowrank_down(torch.from_numpy(X16).cuda(), torch.from_numpy(L1).cuda(), **kw)
     torch.cuda.synchronize()
     got = T.cpu().numpy().astype(np.float64)
     exact = X16.astype(np.float64) @ L1.astype(np.float64).T
@@ -166,6 +167,18 @@ def _check_lowrank(kq, M, K, r, seed=7):
                                    (1000, 3072, 64), (4608, 3072, 16), (4608, 12288, 32)])
 def test_lowrank_down_matches_oracle(kq, M, K, r):
     _check_lowrank(kq, M, K, r)
+
+
+def test_lowrank_down_workspace_sizes(kq):
+    """No workspace (one slice), a workspace for two slices, and the full one: all within
+    the same bound of the exact product."""
+    import torch
+    M, K, r = 300, 3072, 32
+    full = kq.lowrank_down_workspace_bytes(M, K, r)
+    assert full >= 2 * M * r * 4
+    for nb in (0, 2 * M * r * 4, full):
+        ws = torch.empty((nb,), dtype=torch.uint8, device="cuda") if nb else None
+        _check_lowrank(kq, M, K, r, seed=5, workspace=ws)
 
 
 def test_lowrank_down_repeated_calls(kq):

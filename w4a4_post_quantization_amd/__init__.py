@@ -17,7 +17,7 @@ import os
 
 __all__ = ["load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
            "transform_quantize", "fold_inverse_into_weights", "w4a4_linear",
-           "lowrank_down", "KQError"]
+           "lowrank_down", "lowrank_down_workspace_bytes", "KQError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -65,7 +65,9 @@ def load():
     lib.kq_fold_inverse_into_weights.restype = i32
     lib.kq_fold_inverse_into_weights.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp]
     lib.kq_lowrank_down.restype = i32
-    lib.kq_lowrank_down.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    lib.kq_lowrank_down.argtypes = [vp, vp, i64, i64, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.kq_lowrank_down_workspace_bytes.restype = ctypes.c_size_t
+    lib.kq_lowrank_down_workspace_bytes.argtypes = [i64, i64, i32]
     lib.kq_w4a4_linear.restype = i32
     lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib
@@ -221,8 +223,15 @@ def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None
     return wcodes, wscales, wbar
 
 
-def lowrank_down(X, L1, T=None, stream=None):
-    """T = fp16(X L1^T): the low-rank branch's down-projection (fp16 [M][r])."""
+def lowrank_down_workspace_bytes(M, K, r):
+    """Workspace bytes that let kq_lowrank_down split K over workgroups (0: no split)."""
+    return int(load().kq_lowrank_down_workspace_bytes(M, K, r))
+
+
+def lowrank_down(X, L1, T=None, workspace=None, stream=None):
+    """T = fp16(X L1^T): the low-rank branch's down-projection (fp16 [M][r]).  workspace:
+    a uint8 device tensor for the split-K partials; by default one of the size
+    lowrank_down_workspace_bytes is taken from torch's allocator."""
     torch = _torch()
     _check(X, "X", torch.float16)
     M, K = X.shape
@@ -230,7 +239,13 @@ def lowrank_down(X, L1, T=None, stream=None):
     _check(L1, "L1", torch.float16, (r, K))
     T = torch.empty((M, r), dtype=torch.float16, device=X.device) if T is None else T
     _check(T, "T", torch.float16, (M, r))
-    s = load().kq_lowrank_down(_ptr(X), _ptr(L1), M, K, r, _ptr(T), _stream(stream))
+    if workspace is None:
+        nb = lowrank_down_workspace_bytes(M, K, r)
+        workspace = torch.empty((nb,), dtype=torch.uint8, device=X.device) if nb else None
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
+    wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    s = load().kq_lowrank_down(_ptr(X), _ptr(L1), M, K, r, _ptr(T), wp, wn, _stream(stream))
     if s != KQ_OK:
         raise KQError(s, "kq_lowrank_down")
     return T

@@ -192,15 +192,23 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const vo
   return hip_status(e);
 }
 
+size_t kq_lowrank_down_workspace_bytes(int64_t M, int64_t K, int32_t r) {
+  if (M < 1 || K < 32 || K % 32 != 0 || (r != 16 && r != 32 && r != 64)) return 0;
+  return lowrank_workspace_bytes(M, K, r);
+}
+
 kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r, void* T,
-                          hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!X || !L1 || !T) return KQ_ERR_NULL;
   if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
   if (M > (1LL << 31) - 64 || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16)) return KQ_ERR_ALIGN;
+  if (workspace_bytes && !workspace) return KQ_ERR_NULL;
+  if (workspace && !aligned(workspace, 16)) return KQ_ERR_ALIGN;
   return hip_status(launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r,
-                                        static_cast<__half*>(T), stream));
+                                        static_cast<__half*>(T), static_cast<float*>(workspace),
+                                        workspace ? workspace_bytes : 0, stream));
 }
 
 kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,

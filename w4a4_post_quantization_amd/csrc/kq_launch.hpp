@@ -47,9 +47,11 @@ hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K,
                        hipStream_t s);
 hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
 
-// T[M][r] = fp16(X L1^T), fp32 accumulation.
+// T[M][r] = fp16(X L1^T), fp32 accumulation; split over K into `part` (fp32 partials,
+// part_bytes long, may be null) when that helps and fits.
+size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r);
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r,
-                               __half* T, hipStream_t s);
+                               __half* T, float* part, size_t part_bytes, hipStream_t s);
 
 // Y = Xq Wq^T (+ T L2^T) (+ mu wbar^T), MXFP4 x MXFP4.
 hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,

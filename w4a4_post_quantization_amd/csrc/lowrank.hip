@@ -9,15 +9,14 @@
 //     with the LDS destination, full 128-byte lines), NS chunks deep;
 //   - each of the four wavefronts owns 16 rows and all r columns: v_mfma_f32_16x16x32_f16
 //     (lane l: row l%16, eight consecutive k of the 16-byte piece 4 s + l/16 of the chunk);
-//   - with several K slices the fp32 partial tiles go to a workspace and a second, small
-//     kernel sums them in slice order (deterministic) and stores T.  (Summing them in the
+//   - with several K slices the fp32 partial tiles go to the caller's workspace and a
+//     second, small kernel sums them in slice order (deterministic) and stores T.  (Summing them in the
 //     last workgroup to finish a row block would need device-scope fences, which on this
 //     chip write back and invalidate the whole L2 of the compute die: far slower.)
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
-#include <map>
-#include <mutex>
+#include <algorithm>
 
 namespace kq {
 
@@ -147,53 +146,31 @@ __global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __rest
   *reinterpret_cast<v2u*>(T + e) = v2u{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
 }
 
-// ---- split-K workspace: fp32 partial tiles, one per device, allocated on first use and
-// kept until the process ends.
-constexpr int64_t LR_PART_BYTES = 32ll << 20;
-
-static hipError_t lr_workspace(float*& part) {
-  static std::mutex mu;
-  static std::map<int, float*> per_device;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> g(mu);
-  auto it = per_device.find(dev);
-  if (it != per_device.end()) {
-    part = it->second;
-    return hipSuccess;
-  }
-  e = hipMalloc(&part, LR_PART_BYTES);
-  if (e != hipSuccess) return e;
-  per_device[dev] = part;
-  return hipSuccess;
-}
-
 // Slices of K per 64-row block: enough workgroups for every compute unit to hold a few,
-// a slice of at least four chunks, and partials that fit the workspace.
-static int lr_slices(int64_t M, int64_t K, int r) {
+// a slice of at least four chunks, and (with `cap` bytes of workspace) partials that fit.
+static int lr_slices(int64_t M, int64_t K, int r, size_t cap) {
   const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
   const int64_t nch = (K + LR_KC - 1) / LR_KC;
   const int64_t want = 4 * (int64_t)device_cu_count();
   int64_t s = (want + blocks - 1) / blocks;
   s = std::min<int64_t>(s, std::max<int64_t>(1, nch / 4));
-  while (s > 1 && s * M * r * 4 > LR_PART_BYTES) --s;
+  while (s > 1 && (size_t)(s * M * r * 4) > cap) --s;
   return (int)std::max<int64_t>(s, 1);
 }
 
+size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r) {
+  const int s = lr_slices(M, K, r, ~(size_t)0);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)r * 4 : 0;
+}
+
 template <int RR>
-static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, __half* T, hipStream_t s,
-                                 int slices) {
+static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, __half* T, float* part,
+                                 hipStream_t s, int slices) {
   constexpr int NS = RR == 64 ? 2 : 3;
   const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
   const int64_t nch = (K + LR_KC - 1) / LR_KC;
   const int cps = (int)((nch + slices - 1) / slices);
-  slices = (int)((nch + cps - 1) / cps);                     // no empty slice
-  float* part = nullptr;
-  if (slices > 1) {
-    const hipError_t e = lr_workspace(part);
-    if (e != hipSuccess) return e;
-  }
+  slices = (int)((nch + cps - 1) / cps);                     // no empty slice (never more)
   hipLaunchKernelGGL((lowrank_down_kernel<RR, NS>), dim3((unsigned)(blocks * slices)), dim3(256), 0, s, X, L1,
                      (int)M, (int)K, slices, cps, part, T);
   if (slices > 1) {
@@ -205,12 +182,12 @@ static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, i
 }
 
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
-                               hipStream_t s) {
-  const int slices = lr_slices(M, K, r);
+                               float* part, size_t part_bytes, hipStream_t s) {
+  const int slices = part ? lr_slices(M, K, r, part_bytes) : 1;
   switch (r) {
-    case 16: return lowrank_launch<16>(X, L1, M, K, T, s, slices);
-    case 32: return lowrank_launch<32>(X, L1, M, K, T, s, slices);
-    case 64: return lowrank_launch<64>(X, L1, M, K, T, s, slices);
+    case 16: return lowrank_launch<16>(X, L1, M, K, T, part, s, slices);
+    case 32: return lowrank_launch<32>(X, L1, M, K, T, part, s, slices);
+    case 64: return lowrank_launch<64>(X, L1, M, K, T, part, s, slices);
     default: return hipErrorInvalidValue;
   }
 }
