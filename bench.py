@@ -133,6 +133,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="activation buffer sets (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the transform-variant timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -228,6 +229,33 @@ def main():
         per[li][k] += t / args.steps
     dur = [[p[1], p[0], p[2]] for p in per]
 
+    # ---- transform variants beside the path (not part of the step): the Kronecker factors
+    # and a dense 32x32 P on the same streaming matrix-core kernel, MXFP4 without centring,
+    # at the step's widths; event pair around back-to-back launches over the rotated inputs
+    variants = []
+    if not args.no_variants:
+        for K in widths:
+            A, B = synth.kron_factors(CFG, 0)
+            P = torch.from_numpy(synth.dense_block(CFG, 0)).to(dev)
+            codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+            for name, xf in (("kron_4x8", kq.Xform.kron(A, B, K)), ("dense_32", kq.Xform.dense(P, K))):
+                def run(i, xf=xf, K=K):
+                    kq.transform_quantize(Xsets[i % R][K], xf, fmt="mxfp4", codes=codes, scales=scales)
+                run(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 20
+                a.record()
+                for i in range(n):
+                    run(i + 1)
+                b.record()
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / n
+                tb = transform_bytes(M, K, False)
+                variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
+                                 "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
+                log(f"variant {name:>8} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
+
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference
         # dispatch for scaling the HBM byte counters
@@ -305,6 +333,7 @@ def main():
         "per_layer": per_layer,
         "context": "KroQuant page: its quantization kernel up to 14% faster than SmoothQuant's on an MI350 "
                    "(relative only, other chip)",
+        "transform_variants": variants,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 2
+#define KQ_ABI_VERSION 3
 
 typedef int32_t kq_status;
 enum {
@@ -68,7 +68,7 @@ enum {
 };
 
 /* transform kinds */
-enum { KQ_XFORM_NONE = 0, KQ_XFORM_KRON_4X8 = 1, KQ_XFORM_RPBH_32 = 2 };
+enum { KQ_XFORM_NONE = 0, KQ_XFORM_KRON_4X8 = 1, KQ_XFORM_RPBH_32 = 2, KQ_XFORM_DENSE_32 = 3 };
 /* formats */
 enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
 
@@ -82,6 +82,11 @@ enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
  *   perm (int32 [K], a permutation of 0..K-1) and sign (int8 [K]) are device arrays,
  *   16- and 4-byte aligned.  perm is not checked on the device: an entry outside
  *   0..K-1 gives unspecified codes for that call (the on-chip gather cannot fault).
+ * DENSE_32 (KroQuant §01, the block transform P before its Kronecker factorization):
+ *   every 32-element block x_b is replaced by x_b . P, P a dense invertible 32x32 matrix
+ *   (P: device float32 [32][32], row-major, 16-byte aligned; one P shared by all blocks).
+ *   MXFP4 without centring only; the fold inverts P on the device (a singular P gives
+ *   non-finite weights).
  * NONE: identity. */
 typedef struct kq_xform {
   int32_t kind;
@@ -91,6 +96,7 @@ typedef struct kq_xform {
   float B[64];
   const int32_t* perm;
   const int8_t* sign;
+  const float* P;            /* DENSE_32 only */
 } kq_xform;
 
 /* KQ_ABI_VERSION of the built library. */

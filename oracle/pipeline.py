@@ -13,6 +13,7 @@ full-precision branch, since (x - mu 1^T) W + mu (1^T W) = x W).
 Transform descriptors are plain dicts:
   {"kind": "kron", "A": float32 [4, 4], "B": float32 [8, 8]}
   {"kind": "rpbh", "perm": int [K], "sign": int8 [K] (+-1)}
+  {"kind": "dense", "P": float32 [32, 32]}     (y_b = x_b . P)
   {"kind": "none"}
 """
 
@@ -42,6 +43,8 @@ def apply_transform(x, xform):
         return transforms.apply_block_matrix(x, transforms.kron_block_matrix(xform["A"], xform["B"]))
     if kind == "rpbh":
         return transforms.rpbh_apply(x, xform["perm"], xform["sign"])
+    if kind == "dense":
+        return transforms.apply_block_matrix(x, np.asarray(xform["P"], dtype=np.float64))
     if kind == "none":
         return np.asarray(x, dtype=np.float64)
     raise ValueError(kind)
@@ -78,6 +81,8 @@ def inverse_fold(W_out_in, xform):
         return transforms.fold_kron(W_out_in, xform["A"], xform["B"])
     if kind == "rpbh":
         return transforms.fold_rpbh(W_out_in, xform["perm"], xform["sign"])
+    if kind == "dense":
+        return transforms.fold_dense(W_out_in, xform["P"])
     if kind == "none":
         return np.asarray(W_out_in, dtype=np.float64)
     raise ValueError(kind)

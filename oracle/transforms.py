@@ -12,6 +12,8 @@ an explicit permutation gather); it never uses a factored or butterfly form.
   then v = u . blockdiag(H32) with H32 the Sylvester Hadamard matrix, then
   y_j = v_j d_j / sqrt(32).  The 1/sqrt(32) makes R = Pi.blockdiag(H32).D/sqrt(32)
   orthogonal, as the page states R is.
+* Dense block transform (KroQuant page, §01): the same per-block product with a full
+  32x32 P, of which kron(A, B) is the factorized form.
 * Offline fold (KroQuant §01; OrbitQuant §03): W' = P^-1 W (R^-1 = R^T), so that
   (XP)(P^-1 W) = XW.
 """
@@ -72,6 +74,14 @@ def fold_kron(W_out_in, A, B):
     Wt = np.asarray(W_out_in, dtype=np.float64)
     Pinv = np.linalg.inv(kron_block_matrix(A, B))
     # W' = blockdiag(Pinv) W  <=>  W'^T = W^T . blockdiag(Pinv)^T
+    return apply_block_matrix(Wt, Pinv.T)
+
+
+def fold_dense(W_out_in, P32):
+    """W' = P^-1 W for a dense 32x32 block transform P, W given as [N][K]; returns W'^T as
+    [N][K] float64 (P^-1 from LAPACK on the dense block)."""
+    Wt = np.asarray(W_out_in, dtype=np.float64)
+    Pinv = np.linalg.inv(np.asarray(P32, dtype=np.float64).reshape(BLOCK, BLOCK))
     return apply_block_matrix(Wt, Pinv.T)
 
 

@@ -52,7 +52,7 @@ CONFIGS = {
 N_OUTLIERS = 12
 OUTLIER_SCALE = 50.0
 
-_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W = 1, 2, 3, 4
+_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE = 1, 2, 3, 4, 5
 
 
 def _rng(*key):
@@ -86,6 +86,13 @@ def kron_factors(seed, layer):
     A = _haar(rng, 4) * rng.uniform(0.5, 2.0, size=4)[None, :]
     B = _haar(rng, 8) * rng.uniform(0.5, 2.0, size=8)[None, :]
     return A.astype(np.float32), B.astype(np.float32)
+
+
+def dense_block(seed, layer):
+    """Dense 32x32 block transform P (float32), the same recipe as the Kronecker factors at
+    full size: Haar-orthogonal times column scales drawn from U[0.5, 2]."""
+    rng = _rng(seed, _TAG_DENSE, layer)
+    return (_haar(rng, 32) * rng.uniform(0.5, 2.0, size=32)[None, :]).astype(np.float32)
 
 
 def rpbh_params(K, seed, layer):

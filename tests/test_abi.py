@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 2
+    assert kq.abi_version() == 3
     for s in range(0, 7):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)

@@ -60,6 +60,43 @@ def test_fold_mxfp4_matches_oracle(kq, cfg, layer, nrows):
     _wbar_check(W16, wbar.cpu().numpy())
 
 
+def test_fold_dense_matches_oracle(kq):
+    """The fold with a dense P: P^-1 by Gauss-Jordan on the device (float64), then a float32
+    product per 32-block; the bound scales with (|w| |P^-T|)."""
+    K, N = 1152, 160
+    W16, _, _ = synth.weights(K, N, 13, 0, 0)
+    P = synth.dense_block(13, 0)
+    xf = {"kind": "dense", "P": P}
+    wc, ws, wbar = _fold(kq, W16, xf, "mxfp4")
+    wt = pipeline.inverse_fold(W16, xf)
+    inv_t = {"kind": "dense", "P": np.linalg.inv(P.astype(np.float64)).T}
+    tau = ties.gamma_tau(36, gpu_util.abs_transform(np.abs(W16.astype(np.float64)), inv_t))
+    gpu_util.assert_mx_parity(wc.cpu().numpy(), ws.cpu().numpy(), wt, tau, label="fold dense")
+    _wbar_check(W16, wbar.cpu().numpy())
+
+
+def test_w4a4_dense_block_linear(kq):
+    """The whole path with a dense P: transform + quantize, fold, low-rank branch, W4A4
+    linear; the oracle dequantizes the kernel's own packed operands."""
+    import torch
+    M, K, N, r = 300, 1152, 512, 32
+    X16 = synth.activations(M, K, 14, 2.0)
+    W16, L1, L2 = synth.weights(K, N, 14, 0, r)
+    xf = {"kind": "dense", "P": synth.dense_block(14, 0)}
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
+    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    torch.cuda.synchronize()
+    ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
+                             None, None)
+    err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+    print(f"dense-P linear rel frobenius {err:.3e}")
+    assert err <= TOL
+
+
 def test_fold_w2_matches_oracle(kq):
     c = synth.CONFIGS[2]
     _, K, N = c["layers"][0]

@@ -21,6 +21,8 @@ def _dev_xform(kq, torch, xf, K):
     if xf["kind"] == "rpbh":
         return kq.Xform.rpbh(torch.from_numpy(np.ascontiguousarray(xf["perm"], dtype=np.int32)).cuda(),
                              torch.from_numpy(np.ascontiguousarray(xf["sign"], dtype=np.int8)).cuda())
+    if xf["kind"] == "dense":
+        return kq.Xform.dense(torch.from_numpy(np.ascontiguousarray(xf["P"], dtype=np.float32)).cuda(), K)
     return kq.Xform.none(K)
 
 
@@ -67,6 +69,25 @@ def test_mxfp4_other_combinations(kq, kind, center):
     else:
         xf = {"kind": "none"}
     _mx_check(kq, X16, xf, center, f"{kind} center={center}")
+
+
+@pytest.mark.parametrize("K,rows", [(3072, 203), (1152, 150), (96, 7)])
+def test_mxfp4_dense_block_matches_oracle(kq, K, rows):
+    """A dense learned 32x32 P (KroQuant section 01's unfactored transform) on the
+    streaming matrix-core path."""
+    X16 = synth.activations(rows, K, 12, 2.0)
+    xf = {"kind": "dense", "P": synth.dense_block(12, 0)}
+    _mx_check(kq, X16, xf, False, f"dense K={K} M={rows}")
+
+
+def test_dense_block_rejects_unsupported(kq):
+    """Centring and the Lloyd-Max format are not offered with a dense P."""
+    import torch
+    X = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    P = torch.eye(32, dtype=torch.float32, device="cuda")
+    for fmt, center in (("mxfp4", True), ("lm4", False)):
+        with pytest.raises(kq.KQError):
+            kq.transform_quantize(X, kq.Xform.dense(P, 64), fmt=fmt, center=center)
 
 
 def test_edge_rows(kq):

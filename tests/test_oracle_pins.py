@@ -198,7 +198,7 @@ def test_rpbh_orthogonal_and_matches_dense():
 
 # ---------------------------------------------------------------- P5: the identity
 
-@pytest.mark.parametrize("kind", ["kron", "rpbh"])
+@pytest.mark.parametrize("kind", ["kron", "rpbh", "dense"])
 def test_invertible_transform_identity(kind):
     """(XP)(P^-1 W) = XW (KroQuant section 01; OrbitQuant section 03 W' = R^-1 W)."""
     rng = np.random.default_rng(6)
@@ -208,6 +208,8 @@ def test_invertible_transform_identity(kind):
     if kind == "kron":
         A, B = _random_factors(7)
         xf = {"kind": "kron", "A": A, "B": B}
+    elif kind == "dense":
+        xf = {"kind": "dense", "P": rng.standard_normal((32, 32)) + 4 * np.eye(32)}
     else:
         xf = {"kind": "rpbh", "perm": rng.permutation(K), "sign": rng.choice([-1, 1], K)}
     lhs = pipeline.apply_transform(X, xf) @ pipeline.inverse_fold(Wt, xf).T
@@ -226,6 +228,42 @@ def test_fold_solves_forward_transform():
         W_blk = Wt[:, 32 * b:32 * b + 32].T          # [32, N]
         sol = scipy.linalg.solve(P, W_blk)           # P^-1 W
         assert np.allclose(wpt[:, 32 * b:32 * b + 32].T, sol, rtol=1e-12, atol=1e-12)
+
+
+def test_dense_block_special_cases():
+    """The dense block transform (KroQuant section 01's P) against matrices whose action is
+    known elementwise: the identity leaves x unchanged; a permutation matrix with
+    P[pi(j), j] = 1 gathers y_j = x_{pi(j)} inside each block (the row-vector convention:
+    a transposed P would scatter instead); a diagonal P scales; the fold with a diagonal P
+    divides the weight rows by the same factors."""
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((5, 96))
+    assert np.array_equal(pipeline.apply_transform(X, {"kind": "dense", "P": np.eye(32)}), X)
+    pi = rng.permutation(32)
+    P = np.zeros((32, 32))
+    P[pi, np.arange(32)] = 1.0
+    y = pipeline.apply_transform(X, {"kind": "dense", "P": P})
+    for b in range(3):
+        assert np.array_equal(y[:, 32 * b:32 * b + 32], X[:, 32 * b + pi])
+    d = rng.uniform(0.5, 2.0, 32)
+    y = pipeline.apply_transform(X, {"kind": "dense", "P": np.diag(d)})
+    assert np.allclose(y, X * np.tile(d, 3)[None, :], rtol=0, atol=0)
+    Wt = rng.standard_normal((7, 96))
+    wpt = pipeline.inverse_fold(Wt, {"kind": "dense", "P": np.diag(d)})
+    assert np.allclose(wpt, Wt / np.tile(d, 3)[None, :], rtol=1e-15)
+
+
+def test_dense_orthogonal_preserves_block_norms():
+    """An orthogonal dense P (the synthetic recipe's Haar factor) keeps every block's norm."""
+    import synth
+    P = synth.dense_block(3, 0).astype(np.float64)
+    Q = P / np.linalg.norm(P, axis=0)[None, :]       # undo the column scales: Haar-orthogonal
+    assert np.allclose(Q.T @ Q, np.eye(32), atol=1e-6)
+    X = np.random.default_rng(22).standard_normal((4, 64))
+    y = pipeline.apply_transform(X, {"kind": "dense", "P": Q})
+    for b in range(2):
+        assert np.allclose(np.linalg.norm(y[:, 32 * b:32 * b + 32], axis=1),
+                           np.linalg.norm(X[:, 32 * b:32 * b + 32], axis=1), rtol=1e-6)
 
 
 # ---------------------------------------------------------------- P6: centring + rank-1

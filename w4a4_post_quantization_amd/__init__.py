@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 KQ_OK = 0
-XFORM_NONE, XFORM_KRON, XFORM_RPBH = 0, 1, 2
+XFORM_NONE, XFORM_KRON, XFORM_RPBH, XFORM_DENSE = 0, 1, 2, 3
 FMT_MXFP4, FMT_LM4, FMT_LM2 = 0, 1, 2
 _FMT = {"mxfp4": FMT_MXFP4, "lm4": FMT_LM4, "lm2": FMT_LM2}
 
@@ -37,7 +37,7 @@ class KQError(RuntimeError):
 class _XformC(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("K", ctypes.c_int64),
                 ("A", ctypes.c_float * 16), ("B", ctypes.c_float * 64),
-                ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p)]
+                ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p), ("P", ctypes.c_void_p)]
 
 
 def lib_path():
@@ -124,9 +124,9 @@ def _check(t, name, dtype, shape=None):
 
 
 class Xform:
-    """One layer's block transform descriptor (KRON_4X8, RPBH_32 or NONE)."""
+    """One layer's block transform descriptor (KRON_4X8, RPBH_32, DENSE_32 or NONE)."""
 
-    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None):
+    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None, P=None):
         self.kind, self.K = kind, int(K)
         self._c = _XformC()
         self._c.kind, self._c.reserved, self._c.K = kind, 0, self.K
@@ -143,10 +143,20 @@ class Xform:
             _check(perm, "perm", torch.int32, (self.K,))
             _check(sign, "sign", torch.int8, (self.K,))
             self._c.perm, self._c.sign = perm.data_ptr(), sign.data_ptr()
+        self.P = P
+        if kind == XFORM_DENSE:
+            torch = _torch()
+            _check(P, "P", torch.float32, (32, 32))
+            self._c.P = P.data_ptr()
 
     @classmethod
     def kron(cls, A, B, K):
         return cls(XFORM_KRON, K, A=A, B=B)
+
+    @classmethod
+    def dense(cls, P, K):
+        """P: float32 [32][32] device tensor, y_b = x_b . P for every block."""
+        return cls(XFORM_DENSE, K, P=P)
 
     @classmethod
     def rpbh(cls, perm, sign):

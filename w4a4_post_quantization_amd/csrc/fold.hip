@@ -9,14 +9,61 @@ namespace kq {
 
 #define KQ_INV_SQRT32_F 0.17677669529663688110f
 
+// P^-1 of a dense 32x32 P (row-major, global) into LDS as float: Gauss-Jordan elimination
+// with partial pivoting in float64 by the whole workgroup (offline: clarity over speed).
+// A singular P gives non-finite entries.
+__device__ void invert32(const float* __restrict__ P, float* __restrict__ pinv) {
+  __shared__ double aug[32][64];
+  __shared__ double fac[32];
+  __shared__ int piv;
+  const int t = threadIdx.x, T = blockDim.x;
+  for (int e = t; e < 32 * 64; e += T) {
+    const int i = e >> 6, j = e & 63;
+    aug[i][j] = j < 32 ? (double)P[32 * i + j] : (j - 32 == i ? 1.0 : 0.0);
+  }
+  __syncthreads();
+  for (int c = 0; c < 32; ++c) {
+    if (t == 0) {
+      int p = c;
+      for (int i = c + 1; i < 32; ++i)
+        if (fabs(aug[i][c]) > fabs(aug[p][c])) p = i;
+      piv = p;
+    }
+    __syncthreads();
+    if (piv != c && t < 64) {
+      const double a = aug[c][t];
+      aug[c][t] = aug[piv][t];
+      aug[piv][t] = a;
+    }
+    __syncthreads();
+    const double d = aug[c][c];
+    __syncthreads();
+    if (t < 64) aug[c][t] /= d;
+    __syncthreads();
+    if (t < 32) fac[t] = t == c ? 0.0 : aug[t][c];
+    __syncthreads();
+    for (int e = t; e < 32 * 64; e += T) {
+      const int i = e >> 6, j = e & 63;
+      aug[i][j] -= fac[i] * aug[c][j];
+    }
+    __syncthreads();
+  }
+  for (int e = t; e < 32 * 32; e += T) pinv[e] = (float)aug[e >> 5][32 + (e & 31)];
+  __syncthreads();
+}
+
 // One thread: row n of W^T (= column n of W), block b (32 consecutive k).
 // KIND 1: w'_b = (Ai (x) Bi) w_b, i.e. W'm = Ai Wm Bi^T with Wm[k][l] = w_b[8k+l].
 // KIND 2: w' = w R (the forward RPBH of the row, since W'^T = W^T R).
+// KIND 3: w'_b = P^-1 w_b for a dense block transform P.
 // FMT 0: MXFP4 (16 code bytes + 1 E8M0 byte); FMT 2: 2-bit Lloyd-Max + fp16 group scale.
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, KronFactors fi,
                                                    const int32_t* __restrict__ perm, const int8_t* __restrict__ sign,
-                                                   float t4, uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
+                                                   const float* __restrict__ P, float t4, uint8_t* __restrict__ wcodes,
+                                                   void* __restrict__ wscales) {
+  __shared__ float pinv[KIND == 3 ? 32 * 32 : 1];
+  if (KIND == 3) invert32(P, pinv);         // every thread of the workgroup takes part
   const int64_t nb = K >> 5;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= N * nb) return;
@@ -48,6 +95,14 @@ __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W,
         for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(fi.A[4 * i + k], z[8 * k + j], acc);
         y[8 * i + j] = acc;
       }
+  } else if (KIND == 3) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) acc = __builtin_fmaf(pinv[32 * i + j], w[j], acc);
+      y[i] = acc;
+    }
   } else if (KIND == 2) {
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1)
@@ -112,19 +167,22 @@ __global__ __launch_bounds__(256) void colsum_kernel(const __half* __restrict__ 
 
 template <int KIND>
 static void fold_fmt(int fmt, dim3 g, dim3 b, hipStream_t s, const __half* W, int64_t N, int64_t K,
-                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, float t4, uint8_t* wc, void* ws) {
-  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, t4, wc, ws);
-  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, t4, wc, ws);
+                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, const float* P, float t4,
+                     uint8_t* wc, void* ws) {
+  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, P, t4, wc, ws);
+  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, P, t4, wc, ws);
 }
 
 hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
-                       const int32_t* perm, const int8_t* sign, uint8_t* wcodes, void* wscales, hipStream_t s) {
+                       const int32_t* perm, const int8_t* sign, const float* P, uint8_t* wcodes, void* wscales,
+                       hipStream_t s) {
   const int64_t total = N * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const float t4 = lm_tables().t4;
-  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
-  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
-  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, t4, wcodes, wscales);
+  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
+  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
+  else if (kind == 3) fold_fmt<3>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
+  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
   return hipGetLastError();
 }
 

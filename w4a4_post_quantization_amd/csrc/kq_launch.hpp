@@ -27,10 +27,11 @@ bool lloyd_max_levels(int n, double* out);
 hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFactors& f,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s);
 
-// Matrix-core block transforms + MXFP4: streaming Kronecker (or identity) without centring,
-// and row-staged RPBH with optional centring.
-hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, const KronFactors& f, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s);
+// Matrix-core block transforms + MXFP4: streaming identity (kind 0), Kronecker (1) or
+// dense 32x32 P (3, device, row-major) without centring, and row-staged RPBH with
+// optional centring.
+hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
+                               uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s);
 
@@ -42,8 +43,9 @@ hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int
 
 // Offline fold: W'^T rows = inverse transform of W^T rows, quantized along K.
 // fmt: 0 MXFP4, 2 LM2.  f holds the INVERSE factors for kind 1.
+// kind 3: P (device, row-major) is inverted on the device.
 hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
-                       const int32_t* perm, const int8_t* sign, uint8_t* wcodes, void* wscales,
+                       const int32_t* perm, const int8_t* sign, const float* P, uint8_t* wcodes, void* wscales,
                        hipStream_t s);
 hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
 

@@ -343,6 +343,24 @@ __device__ __forceinline__ MfmaXform mfma_xform_kron(const KronFactors& f, int l
   return x;
 }
 
+// The same fragments for a dense 32x32 P (row-major in device memory): P^T rows j, columns k.
+__device__ __forceinline__ MfmaXform mfma_xform_dense(const float* __restrict__ P, int lane) {
+  MfmaXform x;
+  const int q = lane >> 4, jl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = 16 * t + jl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = P[32 * (8 * q + i) + j];   // P[k][j], k = 8q + i
+      const _Float16 hi = (_Float16)p;
+      x.a[t][0][i] = hi;
+      x.a[t][1][i] = (_Float16)(p - (float)hi);
+    }
+  }
+  return x;
+}
+
 __device__ __forceinline__ MfmaXform mfma_xform_hadamard(int lane) {
   MfmaXform x;
   const int q = lane >> 4, jl = lane & 15;
@@ -407,14 +425,19 @@ __device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& d
 // Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
 // flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
 // one 16-byte load per lane and writes 256 contiguous code bytes.
-template <int U, bool KRON>
+// KIND: 0 identity, 1 Kronecker A (x) B, 3 dense P (both through the hi + lo split).
+template <int U, int KIND>
 __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* __restrict__ X, int64_t nblocks,
-                                                                  KronFactors f, uint8_t* __restrict__ codes,
+                                                                  KronFactors f, const float* __restrict__ P,
+                                                                  uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales) {
+  constexpr bool KRON = KIND != 0;        // a general matrix: hi + lo products
   const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15;
   MfmaXform xf;
-  if (KRON) {
+  if (KIND == 1) {
     xf = mfma_xform_kron(f, lane);
+  } else if (KIND == 3) {
+    xf = mfma_xform_dense(P, lane);
   } else {   // identity: P^T rows are unit vectors
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -715,8 +738,8 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
   }
 }
 
-hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, const KronFactors& f, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s) {
+hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
+                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
   constexpr int U = 4;
   const int64_t nchunks = (nblocks + 15) / 16;
   const int64_t waves = (nchunks + U - 1) / U;
@@ -724,12 +747,16 @@ hipError_t launch_kron_mx_mfma(bool kron, const __half* X, int64_t nblocks, cons
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  if (kron)
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, true>), dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(X), nblocks, f, codes, scales);
+  const uint4* Xv = reinterpret_cast<const uint4*>(X);
+  if (kind == 1)
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 1>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
+                       codes, scales);
+  else if (kind == 3)
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 3>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
+                       codes, scales);
   else
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, false>), dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(X), nblocks, f, codes, scales);
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 0>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
+                       codes, scales);
   return hipGetLastError();
 }
 
