@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 3
+#define KQ_ABI_VERSION 4
 
 typedef int32_t kq_status;
 enum {
@@ -87,7 +87,14 @@ enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
  *   (P: device float32 [32][32], row-major, 16-byte aligned; one P shared by all blocks).
  *   MXFP4 without centring only; the fold inverts P on the device (a singular P gives
  *   non-finite weights).
- * NONE: identity. */
+ * NONE: identity.
+ * pts (optional, any kind but RPBH_32; DMQ explainer, channel-wise power-of-two scaling):
+ *   device int8 [K], 16-byte aligned, entries e_k in 0..15.  The activation path first
+ *   replaces x_k by fp16(x_k 2^-e_k) (round-to-nearest-even; exact unless the result is
+ *   subnormal), then transforms; the fold multiplies weight input channel k by 2^e_k
+ *   (exact) before the inverse transform, so the product is unchanged.  MXFP4 without
+ *   centring only.  Entries are not checked on the device: one outside 0..15 gives
+ *   unspecified codes for that call.  NULL: no scaling. */
 typedef struct kq_xform {
   int32_t kind;
   int32_t reserved;          /* must be 0 */
@@ -97,6 +104,7 @@ typedef struct kq_xform {
   const int32_t* perm;
   const int8_t* sign;
   const float* P;            /* DENSE_32 only */
+  const int8_t* pts;         /* NULL or per-channel power-of-two exponents */
 } kq_xform;
 
 /* KQ_ABI_VERSION of the built library. */

@@ -15,6 +15,9 @@ Transform descriptors are plain dicts:
   {"kind": "rpbh", "perm": int [K], "sign": int8 [K] (+-1)}
   {"kind": "dense", "P": float32 [32, 32]}     (y_b = x_b . P)
   {"kind": "none"}
+Any of them except "rpbh" may carry "pts": int [K] of power-of-two exponents (DMQ
+explainer, channel-wise power-of-two scaling): the activation path first replaces
+x_k by fp16(x_k 2^-e_k), and the fold scales weight input channel k by 2^e_k.
 """
 
 import numpy as np
@@ -35,6 +38,15 @@ def token_mean_f16(x):
 def centre(x, mu_f16):
     """x - mu (float64, exact for fp16 inputs)."""
     return np.asarray(x, dtype=np.float64) - np.asarray(mu_f16, dtype=np.float64)[:, None]
+
+
+def apply_pts(x, pts):
+    """Channel-wise power-of-two scaling of the activations (DMQ explainer, PTS): channel
+    k is divided by 2^pts[k].  The pages call it a bit shift of 16-bit values, so the
+    result stays fp16: the scaling is exact unless it lands below the fp16 normal range,
+    where numpy's float64 -> float16 conversion rounds to nearest even."""
+    e = np.asarray(pts, dtype=np.int64)
+    return np.ldexp(np.asarray(x, dtype=np.float64), -e[None, :]).astype(np.float16).astype(np.float64)
 
 
 def apply_transform(x, xform):
@@ -60,6 +72,10 @@ def transform_quantize(X_f16, xform, fmt="mxfp4", center=False, mu_f16=None):
     """
     x = np.asarray(X_f16, dtype=np.float64)
     mu = None
+    if xform.get("pts") is not None:
+        if center or xform["kind"] == "rpbh":
+            raise ValueError("power-of-two channel scaling is defined here without centring or RPBH")
+        x = apply_pts(x, xform["pts"])
     if center:
         mu = token_mean_f16(x) if mu_f16 is None else np.asarray(mu_f16, dtype=np.float16)
         x = centre(x, mu)
@@ -75,8 +91,14 @@ def transform_quantize(X_f16, xform, fmt="mxfp4", center=False, mu_f16=None):
 
 
 def inverse_fold(W_out_in, xform):
-    """W'^T = (P^-1 W)^T as [N][K] float64, for W given as [N][K] (row n = column n of W)."""
+    """W'^T = (P^-1 D W)^T as [N][K] float64, for W given as [N][K] (row n = column n of W);
+    D = diag(2^pts) when the descriptor carries power-of-two exponents, else the identity."""
     kind = xform["kind"]
+    if xform.get("pts") is not None:
+        if kind == "rpbh":
+            raise ValueError("power-of-two channel scaling is defined here without RPBH")
+        e = np.asarray(xform["pts"], dtype=np.int64)
+        W_out_in = np.ldexp(np.asarray(W_out_in, dtype=np.float64), e[None, :])
     if kind == "kron":
         return transforms.fold_kron(W_out_in, xform["A"], xform["B"])
     if kind == "rpbh":

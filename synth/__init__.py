@@ -16,6 +16,9 @@ SANA, FLUX.1 and CogVideoX, which are not available):
   orthogonal (QR of a Gaussian matrix with the sign of R's diagonal folded in) and
   u ~ U[0.5, 2]; one pair per layer; float32;
 * RPBH parameters: a uniform random permutation of K and uniform random +-1 signs;
+* power-of-two channel exponents: round(log2(outlier scale)) = 6 on the planted
+  outlier channels of the activations and 0 elsewhere (the channels the scaling is
+  meant for), or, to exercise every exponent, uniform integers in 0..15;
 * weights W ~ N(0, 1/K), low-rank factors L1 ~ N(0, 1/K), L2 ~ N(0, 1/K), fp16,
   in the [out][in] layout: W as [N][K], L1 as [r][K], L2 as [N][r].
 
@@ -52,19 +55,24 @@ CONFIGS = {
 N_OUTLIERS = 12
 OUTLIER_SCALE = 50.0
 
-_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE = 1, 2, 3, 4, 5
+_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE, _TAG_PTS = 1, 2, 3, 4, 5, 6
 
 
 def _rng(*key):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
 
 
-def activations(M, K, seed, sigma_mu=2.0, frames=None, n_outliers=N_OUTLIERS, outlier_scale=OUTLIER_SCALE):
-    """fp16 [M, K] activations (see module docstring)."""
+def _activation_draws(M, K, seed, sigma_mu, n_outliers):
     rng = _rng(seed, _TAG_ACT, M, K)
     mu_tok = rng.normal(0.0, sigma_mu, size=M)
     z = rng.standard_normal((M, K), dtype=np.float64)
     cols = rng.choice(K, size=min(n_outliers, K), replace=False)
+    return rng, mu_tok, z, cols
+
+
+def activations(M, K, seed, sigma_mu=2.0, frames=None, n_outliers=N_OUTLIERS, outlier_scale=OUTLIER_SCALE):
+    """fp16 [M, K] activations (see module docstring)."""
+    rng, mu_tok, z, cols = _activation_draws(M, K, seed, sigma_mu, n_outliers)
     z[:, cols] *= outlier_scale
     z += mu_tok[:, None]
     if frames:
@@ -72,6 +80,23 @@ def activations(M, K, seed, sigma_mu=2.0, frames=None, n_outliers=N_OUTLIERS, ou
         per = -(-M // frames)
         z += np.repeat(drift, per)[:M, None]
     return z.astype(np.float16)
+
+
+def outlier_channels(M, K, seed, sigma_mu=2.0, n_outliers=N_OUTLIERS):
+    """The channels that activations(M, K, seed, ...) scaled up (sorted int array)."""
+    return np.sort(_activation_draws(M, K, seed, sigma_mu, n_outliers)[3])
+
+
+def pts_exponents(K, channels=None, shift=None, seed=None):
+    """int8 [K] power-of-two exponents.  With `channels`: `shift` (default
+    round(log2(OUTLIER_SCALE))) on those channels, 0 elsewhere.  With `seed` instead:
+    uniform integers in 0..15 on every channel."""
+    if seed is not None:
+        return _rng(seed, _TAG_PTS, K).integers(0, 16, size=K).astype(np.int8)
+    e = np.zeros(K, dtype=np.int8)
+    if channels is not None:
+        e[np.asarray(channels)] = int(round(np.log2(OUTLIER_SCALE))) if shift is None else int(shift)
+    return e
 
 
 def _haar(rng, n):

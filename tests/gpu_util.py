@@ -67,6 +67,8 @@ def oracle_activation_reference(X16, xform, center, mu_gpu=None, fmt="mxfp4"):
         xc = pipeline.centre(X, mu)
     else:
         xc = X
+    if xform.get("pts") is not None:
+        xc = pipeline.apply_pts(xc, xform["pts"])      # fp16 values: the kernel's own inputs
     y = pipeline.apply_transform(xc, xform)
     return y, tau_for(xc, xform, center, fmt, x_raw=X, mu=mu), mu
 

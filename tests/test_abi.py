@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 3
+    assert kq.abi_version() == 4
     for s in range(0, 7):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
@@ -91,6 +91,23 @@ def test_transform_quantize_validation(lib):
     big = _xf(kind=2, K=65536 + 32)
     big.perm, big.sign = 0x100000, 0x100000
     assert f(ctypes.byref(big), 0, 0, FAKE, 4, 65536 + 32, FAKE, FAKE, None, None) == 4  # row too long
+
+
+def test_pts_validation(lib):
+    """Power-of-two channel scaling: streaming path only (MXFP4, no centring, not RPBH),
+    a 16-byte aligned exponent vector."""
+    f, g = lib.kq_transform_quantize, lib.kq_fold_inverse_into_weights
+    xf = _xf()
+    xf.pts = 0x100008
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 3          # misaligned pts
+    assert g(ctypes.byref(xf), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 3
+    xf.pts = 0x100000
+    assert f(ctypes.byref(xf), 0, 1, FAKE, 4, 64, FAKE, FAKE, FAKE, None) == 4          # with centring
+    assert f(ctypes.byref(xf), 1, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with LM4
+    rp = _xf(kind=2)
+    rp.perm, rp.sign, rp.pts = 0x100000, 0x100000, 0x100000
+    assert f(ctypes.byref(rp), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with RPBH
+    assert g(ctypes.byref(rp), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 4
 
 
 def test_fold_validation(lib):

@@ -97,6 +97,66 @@ def test_w4a4_dense_block_linear(kq):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("kind", ["kron", "dense", "none"])
+def test_fold_pts_matches_oracle(kq, kind):
+    """The fold with power-of-two channel exponents: W scaled by 2^e along its input channel
+    (exact), then P^-1; wbar stays the sum of the unscaled weights."""
+    K, N = 1152, 160
+    W16, _, _ = synth.weights(K, N, 15, 0, 0)
+    xf = {"kind": kind, "pts": synth.pts_exponents(K, seed=15)}
+    if kind == "kron":
+        xf["A"], xf["B"] = synth.kron_factors(15, 0)
+        inv_t = {"kind": "kron", "A": np.linalg.inv(xf["A"].astype(np.float64)).T,
+                 "B": np.linalg.inv(xf["B"].astype(np.float64)).T}
+        n = 13
+    elif kind == "dense":
+        xf["P"] = synth.dense_block(15, 0)
+        inv_t = {"kind": "dense", "P": np.linalg.inv(xf["P"].astype(np.float64)).T}
+        n = 36
+    else:
+        inv_t, n = {"kind": "none"}, 2
+    wc, ws, wbar = _fold(kq, W16, xf, "mxfp4")
+    wt = pipeline.inverse_fold(W16, xf)
+    wd = np.ldexp(np.abs(W16.astype(np.float64)), xf["pts"].astype(np.int64)[None, :])
+    tau = ties.gamma_tau(n, gpu_util.abs_transform(wd, inv_t))
+    gpu_util.assert_mx_parity(wc.cpu().numpy(), ws.cpu().numpy(), wt, tau, label=f"fold pts {kind}")
+    _wbar_check(W16, wbar.cpu().numpy())
+
+
+@pytest.mark.parametrize("kind", ["kron", "dense"])
+def test_w4a4_pts_linear(kq, kind):
+    """The whole path with power-of-two scaling on the outlier channels: the linear of the
+    kernel's packed operands against the oracle, and the quantized product against the
+    exact X W.  The scaling cancels between the two sides, so the 4-bit error stays of
+    order one (the oracle's own figure on these inputs is 0.64 for Kronecker and 0.39 for
+    dense P: the weights of the scaled channels grow by 2^6); a shift applied the wrong
+    way on either side would give errors of order 2^12."""
+    import torch
+    M, K, N, r = 260, 3072, 384, 32
+    X16 = synth.activations(M, K, 16, 2.0)
+    W16, L1, L2 = synth.weights(K, N, 16, 0, r)
+    xf = {"kind": kind, "pts": synth.pts_exponents(K, synth.outlier_channels(M, K, 16, 2.0))}
+    if kind == "kron":
+        xf["A"], xf["B"] = synth.kron_factors(16, 0)
+    else:
+        xf["P"] = synth.dense_block(16, 0)
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
+    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    torch.cuda.synchronize()
+    ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
+                             None, None)
+    err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+    exact = X16.astype(np.float64) @ W16.astype(np.float64).T + linear.lowrank_term(X16, L1, L2)
+    qerr = linear.rel_frobenius(Y.cpu().numpy(), exact)
+    print(f"pts {kind} linear rel frobenius {err:.3e}; against exact X W {qerr:.3e}")
+    assert err <= TOL
+    assert qerr < 1.0
+
+
 def test_fold_w2_matches_oracle(kq):
     c = synth.CONFIGS[2]
     _, K, N = c["layers"][0]

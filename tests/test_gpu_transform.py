@@ -17,13 +17,17 @@ pytestmark = pytest.mark.gpu
 
 def _dev_xform(kq, torch, xf, K):
     if xf["kind"] == "kron":
-        return kq.Xform.kron(xf["A"], xf["B"], K)
-    if xf["kind"] == "rpbh":
-        return kq.Xform.rpbh(torch.from_numpy(np.ascontiguousarray(xf["perm"], dtype=np.int32)).cuda(),
-                             torch.from_numpy(np.ascontiguousarray(xf["sign"], dtype=np.int8)).cuda())
-    if xf["kind"] == "dense":
-        return kq.Xform.dense(torch.from_numpy(np.ascontiguousarray(xf["P"], dtype=np.float32)).cuda(), K)
-    return kq.Xform.none(K)
+        d = kq.Xform.kron(xf["A"], xf["B"], K)
+    elif xf["kind"] == "rpbh":
+        d = kq.Xform.rpbh(torch.from_numpy(np.ascontiguousarray(xf["perm"], dtype=np.int32)).cuda(),
+                          torch.from_numpy(np.ascontiguousarray(xf["sign"], dtype=np.int8)).cuda())
+    elif xf["kind"] == "dense":
+        d = kq.Xform.dense(torch.from_numpy(np.ascontiguousarray(xf["P"], dtype=np.float32)).cuda(), K)
+    else:
+        d = kq.Xform.none(K)
+    if xf.get("pts") is not None:
+        d = d.with_pts(torch.from_numpy(np.ascontiguousarray(xf["pts"], dtype=np.int8)).cuda())
+    return d
 
 
 def _run(kq, X16, xf, fmt, center):
@@ -88,6 +92,38 @@ def test_dense_block_rejects_unsupported(kq):
     for fmt, center in (("mxfp4", True), ("lm4", False)):
         with pytest.raises(kq.KQError):
             kq.transform_quantize(X, kq.Xform.dense(P, 64), fmt=fmt, center=center)
+
+
+@pytest.mark.parametrize("kind", ["kron", "dense", "none"])
+@pytest.mark.parametrize("K,rows,which", [(3072, 203, "outliers"), (1152, 150, "random"), (96, 7, "random"),
+                                          (12288, 37, "outliers")])
+def test_mxfp4_pts_matches_oracle(kq, kind, K, rows, which):
+    """DMQ's power-of-two channel scaling ahead of the block transform: exponents 6 on the
+    planted outlier channels, or uniform 0..15 on every channel (many fp16 subnormal
+    results, rounded to nearest even on both sides)."""
+    X16 = synth.activations(rows, K, 13, 2.0)
+    pts = synth.pts_exponents(K, synth.outlier_channels(rows, K, 13, 2.0)) if which == "outliers" \
+        else synth.pts_exponents(K, seed=K)
+    xf = {"kind": kind, "pts": pts}
+    if kind == "kron":
+        xf["A"], xf["B"] = synth.kron_factors(13, 0)
+    if kind == "dense":
+        xf["P"] = synth.dense_block(13, 0)
+    _mx_check(kq, X16, xf, False, f"pts {which} {kind} K={K} M={rows}")
+
+
+def test_pts_rejects_unsupported(kq):
+    """Power-of-two scaling is offered on the streaming MXFP4 path only."""
+    import torch
+    X = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    e = torch.zeros(64, dtype=torch.int8, device="cuda")
+    for fmt, center in (("mxfp4", True), ("lm4", False)):
+        with pytest.raises(kq.KQError):
+            kq.transform_quantize(X, kq.Xform.none(64).with_pts(e), fmt=fmt, center=center)
+    perm = torch.arange(64, dtype=torch.int32, device="cuda")
+    sign = torch.ones(64, dtype=torch.int8, device="cuda")
+    with pytest.raises(kq.KQError):
+        kq.transform_quantize(X, kq.Xform.rpbh(perm, sign).with_pts(e))
 
 
 def test_edge_rows(kq):

@@ -266,6 +266,72 @@ def test_dense_orthogonal_preserves_block_norms():
                            np.linalg.norm(X[:, 32 * b:32 * b + 32], axis=1), rtol=1e-6)
 
 
+# ---------------------------------------------------------------- power-of-two channel scaling
+
+def test_pts_fp16_shift_values():
+    """DMQ's power-of-two scaling of fp16 activations against IEEE binary16 facts: in the
+    normal range a power-of-two divide only lowers the exponent (exact); 2^-14 / 2 is the
+    subnormal 2^-15; below the normal range the spacing is 2^-24, so 3 * 2^-24 / 2 = 1.5
+    ulp rounds to the even 2 * 2^-24, 5 * 2^-24 / 2 = 2.5 ulp to 2 * 2^-24 and 7 * 2^-24 / 4
+    = 1.75 ulp to 2 * 2^-24; 2^-24 / 4 rounds to zero; signs are kept."""
+    x = np.array([[48.0, -2.0 ** -14, 3 * 2.0 ** -24, 5 * 2.0 ** -24, 7 * 2.0 ** -24, -(2.0 ** -24), 65504.0, 1.0]])
+    e = np.array([5, 1, 1, 1, 2, 2, 15, 0])
+    want = np.array([[1.5, -(2.0 ** -15), 2 * 2.0 ** -24, 2 * 2.0 ** -24, 2 * 2.0 ** -24, -0.0, 65504.0 / 32768, 1.0]])
+    got = pipeline.apply_pts(x, e)
+    assert np.array_equal(got, want)
+    assert np.signbit(got[0, 5])
+
+
+def test_pts_constant_shift_moves_only_the_mx_scale():
+    """With the same exponent c on every channel, MXFP4 (a power-of-two shared scale per
+    block) must give the same codes and every scale byte lowered by c, as long as the
+    scaled values stay normal: a check that the scaling divides (not multiplies) and is a
+    power of two."""
+    rng = np.random.default_rng(30)
+    X = (rng.standard_normal((6, 128)) * 8).astype(np.float16)
+    X[np.abs(X.astype(np.float64)) < 2.0 ** -6] = np.float16(0.25)
+    for c in (1, 3, 7):
+        ref = pipeline.transform_quantize(X, {"kind": "none"})
+        got = pipeline.transform_quantize(X, {"kind": "none", "pts": np.full(128, c)})
+        assert np.array_equal(got["codes"], ref["codes"])
+        assert np.array_equal(got["scales"].astype(int), ref["scales"].astype(int) - c)
+
+
+@pytest.mark.parametrize("kind", ["none", "kron", "dense"])
+def test_pts_fold_restores_the_product(kind):
+    """(X D^-1 P)(P^-1 D W) = X W for activations whose scaled values stay fp16-normal
+    (exact shift): checks the direction of the shift on both sides and that both index the
+    input channel k (scaling the output channel instead breaks the product)."""
+    import synth
+    rng = np.random.default_rng(31)
+    K, N = 96, 40
+    X = (rng.standard_normal((5, K)) * 4).astype(np.float16)
+    X[np.abs(X.astype(np.float64)) < 2.0 ** -4] = np.float16(0.5)
+    Wt = rng.standard_normal((N, K))
+    xf = {"kind": kind}
+    if kind == "kron":
+        A, B = synth.kron_factors(0, 0)
+        xf.update(A=A, B=B)
+    if kind == "dense":
+        xf["P"] = synth.dense_block(0, 0)
+    xf["pts"] = rng.integers(0, 9, size=K)
+    y = pipeline.apply_transform(pipeline.apply_pts(X, xf["pts"]), xf)
+    wt = pipeline.inverse_fold(Wt, xf)
+    assert np.allclose(y @ wt.T, X.astype(np.float64) @ Wt.T, rtol=1e-9, atol=1e-9)
+    wrong = dict(xf, pts=xf["pts"][::-1].copy())
+    assert not np.allclose(y @ pipeline.inverse_fold(Wt, wrong).T, X.astype(np.float64) @ Wt.T, rtol=1e-3)
+
+
+def test_pts_zero_exponents_change_nothing():
+    rng = np.random.default_rng(32)
+    X = (rng.standard_normal((4, 64)) * 3).astype(np.float16)
+    a = pipeline.transform_quantize(X, {"kind": "none"})
+    b = pipeline.transform_quantize(X, {"kind": "none", "pts": np.zeros(64, dtype=np.int8)})
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+    with pytest.raises(ValueError):
+        pipeline.transform_quantize(X, {"kind": "none", "pts": np.zeros(64)}, center=True)
+
+
 # ---------------------------------------------------------------- P6: centring + rank-1
 
 def test_centring_restore_exact():

@@ -37,7 +37,8 @@ class KQError(RuntimeError):
 class _XformC(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("K", ctypes.c_int64),
                 ("A", ctypes.c_float * 16), ("B", ctypes.c_float * 64),
-                ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p), ("P", ctypes.c_void_p)]
+                ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p), ("P", ctypes.c_void_p),
+                ("pts", ctypes.c_void_p)]
 
 
 def lib_path():
@@ -126,7 +127,7 @@ def _check(t, name, dtype, shape=None):
 class Xform:
     """One layer's block transform descriptor (KRON_4X8, RPBH_32, DENSE_32 or NONE)."""
 
-    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None, P=None):
+    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None, P=None, pts=None):
         self.kind, self.K = kind, int(K)
         self._c = _XformC()
         self._c.kind, self._c.reserved, self._c.K = kind, 0, self.K
@@ -148,6 +149,16 @@ class Xform:
             torch = _torch()
             _check(P, "P", torch.float32, (32, 32))
             self._c.P = P.data_ptr()
+        self.pts = pts
+        if pts is not None:
+            _check(pts, "pts", _torch().int8, (self.K,))
+            self._c.pts = pts.data_ptr()
+
+    def with_pts(self, pts):
+        """The same transform preceded by power-of-two channel scaling: pts is an int8 [K]
+        device tensor of exponents (0..15); x_k -> fp16(x_k 2^-pts[k]), weights x 2^pts[k]."""
+        return Xform(self.kind, self.K, A=list(self._c.A), B=list(self._c.B), perm=self.perm, sign=self.sign,
+                     P=self.P, pts=pts)
 
     @classmethod
     def kron(cls, A, B, K):

@@ -60,8 +60,8 @@ __device__ void invert32(const float* __restrict__ P, float* __restrict__ pinv) 
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, KronFactors fi,
                                                    const int32_t* __restrict__ perm, const int8_t* __restrict__ sign,
-                                                   const float* __restrict__ P, float t4, uint8_t* __restrict__ wcodes,
-                                                   void* __restrict__ wscales) {
+                                                   const float* __restrict__ P, const int8_t* __restrict__ pts,
+                                                   float t4, uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
   __shared__ float pinv[KIND == 3 ? 32 * 32 : 1];
   if (KIND == 3) invert32(P, pinv);         // every thread of the workgroup takes part
   const int64_t nb = K >> 5;
@@ -73,7 +73,9 @@ __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W,
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int64_t k = 32 * b + i;
-    w[i] = __half2float(wr[KIND == 2 ? (int64_t)perm[k] : k]);
+    const int64_t src = KIND == 2 ? (int64_t)perm[k] : k;
+    w[i] = __half2float(wr[src]);
+    if (pts) w[i] = ldexpf(w[i], (int)pts[src]);   // W' = P^-1 D W with D = diag(2^pts), exact
   }
   if (KIND == 1) {
     float z[32];  // Z = Wm Bi^T : Z[k][j] = sum_l Wm[k][l] Bi[j][l]
@@ -167,22 +169,22 @@ __global__ __launch_bounds__(256) void colsum_kernel(const __half* __restrict__ 
 
 template <int KIND>
 static void fold_fmt(int fmt, dim3 g, dim3 b, hipStream_t s, const __half* W, int64_t N, int64_t K,
-                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, const float* P, float t4,
-                     uint8_t* wc, void* ws) {
-  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, P, t4, wc, ws);
-  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, P, t4, wc, ws);
+                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts,
+                     float t4, uint8_t* wc, void* ws) {
+  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, P, pts, t4, wc, ws);
+  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, P, pts, t4, wc, ws);
 }
 
 hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
-                       const int32_t* perm, const int8_t* sign, const float* P, uint8_t* wcodes, void* wscales,
-                       hipStream_t s) {
+                       const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts, uint8_t* wcodes,
+                       void* wscales, hipStream_t s) {
   const int64_t total = N * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const float t4 = lm_tables().t4;
-  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
-  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
-  else if (kind == 3) fold_fmt<3>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
-  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, t4, wcodes, wscales);
+  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  else if (kind == 3) fold_fmt<3>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
   return hipGetLastError();
 }
 

@@ -108,6 +108,10 @@ static kq_status check_xform(const kq_xform* xf, int64_t K) {
     if (!xf->P) return KQ_ERR_NULL;
     if (!aligned(xf->P, 16)) return KQ_ERR_ALIGN;
   }
+  if (xf->pts) {
+    if (xf->kind == KQ_XFORM_RPBH_32) return KQ_ERR_UNSUPPORTED;
+    if (!aligned(xf->pts, 16)) return KQ_ERR_ALIGN;
+  }
   if (xf->kind == KQ_XFORM_KRON_4X8) {
     for (int i = 0; i < 16; ++i)
       if (!std::isfinite(xf->A[i])) return KQ_ERR_VALUE;
@@ -156,16 +160,17 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   // MXFP4 goes through the matrix-core transforms (streaming for Kronecker / identity
   // without centring, row-staged for RPBH); the per-token Lloyd-Max format and centred
   // Kronecker / identity use the row-staged vector kernel.
-  // A dense P runs on the streaming matrix-core path only (MXFP4, no centring).
+  // A dense P and power-of-two channel scaling run on the streaming matrix-core path
+  // only (MXFP4, no centring).
   const bool mx = fmt == KQ_FMT_MXFP4;
   const bool stream_path = mx && !center && xf->kind != KQ_XFORM_RPBH_32;
   const bool rpbh_mfma = mx && xf->kind == KQ_XFORM_RPBH_32;
-  if (xf->kind == KQ_XFORM_DENSE_32 && !stream_path) return KQ_ERR_UNSUPPORTED;
+  if ((xf->kind == KQ_XFORM_DENSE_32 || xf->pts) && !stream_path) return KQ_ERR_UNSUPPORTED;
   if (!stream_path && K > 16384) return KQ_ERR_UNSUPPORTED;
   hipError_t e;
   if (stream_path) {
-    e = launch_kron_mx_mfma(xf->kind, static_cast<const __half*>(X), M * (K / 32), f, xf->P, codes,
-                            static_cast<uint8_t*>(scales), stream);
+    e = launch_kron_mx_mfma(xf->kind, static_cast<const __half*>(X), M * (K / 32), f, xf->P, xf->pts, K / 32,
+                            codes, static_cast<uint8_t*>(scales), stream);
   } else if (rpbh_mfma) {
     e = launch_rpbh_mx_mfma(center != 0, static_cast<const __half*>(X), M, K, xf->perm, xf->sign, codes,
                             static_cast<uint8_t*>(scales), static_cast<__half*>(mu), stream);
@@ -192,7 +197,7 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const vo
     if (!invert(xf->A, 4, finv.A) || !invert(xf->B, 8, finv.B)) return KQ_ERR_VALUE;
   }
   hipError_t e = launch_fold(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 2, static_cast<const __half*>(W), N, K, finv,
-                             xf->perm, xf->sign, xf->P, wcodes, wscales, stream);
+                             xf->perm, xf->sign, xf->P, xf->pts, wcodes, wscales, stream);
   if (e != hipSuccess) return KQ_ERR_HIP;
   if (wbar) e = launch_colsum(static_cast<const __half*>(W), N, K, static_cast<__half*>(wbar), stream);
   return hip_status(e);

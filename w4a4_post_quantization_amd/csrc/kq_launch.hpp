@@ -30,8 +30,9 @@ hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFac
 // Matrix-core block transforms + MXFP4: streaming identity (kind 0), Kronecker (1) or
 // dense 32x32 P (3, device, row-major) without centring, and row-staged RPBH with
 // optional centring.
+// pts (optional, device int8 [nbk * 32]): per-channel power-of-two exponents applied first.
 hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
-                               uint8_t* codes, uint8_t* scales, hipStream_t s);
+                               const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s);
 
@@ -43,10 +44,11 @@ hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int
 
 // Offline fold: W'^T rows = inverse transform of W^T rows, quantized along K.
 // fmt: 0 MXFP4, 2 LM2.  f holds the INVERSE factors for kind 1.
-// kind 3: P (device, row-major) is inverted on the device.
+// kind 3: P (device, row-major) is inverted on the device.  pts (optional): weight input
+// channel k is multiplied by 2^pts[k] before the inverse transform.
 hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
-                       const int32_t* perm, const int8_t* sign, const float* P, uint8_t* wcodes, void* wscales,
-                       hipStream_t s);
+                       const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts, uint8_t* wcodes,
+                       void* wscales, hipStream_t s);
 hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
 
 // T[M][r] = fp16(X L1^T), fp32 accumulation; split over K into `part` (fp32 partials,

@@ -425,10 +425,27 @@ __device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& d
 // Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
 // flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
 // one 16-byte load per lane and writes 256 contiguous code bytes.
+// Eight fp16 values divided by 2^e (one exponent byte each, in order): v_ldexp_f16 rounds a
+// result below the normal range to nearest even, like a conversion would.
+__device__ __forceinline__ uint32_t pts_scale2(uint32_t x2, uint32_t e2) {
+  const _Float16 lo = __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)(x2 & 0xFFFFu)),
+                                              -(int)(e2 & 0xFFu));
+  const _Float16 hi = __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)(x2 >> 16)),
+                                              -(int)((e2 >> 8) & 0xFFu));
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+__device__ __forceinline__ uint4 pts_scale8(uint4 x, uint2 e) {
+  return make_uint4(pts_scale2(x.x, e.x), pts_scale2(x.y, e.x >> 16), pts_scale2(x.z, e.y), pts_scale2(x.w, e.y >> 16));
+}
+
 // KIND: 0 identity, 1 Kronecker A (x) B, 3 dense P (both through the hi + lo split).
-template <int U, int KIND>
+// PTS (DMQ explainer, channel-wise power-of-two scaling): before the transform, input
+// channel c is divided by 2^pts[c] in fp16 (exact unless the result is subnormal); channel
+// c of block blk is (blk mod nbk) * 32 + its position in the block.
+template <int U, int KIND, bool PTS>
 __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* __restrict__ X, int64_t nblocks,
                                                                   KronFactors f, const float* __restrict__ P,
+                                                                  const int8_t* __restrict__ pts, int64_t nbk,
                                                                   uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales) {
   constexpr bool KRON = KIND != 0;        // a general matrix: hi + lo products
@@ -450,6 +467,25 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
   const int64_t nchunks = (nblocks + 15) >> 4;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // channel block of this lane's block: the blocks a lane visits advance by 16 nwaves,
+  // so the block index modulo nbk is carried along instead of divided out each time.  The
+  // exponents are fetched one step ahead (the table is small and stays in cache; the
+  // fetch past the last step reads valid entries and is discarded).
+  int32_t cb = 0, cstep = 0;
+  uint2 ev[U];
+  auto fetch_exponents = [&](uint2* e) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      e[u] = *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q);     // exponents of the 8 channels
+      cb += cstep;
+      cb -= cb >= nbk ? (int32_t)nbk : 0;
+    }
+  };
+  if (PTS) {
+    cb = (int32_t)((wave * 16 + bl) % nbk);
+    cstep = (int32_t)((nwaves * 16) % nbk);
+    fetch_exponents(ev);
+  }
   for (int64_t c0 = wave; c0 < nchunks; c0 += nwaves * U) {
     uint4 raw[U];
 #pragma unroll
@@ -458,8 +494,11 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
       const int64_t blk = c * 16 + bl;
       raw[u] = (c < nchunks && blk < nblocks) ? X[blk * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
     }
+    uint2 ev_next[U];
+    if (PTS) fetch_exponents(ev_next);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (PTS) raw[u] = pts_scale8(raw[u], ev[u]);
       float y[8];
       mfma_block_transform<KRON>(xf, __builtin_bit_cast(v8h, raw[u]), y);
 #pragma unroll
@@ -473,6 +512,10 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
         *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
         if (q == 0) scales[blk] = (uint8_t)sb;
       }
+    }
+    if (PTS) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ev[u] = ev_next[u];
     }
   }
 }
@@ -738,8 +781,19 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
   }
 }
 
+template <int U, int KIND>
+static void stream_launch(dim3 g, hipStream_t s, const uint4* X, int64_t nblocks, const KronFactors& f, const float* P,
+                          const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales) {
+  if (pts)
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, KIND, true>), g, dim3(256), 0, s, X, nblocks, f, P, pts, nbk,
+                       codes, scales);
+  else
+    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, KIND, false>), g, dim3(256), 0, s, X, nblocks, f, P, pts, nbk,
+                       codes, scales);
+}
+
 hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
-                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                               const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   constexpr int U = 4;
   const int64_t nchunks = (nblocks + 15) / 16;
   const int64_t waves = (nchunks + U - 1) / U;
@@ -748,15 +802,10 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   const uint4* Xv = reinterpret_cast<const uint4*>(X);
-  if (kind == 1)
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 1>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
-                       codes, scales);
-  else if (kind == 3)
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 3>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
-                       codes, scales);
-  else
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, 0>), dim3((unsigned)grid), dim3(256), 0, s, Xv, nblocks, f, P,
-                       codes, scales);
+  const dim3 g((unsigned)grid);
+  if (kind == 1) stream_launch<U, 1>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
+  else if (kind == 3) stream_launch<U, 3>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
+  else stream_launch<U, 0>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
   return hipGetLastError();
 }
 
