@@ -79,51 +79,6 @@ __device__ __forceinline__ void hadamard32_quad(float* v, float s1, float s2) {
 }
 
 // ---------------------------------------------------------------------------------
-// Streaming Kronecker + MXFP4: the activations are a flat sequence of 32-element blocks
-// (rows are contiguous and K % 32 == 0).  A wavefront handles 16 blocks (1 KiB of input,
-// one 16-byte load per lane, fully coalesced) per step and writes 256 contiguous bytes
-// of codes and 16 scale bytes.
-template <int U>
-__global__ __launch_bounds__(256) void kron_mx_stream_kernel(const uint4* __restrict__ X, int64_t nblocks,
-                                                             KronFactors f, uint32_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int qi = lane & 3;
-  float acol[4];
-  kron_acol(f, qi, acol);
-  const int64_t nchunks = (nblocks + 15) >> 4;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  for (int64_t c0 = wave; c0 < nchunks; c0 += nwaves * U) {
-    uint4 raw[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * nwaves;
-      ok[u] = (c < nchunks) && (c * 16 + (lane >> 2) < nblocks);
-      raw[u] = ok[u] ? X[c * 64 + lane] : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[8], y[8];
-      unpack8_f16(raw[u], x);
-      kron_quad(x, f, acol, y);
-      float m = 0.0f;
-#pragma unroll
-      for (int l = 0; l < 8; ++l) m = fmaxf(m, fabsf(y[l]));
-      m = quad_max(m);
-      const uint32_t sb = e8m0_byte(m);
-      const uint32_t w = cvt8_fp4(y, e8m0_as_cvt_scale(sb));
-      const int64_t c = c0 + u * nwaves;
-      if (ok[u]) {
-        codes[c * 64 + lane] = w;
-        if (qi == 0) scales[c * 16 + (lane >> 2)] = (uint8_t)sb;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
 // Row-staged kernel: each workgroup walks token rows (grid-strided).  Thread t owns the
 // 8-element groups g = t + T*j (j < NG) of a row; a group's quad holds one 32-element
 // block.  The next row's 16-byte chunks are loaded into registers while the current row
@@ -325,6 +280,10 @@ struct MfmaXform {
 };
 
 // A-operand fragments of P^T for this lane: tile t rows j = 16t + l%16, k = 8q..8q+7.
+// p is made opaque before it is split: otherwise the compiler rounds the lo part's hi
+// straight from the exact product (v_fma_mix, one rounding) but the hi fragment from the
+// float32 product (two roundings), and where the float32 product sits exactly between two
+// fp16 values the two differ by one fp16 step, so hi + lo misses p by that step.
 __device__ __forceinline__ MfmaXform mfma_xform_kron(const KronFactors& f, int lane) {
   MfmaXform x;
   const int q = lane >> 4, jl = lane & 15;
@@ -334,7 +293,8 @@ __device__ __forceinline__ MfmaXform mfma_xform_kron(const KronFactors& f, int l
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int k = 8 * q + i;                 // input index (row of P)
-      const float p = f.A[4 * (k >> 3) + (j >> 3)] * f.B[8 * (k & 7) + (j & 7)];
+      float p = f.A[4 * (k >> 3) + (j >> 3)] * f.B[8 * (k & 7) + (j & 7)];
+      asm volatile("" : "+v"(p));
       const _Float16 hi = (_Float16)p;
       x.a[t][0][i] = hi;
       x.a[t][1][i] = (_Float16)(p - (float)hi);
@@ -422,9 +382,6 @@ __device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& d
   scale_byte = sb;
 }
 
-// Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
-// flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
-// one 16-byte load per lane and writes 256 contiguous code bytes.
 // Eight fp16 values divided by 2^e (one exponent byte each, in order): v_ldexp_f16 rounds a
 // result below the normal range to nearest even, like a conversion would.
 __device__ __forceinline__ uint32_t pts_scale2(uint32_t x2, uint32_t e2) {
@@ -438,6 +395,9 @@ __device__ __forceinline__ uint4 pts_scale8(uint4 x, uint2 e) {
   return make_uint4(pts_scale2(x.x, e.x), pts_scale2(x.y, e.x >> 16), pts_scale2(x.z, e.y), pts_scale2(x.w, e.y >> 16));
 }
 
+// Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
+// flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
+// one 16-byte load per lane and writes 256 contiguous code bytes.
 // KIND: 0 identity, 1 Kronecker A (x) B, 3 dense P (both through the hi + lo split).
 // PTS (DMQ explainer, channel-wise power-of-two scaling): before the transform, input
 // channel c is divided by 2^pts[c] in fp16 (exact unless the result is subnormal); channel
@@ -516,6 +476,65 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
     if (PTS) {
 #pragma unroll
       for (int u = 0; u < U; ++u) ev[u] = ev_next[u];
+    }
+  }
+}
+
+// Per-block Kronecker factors + MXFP4 on the matrix cores (KroQuant §02 with one (A, B)
+// pair per block index instead of one per layer).  The matrix-core step transforms 16
+// blocks that share one P, so here they are the same block index cb of 16 consecutive
+// token rows: a wavefront owns one cb and a run of 16-row groups, forms its P's fp16
+// hi + lo fragments once, and then streams the rows.  Lane (q, bl) loads 16 bytes of row
+// 16g + bl at channel 32 cb + 8q; the four wavefronts of a workgroup take consecutive
+// block indices, so together they read 256 contiguous bytes of each row.
+// AB: float [nbk][80] per block index: A (16, row-major) then B (64, row-major).
+// PTS as in the streaming kernel; a wavefront's channels are fixed, so its exponents are
+// read once.
+template <int U, bool PTS>
+__global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __restrict__ X, int64_t M, int64_t nbk,
+                                                             int64_t nseg, int64_t gps,
+                                                             const float* __restrict__ AB,
+                                                             const int8_t* __restrict__ pts,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= nbk * nseg) return;                          // whole wavefronts only
+  const int64_t cb = wave % nbk, seg = wave / nbk;
+  KronFactors f;
+  const float* ab = AB + cb * 80;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f.A[i] = ab[i];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) f.B[i] = ab[16 + i];
+  const MfmaXform xf = mfma_xform_kron(f, lane);
+  uint2 ev = make_uint2(0u, 0u);
+  if (PTS) ev = *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q);
+  const int64_t ngroups = (M + 15) >> 4;
+  const int64_t g0 = seg * gps, g1 = g0 + gps < ngroups ? g0 + gps : ngroups;
+  for (int64_t g = g0; g < g1; g += U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = (g + u) * 16 + bl;
+      raw[u] = (g + u < g1 && row < M) ? X[(row * nbk + cb) * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (PTS) raw[u] = pts_scale8(raw[u], ev);
+      float y[8];
+      mfma_block_transform<true>(xf, __builtin_bit_cast(v8h, raw[u]), y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] += 0.0f;      // an exact zero leaves as +0
+      uint32_t w, sb;
+      int off;
+      mx_pack_block(y, q, w, off, sb);
+      const int64_t row = (g + u) * 16 + bl;
+      if (g + u < g1 && row < M) {
+        const int64_t blk = row * nbk + cb;
+        *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
+        if (q == 0) scales[blk] = (uint8_t)sb;
+      }
     }
   }
 }
@@ -809,6 +828,30 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
   return hipGetLastError();
 }
 
+// Per-block factors: nbk * nseg wavefronts, segment s of block index cb taking the 16-row
+// groups [s gps, (s + 1) gps).  About eight workgroups per compute unit in total.
+hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  constexpr int U = 4;
+  const int64_t nbk = K / 32, ngroups = (M + 15) / 16;
+  const int64_t target = (int64_t)device_cu_count() * 8 * 4;
+  int64_t nseg = (target + nbk - 1) / nbk;
+  const int64_t cap = (ngroups + U - 1) / U;                // at least U groups per segment
+  if (nseg > cap) nseg = cap;
+  if (nseg < 1) nseg = 1;
+  const int64_t gps = (ngroups + nseg - 1) / nseg;
+  nseg = (ngroups + gps - 1) / gps;                        // no empty segment
+  const dim3 g((unsigned)((nbk * nseg + 3) / 4));
+  const uint4* Xv = reinterpret_cast<const uint4*>(X);
+  if (pts)
+    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, true>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, false>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
+                       scales);
+  return hipGetLastError();
+}
+
 template <int R, bool CENTER>
 static hipError_t rpbh_group_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
                                     uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
@@ -861,20 +904,6 @@ int device_cu_count() {
     return n;
   }();
   return cus;
-}
-
-hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFactors& f, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s) {
-  constexpr int U = 2;
-  const int64_t nchunks = (nblocks + 15) / 16;
-  const int64_t waves = (nchunks + U - 1) / U;
-  int64_t grid = (waves + 3) / 4;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kron_mx_stream_kernel<U>, dim3((unsigned)grid), dim3(256), 0, s,
-                     reinterpret_cast<const uint4*>(X), nblocks, f, reinterpret_cast<uint32_t*>(codes), scales);
-  return hipGetLastError();
 }
 
 template <int KIND, int FMT, bool CENTER, int NG>
