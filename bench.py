@@ -230,7 +230,8 @@ def main():
     dur = [[p[1], p[0], p[2]] for p in per]
 
     # ---- transform variants beside the path (not part of the step): the Kronecker factors
-    # and a dense 32x32 P on the same streaming matrix-core kernel, MXFP4 without centring,
+    # and a dense 32x32 P on the same streaming matrix-core kernel, per-block factors on
+    # theirs, MXFP4 without centring,
     # each also behind power-of-two channel scaling (exponent 6 on the planted outlier
     # channels), at the step's widths; event pair around back-to-back launches over the
     # rotated inputs
@@ -242,9 +243,11 @@ def main():
             codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
             pts = torch.from_numpy(synth.pts_exponents(K, synth.outlier_channels(M, K, CFG, cfg["sigma_mu"]))).to(dev)
-            kx, dx = kq.Xform.kron(A, B, K), kq.Xform.dense(P, K)
-            for name, xf in (("kron_4x8", kx), ("dense_32", dx), ("kron_4x8+pts", kx.with_pts(pts)),
-                             ("dense_32+pts", dx.with_pts(pts))):
+            Ab, Bb = synth.kron_block_factors(CFG, 0, K // 32)
+            AB = torch.from_numpy(kq.Xform.pack_block_factors(Ab, Bb)).to(dev)
+            kx, dx, bx = kq.Xform.kron(A, B, K), kq.Xform.dense(P, K), kq.Xform.kron_blocks(AB, K)
+            for name, xf in (("kron_4x8", kx), ("dense_32", dx), ("kron_blocks", bx), ("kron_4x8+pts", kx.with_pts(pts)),
+                             ("dense_32+pts", dx.with_pts(pts)), ("kron_blocks+pts", bx.with_pts(pts))):
                 def run(i, xf=xf, K=K):
                     kq.transform_quantize(Xsets[i % R][K], xf, fmt="mxfp4", codes=codes, scales=scales)
                 run(0)
@@ -259,7 +262,7 @@ def main():
                 tb = transform_bytes(M, K, False)
                 variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
                                  "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
-                log(f"variant {name:>12} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
+                log(f"variant {name:>15} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
 
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 4
+#define KQ_ABI_VERSION 5
 
 typedef int32_t kq_status;
 enum {
@@ -68,7 +68,8 @@ enum {
 };
 
 /* transform kinds */
-enum { KQ_XFORM_NONE = 0, KQ_XFORM_KRON_4X8 = 1, KQ_XFORM_RPBH_32 = 2, KQ_XFORM_DENSE_32 = 3 };
+enum { KQ_XFORM_NONE = 0, KQ_XFORM_KRON_4X8 = 1, KQ_XFORM_RPBH_32 = 2, KQ_XFORM_DENSE_32 = 3,
+       KQ_XFORM_KRON_4X8_BLOCKS = 4 };
 /* formats */
 enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
 
@@ -87,6 +88,12 @@ enum { KQ_FMT_MXFP4 = 0, KQ_FMT_LM4_TOKEN = 1, KQ_FMT_LM2_G32 = 2 };
  *   (P: device float32 [32][32], row-major, 16-byte aligned; one P shared by all blocks).
  *   MXFP4 without centring only; the fold inverts P on the device (a singular P gives
  *   non-finite weights).
+ * KRON_4X8_BLOCKS (KroQuant §02 with one factor pair per block index): block b of every
+ *   token is replaced by x_b . (A_b (x) B_b), same convention as KRON_4X8, with
+ *   AB: device float32 [K/32][80], 16-byte aligned; row b holds A_b (16, row-major) then
+ *   B_b (64, row-major).  MXFP4 without centring only.  The factors are not checked: a
+ *   non-finite entry gives unspecified codes, and the fold inverts each A_b (x) B_b on the
+ *   device (a singular one gives non-finite weights for that block).
  * NONE: identity.
  * pts (optional, any kind but RPBH_32; DMQ explainer, channel-wise power-of-two scaling):
  *   device int8 [K], 16-byte aligned, entries e_k in 0..15.  The activation path first
@@ -104,6 +111,7 @@ typedef struct kq_xform {
   const int32_t* perm;
   const int8_t* sign;
   const float* P;            /* DENSE_32 only */
+  const float* AB;           /* KRON_4X8_BLOCKS only */
   const int8_t* pts;         /* NULL or per-channel power-of-two exponents */
 } kq_xform;
 

@@ -14,6 +14,8 @@ Transform descriptors are plain dicts:
   {"kind": "kron", "A": float32 [4, 4], "B": float32 [8, 8]}
   {"kind": "rpbh", "perm": int [K], "sign": int8 [K] (+-1)}
   {"kind": "dense", "P": float32 [32, 32]}     (y_b = x_b . P)
+  {"kind": "kron_blocks", "A": float32 [K/32, 4, 4], "B": float32 [K/32, 8, 8]}
+                                               (y_b = x_b . kron(A_b, B_b))
   {"kind": "none"}
 Any of them except "rpbh" may carry "pts": int [K] of power-of-two exponents (DMQ
 explainer, channel-wise power-of-two scaling): the activation path first replaces
@@ -57,6 +59,8 @@ def apply_transform(x, xform):
         return transforms.rpbh_apply(x, xform["perm"], xform["sign"])
     if kind == "dense":
         return transforms.apply_block_matrix(x, np.asarray(xform["P"], dtype=np.float64))
+    if kind == "kron_blocks":
+        return transforms.apply_block_matrices(x, transforms.kron_block_matrices(xform["A"], xform["B"]))
     if kind == "none":
         return np.asarray(x, dtype=np.float64)
     raise ValueError(kind)
@@ -105,6 +109,8 @@ def inverse_fold(W_out_in, xform):
         return transforms.fold_rpbh(W_out_in, xform["perm"], xform["sign"])
     if kind == "dense":
         return transforms.fold_dense(W_out_in, xform["P"])
+    if kind == "kron_blocks":
+        return transforms.fold_kron_blocks(W_out_in, xform["A"], xform["B"])
     if kind == "none":
         return np.asarray(W_out_in, dtype=np.float64)
     raise ValueError(kind)

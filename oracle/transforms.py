@@ -14,6 +14,8 @@ an explicit permutation gather); it never uses a factored or butterfly form.
   orthogonal, as the page states R is.
 * Dense block transform (KroQuant page, §01): the same per-block product with a full
   32x32 P, of which kron(A, B) is the factorized form.
+* Per-block Kronecker factors (KroQuant page, §02, with one (A_b, B_b) pair per block
+  index b instead of one per layer): y_blk_b = x_blk_b . kron(A_b, B_b).
 * Offline fold (KroQuant §01; OrbitQuant §03): W' = P^-1 W (R^-1 = R^T), so that
   (XP)(P^-1 W) = XW.
 """
@@ -37,6 +39,22 @@ def apply_block_matrix(x, P32):
     M, K = x.shape
     blocks = x.reshape(M, K // BLOCK, BLOCK)
     return (blocks @ P32).reshape(M, K)
+
+
+def kron_block_matrices(A, B):
+    """Per-block dense transforms kron(A_b, B_b), [nb, 32, 32] float64, from A [nb, 4, 4]
+    and B [nb, 8, 8]."""
+    A = np.asarray(A, dtype=np.float64).reshape(-1, 4, 4)
+    B = np.asarray(B, dtype=np.float64).reshape(-1, 8, 8)
+    return np.stack([np.kron(a, b) for a, b in zip(A, B)])
+
+
+def apply_block_matrices(x, Ps):
+    """y_b = x_b . Ps[b] for every 32-block b of rows x [M, K], Ps [K/32, 32, 32]."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    blocks = x.reshape(M, K // BLOCK, BLOCK)
+    return np.einsum("mbi,bij->mbj", blocks, np.asarray(Ps, dtype=np.float64)).reshape(M, K)
 
 
 def hadamard32():
@@ -83,6 +101,14 @@ def fold_dense(W_out_in, P32):
     Wt = np.asarray(W_out_in, dtype=np.float64)
     Pinv = np.linalg.inv(np.asarray(P32, dtype=np.float64).reshape(BLOCK, BLOCK))
     return apply_block_matrix(Wt, Pinv.T)
+
+
+def fold_kron_blocks(W_out_in, A, B):
+    """W' = blockdiag_b(inv(kron(A_b, B_b))) W for per-block factors, W given as [N][K];
+    returns W'^T as [N][K] float64 (each inverse from LAPACK on its dense 32x32 block)."""
+    Wt = np.asarray(W_out_in, dtype=np.float64)
+    Pinv = np.linalg.inv(kron_block_matrices(A, B))
+    return apply_block_matrices(Wt, np.transpose(Pinv, (0, 2, 1)))
 
 
 def fold_rpbh(W_out_in, perm, sign):

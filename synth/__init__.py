@@ -14,7 +14,8 @@ SANA, FLUX.1 and CogVideoX, which are not available):
   N(0, 1) over frame-major tokens;
 * Kronecker factors A = Q_A diag(u_A), B = Q_B diag(u_B) with Q Haar-random
   orthogonal (QR of a Gaussian matrix with the sign of R's diagonal folded in) and
-  u ~ U[0.5, 2]; one pair per layer; float32;
+  u ~ U[0.5, 2]; one pair per layer (or, for per-block factors, one independent pair per
+  block index); float32;
 * RPBH parameters: a uniform random permutation of K and uniform random +-1 signs;
 * power-of-two channel exponents: round(log2(outlier scale)) = 6 on the planted
   outlier channels of the activations and 0 elsewhere (the channels the scaling is
@@ -55,7 +56,7 @@ CONFIGS = {
 N_OUTLIERS = 12
 OUTLIER_SCALE = 50.0
 
-_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE, _TAG_PTS = 1, 2, 3, 4, 5, 6
+_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE, _TAG_PTS, _TAG_KRON_BLOCKS = 1, 2, 3, 4, 5, 6, 7
 
 
 def _rng(*key):
@@ -110,6 +111,15 @@ def kron_factors(seed, layer):
     rng = _rng(seed, _TAG_KRON, layer)
     A = _haar(rng, 4) * rng.uniform(0.5, 2.0, size=4)[None, :]
     B = _haar(rng, 8) * rng.uniform(0.5, 2.0, size=8)[None, :]
+    return A.astype(np.float32), B.astype(np.float32)
+
+
+def kron_block_factors(seed, layer, nb):
+    """Per-block factors (A [nb, 4, 4], B [nb, 8, 8]) float32: the Kronecker recipe drawn
+    independently for each block index."""
+    rng = _rng(seed, _TAG_KRON_BLOCKS, layer, nb)
+    A = np.stack([_haar(rng, 4) * rng.uniform(0.5, 2.0, size=4)[None, :] for _ in range(nb)])
+    B = np.stack([_haar(rng, 8) * rng.uniform(0.5, 2.0, size=8)[None, :] for _ in range(nb)])
     return A.astype(np.float32), B.astype(np.float32)
 
 

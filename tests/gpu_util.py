@@ -8,9 +8,9 @@ from oracle import mxfp4, pipeline, ties, transforms
 U = 2.0 ** -24
 
 # Forward-error bounds of the kernels' float32 arithmetic per output element, by path:
-#  Kronecker or dense P, no centring (matrix cores): P (A (x) B formed in float32, or
-#      given) split into fp16 hi + lo parts (~2^-21 relative), 64 exact products
-#      accumulated in float32;
+#  Kronecker (shared or per-block factors) or dense P, no centring (matrix cores): P
+#      (A (x) B formed in float32, or given) split into fp16 hi + lo parts (~2^-21
+#      relative), 64 exact products accumulated in float32;
 #  Kronecker or identity with centring, and Lloyd-Max (vector units): an 8-term FMA chain
 #      feeding a 4-term chain, plus the centring subtraction;
 #  RPBH, MXFP4 (matrix cores): 32 exact +-1 products of the UNCENTRED inputs accumulated in
@@ -19,7 +19,7 @@ U = 2.0 ** -24
 #  RPBH, Lloyd-Max (vector units): five butterfly stages, 1/sqrt(32), the product, and
 #      the centring subtraction.
 def _path(kind, center, fmt):
-    if kind == "dense":
+    if kind in ("dense", "kron_blocks"):
         return ("uncentred", 80)
     if kind == "kron":
         return ("uncentred", 80) if (not center and fmt == "mxfp4") else ("centred", 14)
@@ -39,6 +39,8 @@ def abs_transform(x_abs, xform):
         return transforms.apply_block_matrix(u, np.abs(transforms.hadamard32())) / np.sqrt(32.0)
     if kind == "dense":
         return transforms.apply_block_matrix(x_abs, np.abs(np.asarray(xform["P"], dtype=np.float64)))
+    if kind == "kron_blocks":
+        return transforms.apply_block_matrices(x_abs, np.abs(transforms.kron_block_matrices(xform["A"], xform["B"])))
     return x_abs
 
 

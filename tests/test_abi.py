@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 4
+    assert kq.abi_version() == 5
     for s in range(0, 7):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
@@ -108,6 +108,22 @@ def test_pts_validation(lib):
     rp.perm, rp.sign, rp.pts = 0x100000, 0x100000, 0x100000
     assert f(ctypes.byref(rp), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with RPBH
     assert g(ctypes.byref(rp), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 4
+
+
+def test_kron_blocks_validation(lib):
+    """Per-block factors: the factor table must be given and 16-byte aligned; MXFP4 without
+    centring only; kinds past the last are refused."""
+    f, g = lib.kq_transform_quantize, lib.kq_fold_inverse_into_weights
+    xf = _xf(kind=4)
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 1          # NULL AB
+    assert g(ctypes.byref(xf), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 1
+    xf.AB = 0x100008
+    assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 3          # misaligned
+    xf.AB = 0x100000
+    assert f(ctypes.byref(xf), 0, 1, FAKE, 4, 64, FAKE, FAKE, FAKE, None) == 4          # with centring
+    assert f(ctypes.byref(xf), 1, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with LM4
+    bad = _xf(kind=5)
+    assert f(ctypes.byref(bad), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4
 
 
 def test_fold_validation(lib):

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import linear, lloyd_max, mxfp4, pipeline, ties
+from oracle import linear, lloyd_max, mxfp4, pipeline, ties, transforms
 from tests import gpu_util
 from tests.test_gpu_transform import _dev_xform
 
@@ -155,6 +155,48 @@ def test_w4a4_pts_linear(kq, kind):
     print(f"pts {kind} linear rel frobenius {err:.3e}; against exact X W {qerr:.3e}")
     assert err <= TOL
     assert qerr < 1.0
+
+
+@pytest.mark.parametrize("K,N,pts", [(1152, 160, False), (96, 40, False), (3072, 64, True)])
+def test_fold_kron_blocks_matches_oracle(kq, K, N, pts):
+    """The fold with per-block factors: each block's A_b (x) B_b formed in float64 and
+    inverted on the device by Gauss-Jordan, then a float32 product per block."""
+    W16, _, _ = synth.weights(K, N, 19, 0, 0)
+    A, B = synth.kron_block_factors(19, 0, K // 32)
+    xf = {"kind": "kron_blocks", "A": A, "B": B}
+    wd = np.abs(W16.astype(np.float64))
+    if pts:
+        xf["pts"] = synth.pts_exponents(K, seed=19)
+        wd = np.ldexp(wd, xf["pts"].astype(np.int64)[None, :])
+    wc, ws, wbar = _fold(kq, W16, xf, "mxfp4")
+    wt = pipeline.inverse_fold(W16, xf)
+    Pinv = np.linalg.inv(transforms.kron_block_matrices(A, B))
+    tau = ties.gamma_tau(36, transforms.apply_block_matrices(wd, np.abs(np.transpose(Pinv, (0, 2, 1)))))
+    gpu_util.assert_mx_parity(wc.cpu().numpy(), ws.cpu().numpy(), wt, tau, label=f"fold kron_blocks K={K}")
+    _wbar_check(W16, wbar.cpu().numpy())
+
+
+def test_w4a4_kron_blocks_linear(kq):
+    """The whole path with per-block factors: transform + quantize, fold, low-rank branch,
+    W4A4 linear, against the oracle on the kernel's own packed operands."""
+    import torch
+    M, K, N, r = 300, 1152, 512, 32
+    X16 = synth.activations(M, K, 20, 2.0)
+    W16, L1, L2 = synth.weights(K, N, 20, 0, r)
+    A, B = synth.kron_block_factors(20, 0, K // 32)
+    xf = {"kind": "kron_blocks", "A": A, "B": B}
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
+    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    torch.cuda.synchronize()
+    ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
+                             None, None)
+    err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+    print(f"kron_blocks linear rel frobenius {err:.3e}")
+    assert err <= TOL
 
 
 def test_fold_w2_matches_oracle(kq):

@@ -23,6 +23,8 @@ def _dev_xform(kq, torch, xf, K):
                           torch.from_numpy(np.ascontiguousarray(xf["sign"], dtype=np.int8)).cuda())
     elif xf["kind"] == "dense":
         d = kq.Xform.dense(torch.from_numpy(np.ascontiguousarray(xf["P"], dtype=np.float32)).cuda(), K)
+    elif xf["kind"] == "kron_blocks":
+        d = kq.Xform.kron_blocks(torch.from_numpy(kq.Xform.pack_block_factors(xf["A"], xf["B"])).cuda(), K)
     else:
         d = kq.Xform.none(K)
     if xf.get("pts") is not None:
@@ -110,6 +112,45 @@ def test_mxfp4_pts_matches_oracle(kq, kind, K, rows, which):
     if kind == "dense":
         xf["P"] = synth.dense_block(13, 0)
     _mx_check(kq, X16, xf, False, f"pts {which} {kind} K={K} M={rows}")
+
+
+@pytest.mark.parametrize("K,rows,pts", [(3072, 203, False), (1152, 150, False), (96, 7, False), (12288, 37, False),
+                                        (64, 1, False), (1152, 150, True), (3072, 48, True)])
+def test_mxfp4_kron_blocks_matches_oracle(kq, K, rows, pts):
+    """Per-block Kronecker factors (one (A_b, B_b) per block index) on the matrix-core
+    kernel that holds one block index per wavefront; ragged row counts, one row, and
+    power-of-two channel scaling ahead of it (random exponents 0..15)."""
+    X16 = synth.activations(rows, K, 17, 2.0)
+    A, B = synth.kron_block_factors(17, 0, K // 32)
+    xf = {"kind": "kron_blocks", "A": A, "B": B}
+    if pts:
+        xf["pts"] = synth.pts_exponents(K, seed=K + 1)
+    _mx_check(kq, X16, xf, False, f"kron_blocks K={K} M={rows} pts={pts}")
+
+
+def test_kron_blocks_full_size_sampled_rows(kq):
+    """The FLUX-like width at full M (4608 x 12288): codes of sampled rows against the
+    oracle, in the launch the bench times."""
+    M, K = 4608, 12288
+    X16 = synth.activations(M, K, 18, 4.0)
+    A, B = synth.kron_block_factors(18, 0, K // 32)
+    xf = {"kind": "kron_blocks", "A": A, "B": B}
+    codes, scales, _ = _run(kq, X16, xf, "mxfp4", False)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    y, tau, _ = gpu_util.oracle_activation_reference(X16[rows], xf, False)
+    gpu_util.assert_mx_parity(codes[rows], scales[rows], y, tau, label=f"kron_blocks full sampled {len(rows)}")
+
+
+def test_kron_blocks_rejects_unsupported(kq):
+    """Per-block factors are offered on the MXFP4 path without centring only."""
+    import torch
+    X = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    AB = torch.zeros((2, 80), dtype=torch.float32, device="cuda")
+    for fmt, center in (("mxfp4", True), ("lm4", False)):
+        with pytest.raises(kq.KQError):
+            kq.transform_quantize(X, kq.Xform.kron_blocks(AB, 64), fmt=fmt, center=center)
+    with pytest.raises(ValueError):
+        kq.Xform.kron_blocks(torch.zeros((3, 80), dtype=torch.float32, device="cuda"), 64)
 
 
 def test_pts_rejects_unsupported(kq):

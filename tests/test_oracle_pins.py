@@ -198,7 +198,7 @@ def test_rpbh_orthogonal_and_matches_dense():
 
 # ---------------------------------------------------------------- P5: the identity
 
-@pytest.mark.parametrize("kind", ["kron", "rpbh", "dense"])
+@pytest.mark.parametrize("kind", ["kron", "rpbh", "dense", "kron_blocks"])
 def test_invertible_transform_identity(kind):
     """(XP)(P^-1 W) = XW (KroQuant section 01; OrbitQuant section 03 W' = R^-1 W)."""
     rng = np.random.default_rng(6)
@@ -210,6 +210,10 @@ def test_invertible_transform_identity(kind):
         xf = {"kind": "kron", "A": A, "B": B}
     elif kind == "dense":
         xf = {"kind": "dense", "P": rng.standard_normal((32, 32)) + 4 * np.eye(32)}
+    elif kind == "kron_blocks":
+        import synth
+        A, B = synth.kron_block_factors(7, 0, K // 32)
+        xf = {"kind": "kron_blocks", "A": A, "B": B}
     else:
         xf = {"kind": "rpbh", "perm": rng.permutation(K), "sign": rng.choice([-1, 1], K)}
     lhs = pipeline.apply_transform(X, xf) @ pipeline.inverse_fold(Wt, xf).T
@@ -251,6 +255,33 @@ def test_dense_block_special_cases():
     Wt = rng.standard_normal((7, 96))
     wpt = pipeline.inverse_fold(Wt, {"kind": "dense", "P": np.diag(d)})
     assert np.allclose(wpt, Wt / np.tile(d, 3)[None, :], rtol=1e-15)
+
+
+def test_kron_blocks_reduce_to_shared_and_index_blocks():
+    """Per-block factors: with every block given the same (A, B) they reduce to the shared
+    Kronecker transform (pinned above against the factored form); with identity factors
+    everywhere except block b, where A = diag(a) and B is the permutation matrix with
+    B[pi(l), l] = 1, only block b changes and y[32b + 8k + l] = a_k x[32b + 8k + pi(l)]
+    (np.kron order, row-vector convention, block b of the table acting on block b of x)."""
+    rng = np.random.default_rng(23)
+    K = 128
+    X = rng.standard_normal((6, K))
+    A, B = _random_factors(24)
+    same = {"kind": "kron_blocks", "A": np.stack([A] * 4), "B": np.stack([B] * 4)}
+    assert np.allclose(pipeline.apply_transform(X, same), pipeline.apply_transform(X, {"kind": "kron", "A": A, "B": B}),
+                       rtol=1e-13, atol=1e-13)
+    Ab = np.stack([np.eye(4)] * 4)
+    Bb = np.stack([np.eye(8)] * 4)
+    a, pi, b = rng.uniform(0.5, 2.0, 4), rng.permutation(8), 2
+    Ab[b] = np.diag(a)
+    Bb[b] = 0.0
+    Bb[b][pi, np.arange(8)] = 1.0
+    y = pipeline.apply_transform(X, {"kind": "kron_blocks", "A": Ab, "B": Bb})
+    want = X.copy()
+    for k in range(4):
+        for l in range(8):
+            want[:, 32 * b + 8 * k + l] = a[k] * X[:, 32 * b + 8 * k + pi[l]]
+    assert np.array_equal(y, want)
 
 
 def test_dense_orthogonal_preserves_block_norms():

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 KQ_OK = 0
-XFORM_NONE, XFORM_KRON, XFORM_RPBH, XFORM_DENSE = 0, 1, 2, 3
+XFORM_NONE, XFORM_KRON, XFORM_RPBH, XFORM_DENSE, XFORM_KRON_BLOCKS = 0, 1, 2, 3, 4
 FMT_MXFP4, FMT_LM4, FMT_LM2 = 0, 1, 2
 _FMT = {"mxfp4": FMT_MXFP4, "lm4": FMT_LM4, "lm2": FMT_LM2}
 
@@ -38,7 +38,7 @@ class _XformC(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("K", ctypes.c_int64),
                 ("A", ctypes.c_float * 16), ("B", ctypes.c_float * 64),
                 ("perm", ctypes.c_void_p), ("sign", ctypes.c_void_p), ("P", ctypes.c_void_p),
-                ("pts", ctypes.c_void_p)]
+                ("AB", ctypes.c_void_p), ("pts", ctypes.c_void_p)]
 
 
 def lib_path():
@@ -127,7 +127,7 @@ def _check(t, name, dtype, shape=None):
 class Xform:
     """One layer's block transform descriptor (KRON_4X8, RPBH_32, DENSE_32 or NONE)."""
 
-    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None, P=None, pts=None):
+    def __init__(self, kind, K, A=None, B=None, perm=None, sign=None, P=None, AB=None, pts=None):
         self.kind, self.K = kind, int(K)
         self._c = _XformC()
         self._c.kind, self._c.reserved, self._c.K = kind, 0, self.K
@@ -149,6 +149,10 @@ class Xform:
             torch = _torch()
             _check(P, "P", torch.float32, (32, 32))
             self._c.P = P.data_ptr()
+        self.AB = AB
+        if kind == XFORM_KRON_BLOCKS:
+            _check(AB, "AB", _torch().float32, (self.K // 32, 80))
+            self._c.AB = AB.data_ptr()
         self.pts = pts
         if pts is not None:
             _check(pts, "pts", _torch().int8, (self.K,))
@@ -158,11 +162,25 @@ class Xform:
         """The same transform preceded by power-of-two channel scaling: pts is an int8 [K]
         device tensor of exponents (0..15); x_k -> fp16(x_k 2^-pts[k]), weights x 2^pts[k]."""
         return Xform(self.kind, self.K, A=list(self._c.A), B=list(self._c.B), perm=self.perm, sign=self.sign,
-                     P=self.P, pts=pts)
+                     P=self.P, AB=self.AB, pts=pts)
 
     @classmethod
     def kron(cls, A, B, K):
         return cls(XFORM_KRON, K, A=A, B=B)
+
+    @classmethod
+    def kron_blocks(cls, AB, K):
+        """AB: float32 [K/32][80] device tensor, row b = A_b (4x4) then B_b (8x8), row-major;
+        block b of every token becomes x_b . (A_b (x) B_b)."""
+        return cls(XFORM_KRON_BLOCKS, K, AB=AB)
+
+    @staticmethod
+    def pack_block_factors(A, B):
+        """Host helper: A [nb][4][4], B [nb][8][8] -> the float32 [nb][80] table (numpy)."""
+        import numpy as np
+        A = np.asarray(A, dtype=np.float32)
+        B = np.asarray(B, dtype=np.float32)
+        return np.ascontiguousarray(np.concatenate([A.reshape(len(A), 16), B.reshape(len(B), 64)], axis=1))
 
     @classmethod
     def dense(cls, P, K):

@@ -9,17 +9,21 @@ namespace kq {
 
 #define KQ_INV_SQRT32_F 0.17677669529663688110f
 
-// P^-1 of a dense 32x32 P (row-major, global) into LDS as float: Gauss-Jordan elimination
-// with partial pivoting in float64 by the whole workgroup (offline: clarity over speed).
-// A singular P gives non-finite entries.
-__device__ void invert32(const float* __restrict__ P, float* __restrict__ pinv) {
+// P^-1 of a 32x32 P into LDS as float: Gauss-Jordan elimination with partial pivoting in
+// float64 by the whole workgroup (offline: clarity over speed).  P is either dense
+// (row-major, global) or, with ab != NULL, the Kronecker product A (x) B of one block's
+// factors ab = {A 4x4, B 8x8} (row-major), formed exactly in float64:
+// (A (x) B)[i][j] = A[i/8][j/8] B[i%8][j%8].  A singular P gives non-finite entries.
+__device__ void invert32(const float* __restrict__ P, const float* __restrict__ ab, float* __restrict__ pinv) {
   __shared__ double aug[32][64];
   __shared__ double fac[32];
   __shared__ int piv;
   const int t = threadIdx.x, T = blockDim.x;
   for (int e = t; e < 32 * 64; e += T) {
     const int i = e >> 6, j = e & 63;
-    aug[i][j] = j < 32 ? (double)P[32 * i + j] : (j - 32 == i ? 1.0 : 0.0);
+    if (j >= 32) aug[i][j] = j - 32 == i ? 1.0 : 0.0;
+    else if (ab) aug[i][j] = (double)ab[4 * (i >> 3) + (j >> 3)] * (double)ab[16 + 8 * (i & 7) + (j & 7)];
+    else aug[i][j] = (double)P[32 * i + j];
   }
   __syncthreads();
   for (int c = 0; c < 32; ++c) {
@@ -56,18 +60,21 @@ __device__ void invert32(const float* __restrict__ P, float* __restrict__ pinv) 
 // KIND 1: w'_b = (Ai (x) Bi) w_b, i.e. W'm = Ai Wm Bi^T with Wm[k][l] = w_b[8k+l].
 // KIND 2: w' = w R (the forward RPBH of the row, since W'^T = W^T R).
 // KIND 3: w'_b = P^-1 w_b for a dense block transform P.
+// KIND 4: w'_b = (A_b (x) B_b)^-1 w_b with per-block factors (P = AB, float [nb][80]); the
+//         grid is 2-D, blockIdx.y = b, so a workgroup inverts one block's P.
 // FMT 0: MXFP4 (16 code bytes + 1 E8M0 byte); FMT 2: 2-bit Lloyd-Max + fp16 group scale.
 template <int KIND, int FMT>
 __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, KronFactors fi,
                                                    const int32_t* __restrict__ perm, const int8_t* __restrict__ sign,
                                                    const float* __restrict__ P, const int8_t* __restrict__ pts,
                                                    float t4, uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
-  __shared__ float pinv[KIND == 3 ? 32 * 32 : 1];
-  if (KIND == 3) invert32(P, pinv);         // every thread of the workgroup takes part
+  __shared__ float pinv[KIND >= 3 ? 32 * 32 : 1];
+  if (KIND == 3) invert32(P, nullptr, pinv);          // every thread of the workgroup takes part
+  if (KIND == 4) invert32(nullptr, P + (int64_t)blockIdx.y * 80, pinv);
   const int64_t nb = K >> 5;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= N * nb) return;
-  const int64_t n = id / nb, b = id % nb;
+  if (KIND == 4 ? id >= N : id >= N * nb) return;
+  const int64_t n = KIND == 4 ? id : id / nb, b = KIND == 4 ? (int64_t)blockIdx.y : id % nb;
   const __half* wr = W + n * K;
   float w[32], y[32];
 #pragma unroll
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W,
         for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(fi.A[4 * i + k], z[8 * k + j], acc);
         y[8 * i + j] = acc;
       }
-  } else if (KIND == 3) {
+  } else if (KIND >= 3) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       float acc = 0.0f;
@@ -181,7 +188,10 @@ hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K,
   const int64_t total = N * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const float t4 = lm_tables().t4;
-  if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  if (kind == 4) {
+    const dim3 g2((unsigned)((N + 255) / 256), (unsigned)(K / 32));
+    fold_fmt<4>(fmt, g2, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  } else if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
   else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
   else if (kind == 3) fold_fmt<3>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
   else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);

@@ -98,7 +98,7 @@ static kq_status hip_status(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_
 
 static kq_status check_xform(const kq_xform* xf, int64_t K) {
   if (!xf) return KQ_ERR_NULL;
-  if (xf->kind < KQ_XFORM_NONE || xf->kind > KQ_XFORM_DENSE_32 || xf->reserved != 0) return KQ_ERR_UNSUPPORTED;
+  if (xf->kind < KQ_XFORM_NONE || xf->kind > KQ_XFORM_KRON_4X8_BLOCKS || xf->reserved != 0) return KQ_ERR_UNSUPPORTED;
   if (xf->K != K) return KQ_ERR_SHAPE;
   if (xf->kind == KQ_XFORM_RPBH_32) {
     if (!xf->perm || !xf->sign) return KQ_ERR_NULL;
@@ -107,6 +107,10 @@ static kq_status check_xform(const kq_xform* xf, int64_t K) {
   if (xf->kind == KQ_XFORM_DENSE_32) {
     if (!xf->P) return KQ_ERR_NULL;
     if (!aligned(xf->P, 16)) return KQ_ERR_ALIGN;
+  }
+  if (xf->kind == KQ_XFORM_KRON_4X8_BLOCKS) {
+    if (!xf->AB) return KQ_ERR_NULL;
+    if (!aligned(xf->AB, 16)) return KQ_ERR_ALIGN;
   }
   if (xf->pts) {
     if (xf->kind == KQ_XFORM_RPBH_32) return KQ_ERR_UNSUPPORTED;
@@ -160,15 +164,19 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   // MXFP4 goes through the matrix-core transforms (streaming for Kronecker / identity
   // without centring, row-staged for RPBH); the per-token Lloyd-Max format and centred
   // Kronecker / identity use the row-staged vector kernel.
-  // A dense P and power-of-two channel scaling run on the streaming matrix-core path
-  // only (MXFP4, no centring).
+  // A dense P, per-block factors and power-of-two channel scaling run on the matrix-core
+  // stream paths only (MXFP4, no centring).
   const bool mx = fmt == KQ_FMT_MXFP4;
   const bool stream_path = mx && !center && xf->kind != KQ_XFORM_RPBH_32;
   const bool rpbh_mfma = mx && xf->kind == KQ_XFORM_RPBH_32;
-  if ((xf->kind == KQ_XFORM_DENSE_32 || xf->pts) && !stream_path) return KQ_ERR_UNSUPPORTED;
+  if ((xf->kind == KQ_XFORM_DENSE_32 || xf->kind == KQ_XFORM_KRON_4X8_BLOCKS || xf->pts) && !stream_path)
+    return KQ_ERR_UNSUPPORTED;
   if (!stream_path && K > 16384) return KQ_ERR_UNSUPPORTED;
   hipError_t e;
-  if (stream_path) {
+  if (stream_path && xf->kind == KQ_XFORM_KRON_4X8_BLOCKS) {
+    e = launch_kron_blocks_mx(static_cast<const __half*>(X), M, K, xf->AB, xf->pts, codes,
+                              static_cast<uint8_t*>(scales), stream);
+  } else if (stream_path) {
     e = launch_kron_mx_mfma(xf->kind, static_cast<const __half*>(X), M * (K / 32), f, xf->P, xf->pts, K / 32,
                             codes, static_cast<uint8_t*>(scales), stream);
   } else if (rpbh_mfma) {
@@ -197,7 +205,8 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const vo
     if (!invert(xf->A, 4, finv.A) || !invert(xf->B, 8, finv.B)) return KQ_ERR_VALUE;
   }
   hipError_t e = launch_fold(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 2, static_cast<const __half*>(W), N, K, finv,
-                             xf->perm, xf->sign, xf->P, xf->pts, wcodes, wscales, stream);
+                             xf->perm, xf->sign, xf->kind == KQ_XFORM_KRON_4X8_BLOCKS ? xf->AB : xf->P, xf->pts,
+                             wcodes, wscales, stream);
   if (e != hipSuccess) return KQ_ERR_HIP;
   if (wbar) e = launch_colsum(static_cast<const __half*>(W), N, K, static_cast<__half*>(wbar), stream);
   return hip_status(e);

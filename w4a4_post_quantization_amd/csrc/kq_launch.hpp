@@ -23,13 +23,14 @@ struct LmTables {
 const LmTables& lm_tables();
 bool lloyd_max_levels(int n, double* out);
 
-// Kronecker transform + MXFP4 for a flat array of nblocks 32-element fp16 blocks.
-hipError_t launch_kron_mx_stream(const __half* X, int64_t nblocks, const KronFactors& f,
-                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // Matrix-core block transforms + MXFP4: streaming identity (kind 0), Kronecker (1) or
 // dense 32x32 P (3, device, row-major) without centring, and row-staged RPBH with
 // optional centring.
+// Per-block Kronecker factors AB (device float [K/32][80]: A then B, row-major, per block
+// index) + MXFP4 for X [M][K]; pts optional as below.
+hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
 // pts (optional, device int8 [nbk * 32]): per-channel power-of-two exponents applied first.
 hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
                                const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s);
@@ -44,7 +45,8 @@ hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int
 
 // Offline fold: W'^T rows = inverse transform of W^T rows, quantized along K.
 // fmt: 0 MXFP4, 2 LM2.  f holds the INVERSE factors for kind 1.
-// kind 3: P (device, row-major) is inverted on the device.  pts (optional): weight input
+// kind 3: P (device, row-major) is inverted on the device; kind 4: P is the per-block
+// factor table (float [K/32][80]) and each block's A (x) B is inverted on the device.  pts (optional): weight input
 // channel k is multiplied by 2^pts[k] before the inverse transform.
 hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
                        const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts, uint8_t* wcodes,

@@ -303,6 +303,29 @@ __device__ __forceinline__ MfmaXform mfma_xform_kron(const KronFactors& f, int l
   return x;
 }
 
+// The same fragments from one block's factors in device memory (ab = {A 4x4, B 8x8},
+// row-major): each lane reads only the two A and eight B entries its fragments use.
+__device__ __forceinline__ MfmaXform mfma_xform_kron_g(const float* __restrict__ ab, int lane) {
+  MfmaXform x;
+  const int q = lane >> 4, jl = lane & 15;
+  float a[2], b[8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) a[t] = ab[4 * q + 2 * t + (jl >> 3)];      // A[k >> 3][j >> 3], k = 8q + i
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = ab[16 + 8 * i + (jl & 7)];           // B[k & 7][j & 7]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float p = a[t] * b[i];
+      asm volatile("" : "+v"(p));                // see mfma_xform_kron
+      const _Float16 hi = (_Float16)p;
+      x.a[t][0][i] = hi;
+      x.a[t][1][i] = (_Float16)(p - (float)hi);
+    }
+  return x;
+}
+
 // The same fragments for a dense 32x32 P (row-major in device memory): P^T rows j, columns k.
 __device__ __forceinline__ MfmaXform mfma_xform_dense(const float* __restrict__ P, int lane) {
   MfmaXform x;
@@ -482,15 +505,16 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
 
 // Per-block Kronecker factors + MXFP4 on the matrix cores (KroQuant §02 with one (A, B)
 // pair per block index instead of one per layer).  The matrix-core step transforms 16
-// blocks that share one P, so here they are the same block index cb of 16 consecutive
-// token rows: a wavefront owns one cb and a run of 16-row groups, forms its P's fp16
-// hi + lo fragments once, and then streams the rows.  Lane (q, bl) loads 16 bytes of row
-// 16g + bl at channel 32 cb + 8q; the four wavefronts of a workgroup take consecutive
-// block indices, so together they read 256 contiguous bytes of each row.
+// blocks that share one P, so here they are the same block index of 16 consecutive token
+// rows.  A wavefront owns U consecutive block indices and a run of 16-row groups: it forms
+// the U fragment sets once, then per group loads, for each of its block indices, 16 bytes
+// per lane (lane (q, bl): row 16g + bl, channels 32 cb + 8q ..+7), G groups at a time.  The four wavefronts of
+// a workgroup take consecutive runs of block indices, so per row a workgroup reads 4U
+// consecutive blocks (2 KiB at U = 4) and writes their 256 code bytes as whole lines.
 // AB: float [nbk][80] per block index: A (16, row-major) then B (64, row-major).
 // PTS as in the streaming kernel; a wavefront's channels are fixed, so its exponents are
 // read once.
-template <int U, bool PTS>
+template <int U, int G, bool PTS>
 __global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __restrict__ X, int64_t M, int64_t nbk,
                                                              int64_t nseg, int64_t gps,
                                                              const float* __restrict__ AB,
@@ -499,41 +523,47 @@ __global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __rest
                                                              uint8_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15;
   const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= nbk * nseg) return;                          // whole wavefronts only
-  const int64_t cb = wave % nbk, seg = wave / nbk;
-  KronFactors f;
-  const float* ab = AB + cb * 80;
+  const int64_t nrun = (nbk + U - 1) / U;                  // runs of U block indices
+  if (wave >= nrun * nseg) return;                         // whole wavefronts only
+  const int64_t cb0 = (wave % nrun) * U, seg = wave / nrun;
+  MfmaXform xf[U];
+  uint2 ev[U];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) f.A[i] = ab[i];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) f.B[i] = ab[16 + i];
-  const MfmaXform xf = mfma_xform_kron(f, lane);
-  uint2 ev = make_uint2(0u, 0u);
-  if (PTS) ev = *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q);
+  for (int u = 0; u < U; ++u) {
+    const int64_t cb = cb0 + u < nbk ? cb0 + u : nbk - 1;  // a run past the end repeats the last
+    xf[u] = mfma_xform_kron_g(AB + cb * 80, lane);
+    ev[u] = PTS ? *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q) : make_uint2(0u, 0u);
+  }
   const int64_t ngroups = (M + 15) >> 4;
   const int64_t g0 = seg * gps, g1 = g0 + gps < ngroups ? g0 + gps : ngroups;
-  for (int64_t g = g0; g < g1; g += U) {
-    uint4 raw[U];
+  for (int64_t g = g0; g < g1; g += G) {               // G groups' loads in flight together
+    uint4 raw[G][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t row = (g + u) * 16 + bl;
-      raw[u] = (g + u < g1 && row < M) ? X[(row * nbk + cb) * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+    for (int h = 0; h < G; ++h) {
+      const int64_t row = (g + h) * 16 + bl;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        raw[h][u] = (g + h < g1 && row < M && cb0 + u < nbk) ? X[(row * nbk + cb0 + u) * 4 + q]
+                                                             : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (PTS) raw[u] = pts_scale8(raw[u], ev);
-      float y[8];
-      mfma_block_transform<true>(xf, __builtin_bit_cast(v8h, raw[u]), y);
+    for (int h = 0; h < G; ++h) {
+      const int64_t row = (g + h) * 16 + bl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] += 0.0f;      // an exact zero leaves as +0
-      uint32_t w, sb;
-      int off;
-      mx_pack_block(y, q, w, off, sb);
-      const int64_t row = (g + u) * 16 + bl;
-      if (g + u < g1 && row < M) {
-        const int64_t blk = row * nbk + cb;
-        *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
-        if (q == 0) scales[blk] = (uint8_t)sb;
+      for (int u = 0; u < U; ++u) {
+        if (PTS) raw[h][u] = pts_scale8(raw[h][u], ev[u]);
+        float y[8];
+        mfma_block_transform<true>(xf[u], __builtin_bit_cast(v8h, raw[h][u]), y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] += 0.0f;      // an exact zero leaves as +0
+        uint32_t w, sb;
+        int off;
+        mx_pack_block(y, q, w, off, sb);
+        if (g + h < g1 && row < M && cb0 + u < nbk) {
+          const int64_t blk = row * nbk + cb0 + u;
+          *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
+          if (q == 0) scales[blk] = (uint8_t)sb;
+        }
       }
     }
   }
@@ -828,26 +858,25 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
   return hipGetLastError();
 }
 
-// Per-block factors: nbk * nseg wavefronts, segment s of block index cb taking the 16-row
+// Per-block factors: ceil(nbk / U) * nseg wavefronts, segment s of a run taking the 16-row
 // groups [s gps, (s + 1) gps).  About eight workgroups per compute unit in total.
 hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  constexpr int U = 4;
-  const int64_t nbk = K / 32, ngroups = (M + 15) / 16;
+  constexpr int U = 4, G = 2;
+  const int64_t nbk = K / 32, nrun = (nbk + U - 1) / U, ngroups = (M + 15) / 16;
   const int64_t target = (int64_t)device_cu_count() * 8 * 4;
-  int64_t nseg = (target + nbk - 1) / nbk;
-  const int64_t cap = (ngroups + U - 1) / U;                // at least U groups per segment
-  if (nseg > cap) nseg = cap;
+  int64_t nseg = (target + nrun - 1) / nrun;
+  if (nseg > ngroups) nseg = ngroups;
   if (nseg < 1) nseg = 1;
   const int64_t gps = (ngroups + nseg - 1) / nseg;
   nseg = (ngroups + gps - 1) / gps;                        // no empty segment
-  const dim3 g((unsigned)((nbk * nseg + 3) / 4));
+  const dim3 g((unsigned)((nrun * nseg + 3) / 4));
   const uint4* Xv = reinterpret_cast<const uint4*>(X);
   if (pts)
-    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, true>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
+    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, G, true>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
                        scales);
   else
-    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, false>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
+    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, G, false>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
                        scales);
   return hipGetLastError();
 }
