@@ -263,6 +263,33 @@ def main():
                 variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
                                  "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
                 log(f"variant {name:>15} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
+            # the Kronecker transform and the rank-32 down-projection: two calls (X read
+            # twice) against the fused pass (X read once)
+            L1 = torch.from_numpy(np.ascontiguousarray(synth.weights(K, 64, CFG, 0, 32)[1])).to(dev)
+            T = torch.empty((M, 32), dtype=torch.float16, device=dev)
+            nbw = kq.lowrank_down_workspace_bytes(M, K, 32)
+            wsp = torch.empty((max(nbw, 16),), dtype=torch.uint8, device=dev)
+            tb = transform_bytes(M, K, False) + 2 * 32 * K + 2 * M * 32
+            for name in ("kron_4x8 then lowrank", "kron_4x8+lowrank fused"):
+                def run(i, name=name, K=K):
+                    Xi = Xsets[i % R][K]
+                    if name.endswith("fused"):
+                        kq.transform_quantize_lowrank(Xi, kx, L1, codes=codes, scales=scales, T=T, workspace=wsp)
+                    else:
+                        kq.transform_quantize(Xi, kx, fmt="mxfp4", codes=codes, scales=scales)
+                        kq.lowrank_down(Xi, L1, T=T, workspace=wsp)
+                run(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 20
+                a.record()
+                for i in range(n):
+                    run(i + 1)
+                b.record()
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / n
+                variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
+                                 "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
+                log(f"variant {name:>22} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s (X read once: algorithmic)")
 
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference

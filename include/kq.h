@@ -173,6 +173,19 @@ size_t kq_lowrank_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
 kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, int32_t r,
                           void* T, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The online activation path and the low-rank down-projection in one pass over X
+ * (SVDQuant explainer §3: the 16-bit branch and the 4-bit branch read the same input, and
+ * running the branch separately costs an extra read of it):
+ *   codes, scales = MXFP4 of x . P per 32-block (as kq_transform_quantize, fmt MXFP4, no
+ *                   centring; kinds NONE, KRON_4X8 and DENSE_32, no pts),
+ *   T = fp16(X L1^T) (as kq_lowrank_down).
+ * Shapes, layouts, alignment and the workspace rule are those of the two calls it
+ * replaces; kq_lowrank_down_workspace_bytes(M, K, r) gives the workspace size.  Codes may
+ * differ from kq_transform_quantize's only at rounding ties of the float32 transform. */
+kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64_t M, int64_t K,
+                                        uint8_t* codes, void* scales, const void* L1, int32_t r, void* T,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The 4-bit linear with its full-precision branches, one kernel:
  *   Y = Xq . Wq^T  +  T L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
  * fmt MXFP4: Xq, Wq MXFP4 (xscales u8 [M][K/32], wscales u8 [N][K/32]); products on

@@ -175,6 +175,33 @@ def test_lowrank_validation(lib):
     assert f(FAKE, FAKE, 4, 64, 32, FAKE, FAKE_ODD, 1024, None) == 3
 
 
+def test_transform_quantize_lowrank_validation(lib):
+    """The fused pass: both calls' argument rules, and only the streaming transform kinds
+    (no RPBH, no per-block factors, no power-of-two scaling)."""
+    f = lib.kq_transform_quantize_lowrank
+    xf = _xf()
+    args = lambda **kw: [kw.get("X", FAKE), kw.get("M", 4), kw.get("K", 64), kw.get("codes", FAKE), FAKE,
+                         kw.get("L1", FAKE), kw.get("r", 32), FAKE, kw.get("ws", None), kw.get("wn", 0), None]
+    assert f(ctypes.byref(xf), *args(X=None)) == 1
+    assert f(ctypes.byref(xf), *args(L1=None)) == 1
+    assert f(None, *args()) == 1
+    assert f(ctypes.byref(xf), *args(K=48)) == 2
+    assert f(ctypes.byref(xf), *args(r=8)) == 2
+    assert f(ctypes.byref(xf), *args(M=0)) == 2
+    assert f(ctypes.byref(xf), *args(codes=FAKE_ODD)) == 3
+    assert f(ctypes.byref(xf), *args(wn=1024)) == 1
+    assert f(ctypes.byref(xf), *args(ws=FAKE_ODD, wn=1024)) == 3
+    rp = _xf(kind=2)
+    rp.perm, rp.sign = 0x100000, 0x100000
+    assert f(ctypes.byref(rp), *args()) == 4
+    kb = _xf(kind=4)
+    kb.AB = 0x100000
+    assert f(ctypes.byref(kb), *args()) == 4
+    ps = _xf()
+    ps.pts = 0x100000
+    assert f(ctypes.byref(ps), *args()) == 4
+
+
 def test_lowrank_workspace_size(lib):
     """The split only pays for small M; the size is slices x M x r x 4 bytes, 0 when unsplit."""
     n = kq.lowrank_down_workspace_bytes(4608, 3072, 32)

@@ -1,0 +1,112 @@
+"""GPU parity of the fused pass (kq_transform_quantize_lowrank): one read of X gives the
+MXFP4 codes of the block-transformed activations and the low-rank down-projection T.
+
+Both outputs are checked against the oracle (codes with the tie rule, T against the fp64
+product within its float32 accumulation bound) and, bit for bit, against the two separate
+calls, which run the same arithmetic."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import linear, ties
+from tests import gpu_util
+from tests.test_gpu_transform import _dev_xform
+
+pytestmark = pytest.mark.gpu
+
+
+def _xf(kind, seed, K):
+    if kind == "kron":
+        A, B = synth.kron_factors(seed, 0)
+        return {"kind": "kron", "A": A, "B": B}
+    if kind == "dense":
+        return {"kind": "dense", "P": synth.dense_block(seed, 0)}
+    return {"kind": "none"}
+
+
+def _run(kq, X16, L1, xf):
+    import torch
+    X = torch.from_numpy(X16).cuda()
+    L = torch.from_numpy(np.ascontiguousarray(L1)).cuda()
+    dxf = _dev_xform(kq, torch, xf, X16.shape[1])
+    c, s, T = kq.transform_quantize_lowrank(X, dxf, L)
+    c2, s2, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
+    T2 = kq.lowrank_down(X, L)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (c, s, T, c2, s2, T2)]
+
+
+def _check_T(X16, L1, T, rows=None):
+    """Within one fp16 rounding of the exact product plus the float32 accumulation bound
+    (the rule of the separate down-projection's test)."""
+    K = X16.shape[1]
+    X = X16.astype(np.float64) if rows is None else X16[rows].astype(np.float64)
+    exact = X @ L1.astype(np.float64).T
+    bound = np.abs(X) @ np.abs(L1.astype(np.float64)).T
+    got = (T if rows is None else T[rows]).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -11 + ties.gamma_tau(K // 8 + 16, bound) + 2.0 ** -24)
+
+
+@pytest.mark.parametrize("kind", ["kron", "dense", "none"])
+@pytest.mark.parametrize("M,K,r", [(300, 1152, 32), (203, 160, 16), (7, 96, 64), (1000, 12288, 32), (64, 3072, 16)])
+def test_fused_matches_oracle_and_separate_calls(kq, kind, M, K, r):
+    X16 = synth.activations(M, K, 21, 2.0)
+    _, L1, _ = synth.weights(K, 64, 21, 0, r)
+    xf = _xf(kind, 21, K)
+    c, s, T, c2, s2, T2 = _run(kq, X16, L1, xf)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    assert np.array_equal(T.view(np.uint16), T2.view(np.uint16))
+    y, tau, _ = gpu_util.oracle_activation_reference(X16, xf, False)
+    gpu_util.assert_mx_parity(c, s, y, tau, label=f"fused {kind} M={M} K={K} r={r}")
+    _check_T(X16, L1, T)
+
+
+def test_fused_full_size_sampled_rows(kq):
+    """The FLUX-like width at full M (4608 x 3072, rank 32), Kronecker factors: sampled rows
+    against the oracle, all rows against the separate calls."""
+    M, K, r = 4608, 3072, 32
+    X16 = synth.activations(M, K, 22, 4.0)
+    _, L1, _ = synth.weights(K, 64, 22, 0, r)
+    xf = _xf("kron", 22, K)
+    c, s, T, c2, s2, T2 = _run(kq, X16, L1, xf)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    assert np.array_equal(T.view(np.uint16), T2.view(np.uint16))
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    y, tau, _ = gpu_util.oracle_activation_reference(X16[rows], xf, False)
+    gpu_util.assert_mx_parity(c[rows], s[rows], y, tau, label="fused full sampled")
+    _check_T(X16, L1, T, rows)
+
+
+def test_fused_linear(kq):
+    """The whole layer from the fused pass: Y = Xq Wq^T + T L2^T against the oracle on the
+    kernel's own packed operands."""
+    import torch
+    M, K, N, r = 300, 3072, 384, 32
+    X16 = synth.activations(M, K, 23, 2.0)
+    W16, L1, L2 = synth.weights(K, N, 23, 0, r)
+    xf = _xf("kron", 23, K)
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, T = kq.transform_quantize_lowrank(X, dxf, torch.from_numpy(L1).cuda())
+    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    torch.cuda.synchronize()
+    ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
+                             None, None)
+    err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+    print(f"fused linear rel frobenius {err:.3e}")
+    assert err <= 2e-3
+
+
+def test_fused_rejects_unsupported(kq):
+    import torch
+    X = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    L = torch.zeros((16, 64), dtype=torch.float16, device="cuda")
+    perm = torch.arange(64, dtype=torch.int32, device="cuda")
+    sign = torch.ones(64, dtype=torch.int8, device="cuda")
+    with pytest.raises(kq.KQError):
+        kq.transform_quantize_lowrank(X, kq.Xform.rpbh(perm, sign), L)
+    with pytest.raises(kq.KQError):
+        kq.transform_quantize_lowrank(X, kq.Xform.none(64).with_pts(torch.zeros(64, dtype=torch.int8, device="cuda")),
+                                      L)

@@ -69,6 +69,9 @@ def load():
     lib.kq_lowrank_down.argtypes = [vp, vp, i64, i64, i32, vp, vp, ctypes.c_size_t, vp]
     lib.kq_lowrank_down_workspace_bytes.restype = ctypes.c_size_t
     lib.kq_lowrank_down_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.kq_transform_quantize_lowrank.restype = i32
+    lib.kq_transform_quantize_lowrank.argtypes = [ctypes.POINTER(_XformC), vp, i64, i64, vp, vp, vp, i32, vp, vp,
+                                                  ctypes.c_size_t, vp]
     lib.kq_w4a4_linear.restype = i32
     lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib
@@ -288,6 +291,36 @@ def lowrank_down(X, L1, T=None, workspace=None, stream=None):
     if s != KQ_OK:
         raise KQError(s, "kq_lowrank_down")
     return T
+
+
+def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, workspace=None, stream=None):
+    """One pass over X: MXFP4 codes and scales of the block-transformed X (no centring)
+    and the low-rank down-projection T = fp16(X L1^T).  Returns (codes, scales, T)."""
+    torch = _torch()
+    _check(X, "X", torch.float16)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M, K]")
+    M, K = X.shape
+    r = L1.shape[0]
+    _check(L1, "L1", torch.float16, (r, K))
+    dev = X.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    _check(codes, "codes", torch.uint8, (M, K // 2))
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+    _check(scales, "scales", torch.uint8, (M, K // 32))
+    T = torch.empty((M, r), dtype=torch.float16, device=dev) if T is None else T
+    _check(T, "T", torch.float16, (M, r))
+    if workspace is None:
+        nb = lowrank_down_workspace_bytes(M, K, r)
+        workspace = torch.empty((nb,), dtype=torch.uint8, device=dev) if nb else None
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
+    wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    s = load().kq_transform_quantize_lowrank(xform.c(), _ptr(X), M, K, _ptr(codes), _ptr(scales), _ptr(L1), r,
+                                             _ptr(T), wp, wn, _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_transform_quantize_lowrank")
+    return codes, scales, T
 
 
 def w4a4_linear(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar=None,

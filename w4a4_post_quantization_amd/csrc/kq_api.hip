@@ -231,6 +231,30 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
                                         workspace ? workspace_bytes : 0, stream));
 }
 
+kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64_t M, int64_t K, uint8_t* codes,
+                                        void* scales, const void* L1, int32_t r, void* T, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !codes || !scales || !L1 || !T) return KQ_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  kq_status st = check_xform(xf, K);
+  if (st != KQ_OK) return st;
+  if (xf->kind != KQ_XFORM_NONE && xf->kind != KQ_XFORM_KRON_4X8 && xf->kind != KQ_XFORM_DENSE_32)
+    return KQ_ERR_UNSUPPORTED;
+  if (xf->pts) return KQ_ERR_UNSUPPORTED;
+  if (M > (1LL << 31) - 64 || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
+  if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16) || !aligned(codes, 16)) return KQ_ERR_ALIGN;
+  if (workspace_bytes && !workspace) return KQ_ERR_NULL;
+  if (workspace && !aligned(workspace, 16)) return KQ_ERR_ALIGN;
+  KronFactors f;
+  std::memcpy(f.A, xf->A, sizeof f.A);
+  std::memcpy(f.B, xf->B, sizeof f.B);
+  return hip_status(launch_lowrank_xform_mx(xf->kind, static_cast<const __half*>(X), static_cast<const __half*>(L1),
+                                            M, K, r, static_cast<__half*>(T), static_cast<float*>(workspace),
+                                            workspace ? workspace_bytes : 0, f, xf->P, codes,
+                                            static_cast<uint8_t*>(scales), stream));
+}
+
 kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
                          const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
                          int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {

@@ -58,6 +58,11 @@ hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hi
 size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r);
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r,
                                __half* T, float* part, size_t part_bytes, hipStream_t s);
+// The same down-projection fused with the block transform (kind 0 identity, 1 Kronecker,
+// 3 dense P) and MXFP4 of X (codes [M][K/2], scales [M][K/32]): X is read once.
+hipError_t launch_lowrank_xform_mx(int kind, const __half* X, const __half* L1, int64_t M, int64_t K, int r,
+                                   __half* T, float* part, size_t part_bytes, const KronFactors& fk, const float* P,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // Y = Xq Wq^T (+ T L2^T) (+ mu wbar^T), MXFP4 x MXFP4.
 hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,

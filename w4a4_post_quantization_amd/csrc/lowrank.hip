@@ -13,8 +13,16 @@
 //     second, small kernel sums them in slice order (deterministic) and stores T.  (Summing them in the
 //     last workgroup to finish a row block would need device-scope fences, which on this
 //     chip write back and invalidate the whole L2 of the compute die: far slower.)
+//
+// The same kernel can also quantize what it streams (XK >= 0): the A fragment of each
+// 32-wide step is, lane for lane, the B operand of the matrix-core block transform (16
+// rows of one block index as the 16 blocks), so the chunk in LDS is transformed and
+// packed to MXFP4 as well, and X is read once for both (SVDQuant explainer §3: the
+// down-projection shares its input with the 4-bit branch).  XK: -1 none, 0 identity,
+// 1 Kronecker A (x) B, 3 dense P; MXFP4 without centring.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
+#include "kq_mfma_xform.hpp"
 
 #include <algorithm>
 
@@ -36,11 +44,14 @@ struct LrCfg {
   static constexpr int LPW = 4 + RR / 16;               // load instructions per wave per chunk
 };
 
-template <int RR, int NS>
+template <int RR, int NS, int XK>
 __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restrict__ X,
                                                            const __half* __restrict__ L1, int M, int K,
                                                            int slices, int cps, float* __restrict__ part,
-                                                           __half* __restrict__ T) {
+                                                           __half* __restrict__ T, KronFactors fk,
+                                                           const float* __restrict__ P,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
   using C = LrCfg<RR, NS>;
   __shared__ __align__(16) uint8_t lds[C::LDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -91,6 +102,19 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
   v4f acc[C::RT];
 #pragma unroll
   for (int t = 0; t < C::RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  MfmaXform xf;
+  if (XK == 1) xf = mfma_xform_kron(fk, lane);
+  else if (XK == 3) xf = mfma_xform_dense(P, lane);
+  else if (XK == 0) {   // identity: P^T rows are unit vectors
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xf.a[t][0][i] = (16 * t + (lane & 15) == 8 * (lane >> 4) + i) ? (_Float16)1.0f : (_Float16)0.0f;
+        xf.a[t][1][i] = (_Float16)0.0f;
+      }
+  }
+  const int nbk = K >> 5;
 
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) issue(p);
@@ -110,6 +134,21 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
         const int n = 16 * t + (lane & 15);
         const v8h b = *reinterpret_cast<const v8h*>(st + C::X_BYTES + n * 256 + 16 * lr_slot(n, piece));
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+      }
+      if (XK >= 0) {                 // block (c0 + f) * 4 + s of rows m0 + 16 w + lane % 16
+        float y[8];
+        mfma_block_transform<(XK > 0)>(xf, a, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] += 0.0f;    // an exact zero leaves as +0
+        uint32_t wd, sb;
+        int off;
+        mx_pack_block(y, lane >> 4, wd, off, sb);
+        const int kb = (c0 + f) * 4 + s;
+        if (kb < nbk && m0 + arow < M) {
+          const int64_t blk = (int64_t)(m0 + arow) * nbk + kb;
+          *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = wd;
+          if ((lane >> 4) == 0) scales[blk] = (uint8_t)sb;
+        }
       }
     }
   }
@@ -163,16 +202,17 @@ size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r) {
   return s > 1 ? (size_t)s * (size_t)M * (size_t)r * 4 : 0;
 }
 
-template <int RR>
+template <int RR, int XK>
 static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, __half* T, float* part,
-                                 hipStream_t s, int slices) {
+                                 hipStream_t s, int slices, const KronFactors& fk, const float* P, uint8_t* codes,
+                                 uint8_t* scales) {
   constexpr int NS = RR == 64 ? 2 : 3;
   const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
   const int64_t nch = (K + LR_KC - 1) / LR_KC;
   const int cps = (int)((nch + slices - 1) / slices);
   slices = (int)((nch + cps - 1) / cps);                     // no empty slice (never more)
-  hipLaunchKernelGGL((lowrank_down_kernel<RR, NS>), dim3((unsigned)(blocks * slices)), dim3(256), 0, s, X, L1,
-                     (int)M, (int)K, slices, cps, part, T);
+  hipLaunchKernelGGL((lowrank_down_kernel<RR, NS, XK>), dim3((unsigned)(blocks * slices)), dim3(256), 0, s, X, L1,
+                     (int)M, (int)K, slices, cps, part, T, fk, P, codes, scales);
   if (slices > 1) {
     const int64_t threads = M * RR / 4;
     hipLaunchKernelGGL((lowrank_reduce_kernel<RR>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
@@ -181,15 +221,32 @@ static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, i
   return hipGetLastError();
 }
 
+template <int XK>
+static hipError_t lowrank_rank(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T, float* part,
+                               hipStream_t s, int slices, const KronFactors& fk, const float* P, uint8_t* codes,
+                               uint8_t* scales) {
+  switch (r) {
+    case 16: return lowrank_launch<16, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
+    case 32: return lowrank_launch<32, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
+    case 64: return lowrank_launch<64, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r, __half* T,
                                float* part, size_t part_bytes, hipStream_t s) {
   const int slices = part ? lr_slices(M, K, r, part_bytes) : 1;
-  switch (r) {
-    case 16: return lowrank_launch<16>(X, L1, M, K, T, part, s, slices);
-    case 32: return lowrank_launch<32>(X, L1, M, K, T, part, s, slices);
-    case 64: return lowrank_launch<64>(X, L1, M, K, T, part, s, slices);
-    default: return hipErrorInvalidValue;
-  }
+  const KronFactors none{};
+  return lowrank_rank<-1>(X, L1, M, K, r, T, part, s, slices, none, nullptr, nullptr, nullptr);
+}
+
+hipError_t launch_lowrank_xform_mx(int kind, const __half* X, const __half* L1, int64_t M, int64_t K, int r,
+                                   __half* T, float* part, size_t part_bytes, const KronFactors& fk, const float* P,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int slices = part ? lr_slices(M, K, r, part_bytes) : 1;
+  if (kind == 1) return lowrank_rank<1>(X, L1, M, K, r, T, part, s, slices, fk, P, codes, scales);
+  if (kind == 3) return lowrank_rank<3>(X, L1, M, K, r, T, part, s, slices, fk, P, codes, scales);
+  return lowrank_rank<0>(X, L1, M, K, r, T, part, s, slices, fk, P, codes, scales);
 }
 
 }  // namespace kq
