@@ -186,6 +186,27 @@ kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64
                                         uint8_t* codes, void* scales, const void* L1, int32_t r, void* T,
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Offline rank-r extraction of the 16-bit branch (SVDQuant explainer §3: the weight's
+ * leading singular directions stay in 16 bits, the residual is quantized to 4 bits):
+ *   W (fp16 [N][K], row n = output n) ~ L2 L1 with L2 = U_r S_r^1/2 (fp16 [N][r]),
+ *   L1 = S_r^1/2 V_r^T (fp16 [r][K]) from the r leading singular triplets, and
+ *   R = fp16(W - L2 L1) (fp16 [N][K]) computed with the fp16 factors, to be folded and
+ *   quantized in place of W (kq_fold_inverse_into_weights; its wbar is then 1^T R).
+ *   sigma (optional, float [r]): the singular value estimates, descending.
+ * The subspace comes from randomized subspace iteration (Halko, Martinsson and Tropp 2011,
+ * algorithms 4.4 / 5.1) started from the caller's omega (float32 [K][l], e.g. Gaussian;
+ * the library draws no random numbers) with l - r extra columns and `iters` power steps,
+ * re-orthonormalized after every product; float32 products, float64 for the l x l parts.
+ * Accuracy depends on the gap between sigma_r and sigma_{l+1} and on iters.
+ * r in {16, 32, 64}; r < l <= 96, l <= min(N, K); 0 <= iters <= 16; K % 32 == 0.
+ * workspace: caller-owned device memory of kq_svd_lowrank_workspace_bytes(N, K, r, l)
+ * bytes, 256-byte aligned; other pointers 16-byte aligned (sigma 4).  Runs several kernels
+ * on `stream`; calls sharing a workspace must not overlap. */
+size_t kq_svd_lowrank_workspace_bytes(int64_t N, int64_t K, int32_t r, int32_t l);
+kq_status kq_svd_lowrank(const void* W, int64_t N, int64_t K, int32_t r, const float* omega, int32_t l,
+                         int32_t iters, void* L1, void* L2, void* R, float* sigma, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* The 4-bit linear with its full-precision branches, one kernel:
  *   Y = Xq . Wq^T  +  T L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
  * fmt MXFP4: Xq, Wq MXFP4 (xscales u8 [M][K/32], wscales u8 [N][K/32]); products on

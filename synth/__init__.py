@@ -21,7 +21,10 @@ SANA, FLUX.1 and CogVideoX, which are not available):
   outlier channels of the activations and 0 elsewhere (the channels the scaling is
   meant for), or, to exercise every exponent, uniform integers in 0..15;
 * weights W ~ N(0, 1/K), low-rank factors L1 ~ N(0, 1/K), L2 ~ N(0, 1/K), fp16,
-  in the [out][in] layout: W as [N][K], L1 as [r][K], L2 as [N][r].
+  in the [out][in] layout: W as [N][K], L1 as [r][K], L2 as [N][r];
+* for the low-rank extraction: W = N(0, 1/K) plus r planted directions whose strengths
+  fall geometrically from 16 to 4 times the bulk's spectral edge, and a Gaussian
+  starting block for the subspace iteration;
 
 Every stream comes from numpy's PCG64 seeded by a SeedSequence of
 (config seed, stream tag, sizes), so any piece can be drawn on its own.
@@ -56,7 +59,8 @@ CONFIGS = {
 N_OUTLIERS = 12
 OUTLIER_SCALE = 50.0
 
-_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE, _TAG_PTS, _TAG_KRON_BLOCKS = 1, 2, 3, 4, 5, 6, 7
+(_TAG_ACT, _TAG_KRON, _TAG_RPBH, _TAG_W, _TAG_DENSE, _TAG_PTS, _TAG_KRON_BLOCKS, _TAG_LOWRANK_W,
+ _TAG_OMEGA) = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def _rng(*key):
@@ -148,6 +152,25 @@ def weights(K, N, seed, layer, rank=32):
     L1 = rng.normal(0.0, sd, size=(rank, K)).astype(np.float16)
     L2 = rng.normal(0.0, sd, size=(N, rank)).astype(np.float16)
     return W, L1, L2
+
+
+def planted_lowrank_weights(K, N, seed, layer, r, top=16.0, bottom=4.0):
+    """fp16 Wt [N][K] = G + U diag(s) V^T: G ~ N(0, 1/K) and r planted directions (U, V
+    with orthonormal columns from QR of Gaussians) whose strengths fall geometrically from
+    `top` to `bottom` times the bulk's spectral edge 1 + sqrt(N / K) -- weights whose
+    leading singular directions stand out, as the low-rank branch assumes."""
+    rng = _rng(seed, _TAG_LOWRANK_W, layer, K, N, r)
+    G = rng.normal(0.0, 1.0 / np.sqrt(K), size=(N, K))
+    U, _ = np.linalg.qr(rng.standard_normal((N, r)))
+    V, _ = np.linalg.qr(rng.standard_normal((K, r)))
+    edge = 1.0 + np.sqrt(N / K)
+    s = edge * np.geomspace(top, bottom, r)
+    return (G + (U * s[None, :]) @ V.T).astype(np.float16)
+
+
+def gaussian_block(K, l, seed):
+    """float32 [K][l] of N(0, 1): the starting block of randomized subspace iteration."""
+    return _rng(seed, _TAG_OMEGA, K, l).standard_normal((K, l)).astype(np.float32)
 
 
 def xform_for(cfg_idx, layer, K):

@@ -202,6 +202,27 @@ def test_transform_quantize_lowrank_validation(lib):
     assert f(ctypes.byref(ps), *args()) == 4
 
 
+def test_svd_lowrank_validation(lib):
+    """Offline extraction: pointers, ranks, the oversampled width l, power steps, and a
+    workspace of at least the reported size, 256-byte aligned."""
+    f, wb = lib.kq_svd_lowrank, lib.kq_svd_lowrank_workspace_bytes
+    need = wb(64, 96, 16, 24)
+    assert need > 0 and wb(64, 96, 16, 16) == 0 and wb(64, 96, 8, 24) == 0
+    big = need + 1024
+    args = lambda **kw: [kw.get("W", FAKE), 64, kw.get("K", 96), kw.get("r", 16), FAKE, kw.get("l", 24),
+                         kw.get("it", 4), FAKE, FAKE, FAKE, None, kw.get("ws", FAKE), kw.get("wn", big), None]
+    assert f(*args(W=None)) == 1
+    assert f(*args(ws=None)) == 1
+    assert f(*args(r=8)) == 2
+    assert f(*args(l=16)) == 2
+    assert f(*args(l=97)) == 2
+    assert f(*args(l=100, K=128)) == 2
+    assert f(*args(it=17)) == 2
+    assert f(*args(K=80)) == 2
+    assert f(*args(wn=need - 1)) == 2
+    assert f(*args(ws=ctypes.c_void_p(0x100010))) == 3
+
+
 def test_lowrank_workspace_size(lib):
     """The split only pays for small M; the size is slices x M x r x 4 bytes, 0 when unsplit."""
     n = kq.lowrank_down_workspace_bytes(4608, 3072, 32)

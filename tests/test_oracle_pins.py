@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from oracle import linear, lloyd_max, mxfp4, pipeline, ties, transforms
+from oracle import linear, lloyd_max, mxfp4, pipeline, svd, ties, transforms
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -361,6 +361,61 @@ def test_pts_zero_exponents_change_nothing():
     assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
     with pytest.raises(ValueError):
         pipeline.transform_quantize(X, {"kind": "none", "pts": np.zeros(64)}, center=True)
+
+
+# ---------------------------------------------------------------- low-rank extraction
+
+def _haar_np(rng, n, k):
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def test_svd_lowrank_recovers_a_known_spectrum():
+    """Wt = U diag(s) V^T built from orthonormal U, V and distinct s: the rank-r part is
+    U_r diag(s_r) V_r^T, the singular values are s, the residual's squared norm is the
+    sum of the dropped s_i^2 (Eckart-Young), and the split is even:
+    L2^T L2 = L1 L1^T = diag(s_r)."""
+    rng = np.random.default_rng(40)
+    N, K, r = 48, 80, 6
+    U, V = _haar_np(rng, N, N), _haar_np(rng, K, N)
+    s_true = np.sort(rng.uniform(0.1, 10.0, N))[::-1]
+    Wt = (U * s_true[None, :]) @ V.T
+    L1, L2, s = svd.svd_lowrank_f64(Wt, r)
+    assert np.allclose(s, s_true, rtol=1e-12, atol=1e-12)
+    best = (U[:, :r] * s_true[None, :r]) @ V[:, :r].T
+    assert np.linalg.norm(L2 @ L1 - best) <= 1e-11 * np.linalg.norm(best)
+    resid = np.linalg.norm(Wt - L2 @ L1) ** 2
+    assert abs(resid - np.sum(s_true[r:] ** 2)) <= 1e-10 * np.sum(s_true ** 2)
+    assert np.allclose(L2.T @ L2, np.diag(s_true[:r]), atol=1e-11)
+    assert np.allclose(L1 @ L1.T, np.diag(s_true[:r]), atol=1e-11)
+
+
+def test_svd_rank_one_matches_power_iteration():
+    """Rank 1 of a small matrix against the textbook power iteration on Wt^T Wt, written
+    here: the leading right singular vector and value agree."""
+    rng = np.random.default_rng(41)
+    Wt = rng.standard_normal((5, 7))
+    v = np.ones(7)
+    for _ in range(2000):
+        v = Wt.T @ (Wt @ v)
+        v /= np.linalg.norm(v)
+    sigma = np.linalg.norm(Wt @ v)
+    L1, L2, s = svd.svd_lowrank_f64(Wt, 1)
+    assert abs(s[0] - sigma) <= 1e-12 * sigma
+    assert np.allclose(L2 @ L1, np.outer(Wt @ v, v), atol=1e-10)
+
+
+def test_svd_residual_uses_the_fp16_factors():
+    """R is formed with the fp16 factors the branch will use: R64 + L2_16 L1_16 = Wt
+    (float64, exact up to the final subtraction's rounding) and R is R64 rounded to fp16."""
+    import synth
+    Wt = synth.planted_lowrank_weights(96, 64, 3, 0, 8)
+    out = svd.svd_lowrank(Wt, 8)
+    back = out["R64"] + out["L2"].astype(np.float64) @ out["L1"].astype(np.float64)
+    assert np.allclose(back, Wt.astype(np.float64), rtol=0, atol=1e-12)
+    assert np.array_equal(out["R"], out["R64"].astype(np.float16))
+    # the planted directions dominate: the residual is the bulk, far below W
+    assert np.linalg.norm(out["R64"]) < 0.2 * np.linalg.norm(Wt.astype(np.float64))
 
 
 # ---------------------------------------------------------------- P6: centring + rank-1

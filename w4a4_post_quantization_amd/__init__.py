@@ -72,6 +72,10 @@ def load():
     lib.kq_transform_quantize_lowrank.restype = i32
     lib.kq_transform_quantize_lowrank.argtypes = [ctypes.POINTER(_XformC), vp, i64, i64, vp, vp, vp, i32, vp, vp,
                                                   ctypes.c_size_t, vp]
+    lib.kq_svd_lowrank_workspace_bytes.restype = ctypes.c_size_t
+    lib.kq_svd_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.kq_svd_lowrank.restype = i32
+    lib.kq_svd_lowrank.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kq_w4a4_linear.restype = i32
     lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib
@@ -321,6 +325,40 @@ def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, wo
     if s != KQ_OK:
         raise KQError(s, "kq_transform_quantize_lowrank")
     return codes, scales, T
+
+
+def svd_lowrank_workspace_bytes(N, K, r, l):
+    return int(load().kq_svd_lowrank_workspace_bytes(N, K, r, l))
+
+
+def svd_lowrank(W, r, omega, iters=4, L1=None, L2=None, R=None, sigma=None, workspace=None, stream=None):
+    """Offline rank-r extraction: W (fp16 [N][K]) ~ L2 L1 + R.  omega: float32 [K][l]
+    device starting block (l > r).  Returns (L1 [r][K], L2 [N][r], R [N][K], sigma [r])."""
+    torch = _torch()
+    _check(W, "W", torch.float16)
+    N, K = W.shape
+    _check(omega, "omega", torch.float32)
+    if omega.dim() != 2 or omega.shape[0] != K:
+        raise ValueError("omega must be [K, l]")
+    l = omega.shape[1]
+    dev = W.device
+    L1 = torch.empty((r, K), dtype=torch.float16, device=dev) if L1 is None else L1
+    L2 = torch.empty((N, r), dtype=torch.float16, device=dev) if L2 is None else L2
+    R = torch.empty((N, K), dtype=torch.float16, device=dev) if R is None else R
+    sigma = torch.empty((r,), dtype=torch.float32, device=dev) if sigma is None else sigma
+    _check(L1, "L1", torch.float16, (r, K))
+    _check(L2, "L2", torch.float16, (N, r))
+    _check(R, "R", torch.float16, (N, K))
+    _check(sigma, "sigma", torch.float32, (r,))
+    nb = svd_lowrank_workspace_bytes(N, K, r, l)
+    if workspace is None:
+        workspace = torch.empty((max(nb, 256),), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8)
+    s = load().kq_svd_lowrank(_ptr(W), N, K, r, _ptr(omega), l, int(iters), _ptr(L1), _ptr(L2), _ptr(R),
+                              _ptr(sigma), _ptr(workspace), workspace.numel(), _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_svd_lowrank")
+    return L1, L2, R, sigma
 
 
 def w4a4_linear(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar=None,

@@ -255,6 +255,28 @@ kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64
                                             static_cast<uint8_t*>(scales), stream));
 }
 
+size_t kq_svd_lowrank_workspace_bytes(int64_t N, int64_t K, int32_t r, int32_t l) {
+  if (N < 1 || K < 32 || K % 32 != 0 || (r != 16 && r != 32 && r != 64) || l <= r || l > 96) return 0;
+  return svd_workspace_bytes(N, K, l, r);
+}
+
+kq_status kq_svd_lowrank(const void* W, int64_t N, int64_t K, int32_t r, const float* omega, int32_t l,
+                         int32_t iters, void* L1, void* L2, void* R, float* sigma, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!W || !omega || !L1 || !L2 || !R || !workspace) return KQ_ERR_NULL;
+  if (N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if (l <= r || l > 96 || l > N || l > K || iters < 0 || iters > 16) return KQ_ERR_SHAPE;
+  if (N > (1LL << 20) || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
+  if (workspace_bytes < svd_workspace_bytes(N, K, l, r)) return KQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(omega, 16) || !aligned(L1, 16) || !aligned(L2, 16) || !aligned(R, 16) ||
+      !aligned(workspace, 256) || (sigma && !aligned(sigma, 4)))
+    return KQ_ERR_ALIGN;
+  return hip_status(launch_svd_lowrank(static_cast<const __half*>(W), N, K, r, omega, l, iters,
+                                       static_cast<__half*>(L1), static_cast<__half*>(L2), static_cast<__half*>(R),
+                                       sigma, workspace, stream));
+}
+
 kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
                          const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
                          int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {

@@ -65,6 +65,13 @@ hipError_t launch_lowrank_xform_mx(int kind, const __half* X, const __half* L1, 
                                    uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // Y = Xq Wq^T (+ T L2^T) (+ mu wbar^T), MXFP4 x MXFP4.
+// Offline rank-r extraction: Wt [N][K] fp16 -> L1 [r][K], L2 [N][r], R = fp16(Wt - L2 L1)
+// [N][K] (fp16), sigma [r] (optional); omega [K][l] float32 starting block; workspace of
+// svd_workspace_bytes(N, K, l, r) bytes, 256-byte aligned.
+size_t svd_workspace_bytes(int64_t N, int64_t K, int l, int r);
+hipError_t launch_svd_lowrank(const __half* Wt, int64_t N, int64_t K, int r, const float* omega, int l, int iters,
+                              __half* L1, __half* L2, __half* R, float* sigma, void* workspace, hipStream_t s);
+
 hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,
                             const uint8_t* wcodes, const uint8_t* wscales, int64_t N,
                             const __half* T, const __half* L2, int r, const __half* mu,
