@@ -49,7 +49,8 @@ def _check_T(X16, L1, T, rows=None):
 
 
 @pytest.mark.parametrize("kind", ["kron", "dense", "none"])
-@pytest.mark.parametrize("M,K,r", [(300, 1152, 32), (203, 160, 16), (7, 96, 64), (1000, 12288, 32), (64, 3072, 16)])
+@pytest.mark.parametrize("M,K,r", [(300, 1152, 32), (203, 160, 16), (7, 96, 64), (1000, 12288, 32), (64, 3072, 16),
+                                   (1, 32, 16), (65, 32, 32)])
 def test_fused_matches_oracle_and_separate_calls(kq, kind, M, K, r):
     X16 = synth.activations(M, K, 21, 2.0)
     _, L1, _ = synth.weights(K, 64, 21, 0, r)

@@ -98,7 +98,7 @@ def test_dense_block_rejects_unsupported(kq):
 
 @pytest.mark.parametrize("kind", ["kron", "dense", "none"])
 @pytest.mark.parametrize("K,rows,which", [(3072, 203, "outliers"), (1152, 150, "random"), (96, 7, "random"),
-                                          (12288, 37, "outliers")])
+                                          (12288, 37, "outliers"), (32, 1, "random")])
 def test_mxfp4_pts_matches_oracle(kq, kind, K, rows, which):
     """DMQ's power-of-two channel scaling ahead of the block transform: exponents 6 on the
     planted outlier channels, or uniform 0..15 on every channel (many fp16 subnormal
@@ -115,7 +115,8 @@ def test_mxfp4_pts_matches_oracle(kq, kind, K, rows, which):
 
 
 @pytest.mark.parametrize("K,rows,pts", [(3072, 203, False), (1152, 150, False), (96, 7, False), (12288, 37, False),
-                                        (64, 1, False), (1152, 150, True), (3072, 48, True)])
+                                        (64, 1, False), (32, 17, False), (1152, 150, True), (3072, 48, True),
+                                        (32, 3, True)])
 def test_mxfp4_kron_blocks_matches_oracle(kq, K, rows, pts):
     """Per-block Kronecker factors (one (A_b, B_b) per block index) on the matrix-core
     kernel that holds one block index per wavefront; ragged row counts, one row, and
