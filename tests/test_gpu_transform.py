@@ -234,7 +234,16 @@ def test_lm4_zero_row(kq):
     assert s[2] == 0 and np.all(codes[2] == 0)
 
 
-@pytest.mark.parametrize("cfg,layer", [(3, 0), (4, 0)])
+@pytest.mark.parametrize("K,rows", [(6144, 9), (6176, 9), (16384, 5)])
+def test_rpbh_centred_row_group_widths(kq, K, rows):
+    """The row-group kernel stages four rows per group up to K = 6144 and two above: both
+    sides of the switch and the widest row, centred, odd row counts."""
+    X16 = synth.activations(rows, K, 24, 4.0)
+    perm, sign = synth.rpbh_params(K, 24, 0)
+    _mx_check(kq, X16, {"kind": "rpbh", "perm": perm, "sign": sign}, True, f"rpbh centred K={K} M={rows}")
+
+
+@pytest.mark.parametrize("cfg,layer", [(3, 0), (3, 2), (4, 0)])
 def test_full_size_sampled_rows(kq, cfg, layer):
     """Full workload size in the launch configuration of the bench; parity on sampled rows
     (rows are independent)."""
