@@ -16,7 +16,10 @@
  *     arXiv abstract: centre each token before the rotation, restore the mean
  *     exactly through a rank-1 full-precision branch; closed-form per-token scale.
  *   - SVDQuant explainer, §3: a 16-bit low-rank branch L1 L2 added to the 4-bit
- *     product, fused into the 4-bit kernel so it costs no separate pass.
+ *     product, fused into the 4-bit kernel so it costs no separate pass; the branch
+ *     holds the weight's leading singular directions, the residual is quantized.
+ *   - DMQ explainer: channel-wise power-of-two scaling of outlier channels, a bit
+ *     shift, as an optional step ahead of the transform.
  *
  * Layouts (all row-major, contiguous, device memory unless stated):
  *   X     fp16 [M][K]           activations, K a multiple of 32
@@ -34,13 +37,14 @@
  *
  * Ownership: the caller allocates and owns every buffer; the library never
  * allocates, frees or caches device memory, and holds no per-call state (it is
- * re-entrant).  Descriptor contents (kind, K, A, B) travel by value; perm/sign are
- * caller-owned device arrays.  Every call is asynchronous on `stream` (0 = the
+ * re-entrant).  Descriptor contents (kind, K, A, B) travel by value; perm, sign, P,
+ * AB and pts are caller-owned device arrays.  Every call is asynchronous on `stream` (0 = the
  * null stream); inputs must stay alive until the stream has passed the call.
  *
  * Errors: the return value is a status.  Arguments are validated on the host
  * before anything is launched; a non-zero status means nothing was enqueued
- * (KQ_ERR_HIP: the launch itself failed, reported by hipGetLastError).  Faults
+ * (KQ_ERR_HIP: a launch itself failed, reported by hipGetLastError; in a call that
+ * launches several kernels, those before the failing one may have been enqueued).  Faults
  * inside kernels surface at the caller's next synchronisation, as HIP defines.
  */
 #ifndef KQ_H
