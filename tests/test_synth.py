@@ -61,3 +61,30 @@ def test_config_table_matches_workloads():
     assert c[3]["M"] == 4608 and c[4]["M"] == 17550
     assert [l[1:] for l in c[3]["layers"]] == [(3072, 9216), (3072, 12288), (12288, 3072)]
     assert c[3]["center"] and c[3]["xform"] == "rpbh" and c[2]["fmt"] == "lm4"
+
+
+def test_outlier_channels_are_the_scaled_ones():
+    """outlier_channels replays the activations' draw: exactly the channels with the large
+    spread, and the power-of-two exponents land on them."""
+    M, K = 512, 384
+    X = synth.activations(M, K, seed=5, sigma_mu=2.0).astype(np.float64)
+    ch = synth.outlier_channels(M, K, seed=5, sigma_mu=2.0)
+    assert np.array_equal(np.sort(np.argsort(X.std(axis=0))[-12:]), ch)
+    e = synth.pts_exponents(K, ch)
+    assert e.dtype == np.int8 and np.all(e[ch] == 6) and np.count_nonzero(e) == 12
+    r = synth.pts_exponents(K, seed=9)
+    assert r.min() >= 0 and r.max() <= 15 and np.array_equal(r, synth.pts_exponents(K, seed=9))
+
+
+def test_block_factors_and_planted_weights():
+    A, B = synth.kron_block_factors(1, 0, 6)
+    assert A.shape == (6, 4, 4) and B.shape == (6, 8, 8) and not np.array_equal(A[0], A[1])
+    for a in A.astype(np.float64):                  # Haar times positive column scales
+        q = a / np.linalg.norm(a, axis=0)[None, :]
+        assert np.allclose(q.T @ q, np.eye(4), atol=1e-5)
+    W = synth.planted_lowrank_weights(512, 128, 2, 0, 8).astype(np.float64)
+    s = np.linalg.svd(W, compute_uv=False)
+    edge = 1.0 + np.sqrt(128 / 512)
+    assert s[7] > 3.0 * edge and s[8] < 1.3 * edge   # the planted directions stand out of the bulk
+    om = synth.gaussian_block(96, 24, 3)
+    assert om.shape == (96, 24) and om.dtype == np.float32 and abs(om.std() - 1.0) < 0.05
