@@ -303,8 +303,11 @@ def _check_lowrank(kq, M, K, r, seed=7, workspace="default"):
 
 
 @pytest.mark.parametrize("M,K,r", [(1, 128, 32), (77, 1152, 16), (301, 3072, 32), (40, 12288, 64), (19, 2240, 32),
-                                   (1000, 3072, 64), (4608, 3072, 16), (4608, 12288, 32)])
+                                   (1000, 3072, 64), (4608, 3072, 16), (4608, 12288, 32), (4096, 3072, 64),
+                                   (4103, 96, 32), (17550, 3072, 32)])
 def test_lowrank_down_matches_oracle(kq, M, K, r):
+    """Ranks 16, 32, 64; one row to the video workload's 17550 rows; K from 96 (one
+    partial chunk) to 12288; ragged last row blocks."""
     _check_lowrank(kq, M, K, r)
 
 
@@ -321,8 +324,8 @@ def test_lowrank_down_workspace_sizes(kq):
 
 
 def test_lowrank_down_repeated_calls(kq):
-    """Split-K calls in a row with different shapes: each call leaves the per-row-block
-    arrival counters at zero for the next."""
+    """Split-K calls in a row with different shapes sharing the default workspaces: each
+    call's partial sums are complete before the next call overwrites them."""
     for i, (M, K, r) in enumerate(((300, 3072, 32), (130, 12288, 32), (300, 3072, 32), (64, 5120, 16))):
         _check_lowrank(kq, M, K, r, seed=11 + i)
 
