@@ -351,16 +351,17 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
 }
 
 // Per-block Kronecker factors + MXFP4 on the matrix cores (KroQuant §02 with one (A, B)
-// pair per block index instead of one per layer).  The matrix-core step transforms 16
-// blocks that share one P, so here they are the same block index of 16 consecutive token
-// rows.  A wavefront owns U consecutive block indices and a run of 16-row groups: it forms
-// the U fragment sets once, then per group loads, for each of its block indices, 16 bytes
-// per lane (lane (q, bl): row 16g + bl, channels 32 cb + 8q ..+7), G groups at a time.  The four wavefronts of
-// a workgroup take consecutive runs of block indices, so per row a workgroup reads 4U
-// consecutive blocks (2 KiB at U = 4) and writes their 256 code bytes as whole lines.
+// pair per block index instead of one per layer).  A matrix-core step transforms 16
+// columns with one P, so a wavefront owns U consecutive block indices and a run of 8-row
+// groups and takes them two block indices at a time: lane (q, c) holds quarter q of block
+// (row 8 g + c % 8, index cb + c / 8), so one load instruction reads 8 rows x 128
+// contiguous bytes (whole cache lines), the step runs once with P_cb and once with
+// P_cb+1, and each lane keeps the result for its own index.  The fragments of the U
+// indices are formed once per wavefront; the four wavefronts of a workgroup take
+// consecutive runs, so per row a workgroup reads 4U consecutive blocks.
 // AB: float [nbk][80] per block index: A (16, row-major) then B (64, row-major).
-// PTS as in the streaming kernel; a wavefront's channels are fixed, so its exponents are
-// read once.
+// PTS as in the streaming kernel; a lane's channels are fixed, so its exponents are read
+// once.
 template <int U, int G, bool PTS>
 __global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __restrict__ X, int64_t M, int64_t nbk,
                                                              int64_t nseg, int64_t gps,
@@ -368,46 +369,56 @@ __global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __rest
                                                              const int8_t* __restrict__ pts,
                                                              uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15;
+  static_assert(U % 2 == 0, "block indices go in pairs");
+  constexpr int NP = U / 2;
+  const int lane = threadIdx.x & 63, q = lane >> 4, bl = lane & 15, rr = bl & 7, hf = bl >> 3;
   const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nrun = (nbk + U - 1) / U;                  // runs of U block indices
   if (wave >= nrun * nseg) return;                         // whole wavefronts only
   const int64_t cb0 = (wave % nrun) * U, seg = wave / nrun;
   MfmaXform xf[U];
-  uint2 ev[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t cb = cb0 + u < nbk ? cb0 + u : nbk - 1;  // a run past the end repeats the last
     xf[u] = mfma_xform_kron_g(AB + cb * 80, lane);
-    ev[u] = PTS ? *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q) : make_uint2(0u, 0u);
   }
-  const int64_t ngroups = (M + 15) >> 4;
+  uint2 ev[NP];                                            // this lane's exponents, per pair
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t cb = cb0 + 2 * p + hf < nbk ? cb0 + 2 * p + hf : nbk - 1;
+    ev[p] = PTS ? *reinterpret_cast<const uint2*>(pts + cb * 32 + 8 * q) : make_uint2(0u, 0u);
+  }
+  const int64_t ngroups = (M + 7) >> 3;
   const int64_t g0 = seg * gps, g1 = g0 + gps < ngroups ? g0 + gps : ngroups;
   for (int64_t g = g0; g < g1; g += G) {               // G groups' loads in flight together
-    uint4 raw[G][U];
+    uint4 raw[G][NP];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t row = (g + h) * 16 + bl;
+      const int64_t row = (g + h) * 8 + rr;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        raw[h][u] = (g + h < g1 && row < M && cb0 + u < nbk) ? X[(row * nbk + cb0 + u) * 4 + q]
-                                                             : make_uint4(0u, 0u, 0u, 0u);
+      for (int p = 0; p < NP; ++p) {
+        const int64_t cb = cb0 + 2 * p + hf;
+        raw[h][p] = (g + h < g1 && row < M && cb < nbk) ? X[(row * nbk + cb) * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t row = (g + h) * 16 + bl;
+      const int64_t row = (g + h) * 8 + rr;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (PTS) raw[h][u] = pts_scale8(raw[h][u], ev[u]);
-        float y[8];
-        mfma_block_transform<true>(xf[u], __builtin_bit_cast(v8h, raw[h][u]), y);
+      for (int p = 0; p < NP; ++p) {
+        if (PTS) raw[h][p] = pts_scale8(raw[h][p], ev[p]);
+        const v8h b = __builtin_bit_cast(v8h, raw[h][p]);
+        float y0[8], y1[8], y[8];
+        mfma_block_transform<true>(xf[2 * p], b, y0);
+        mfma_block_transform<true>(xf[2 * p + 1], b, y1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] += 0.0f;      // an exact zero leaves as +0
+        for (int i = 0; i < 8; ++i) y[i] = (hf ? y1[i] : y0[i]) + 0.0f;   // an exact zero leaves as +0
         uint32_t w, sb;
         int off;
         mx_pack_block(y, q, w, off, sb);
-        if (g + h < g1 && row < M && cb0 + u < nbk) {
-          const int64_t blk = row * nbk + cb0 + u;
+        const int64_t cb = cb0 + 2 * p + hf;
+        if (g + h < g1 && row < M && cb < nbk) {
+          const int64_t blk = row * nbk + cb;
           *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = w;
           if (q == 0) scales[blk] = (uint8_t)sb;
         }
@@ -705,12 +716,12 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
   return hipGetLastError();
 }
 
-// Per-block factors: ceil(nbk / U) * nseg wavefronts, segment s of a run taking the 16-row
+// Per-block factors: ceil(nbk / U) * nseg wavefronts, segment s of a run taking the 8-row
 // groups [s gps, (s + 1) gps).  About eight workgroups per compute unit in total.
 hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s) {
   constexpr int U = 4, G = 2;
-  const int64_t nbk = K / 32, nrun = (nbk + U - 1) / U, ngroups = (M + 15) / 16;
+  const int64_t nbk = K / 32, nrun = (nbk + U - 1) / U, ngroups = (M + 7) / 8;
   const int64_t target = (int64_t)device_cu_count() * 8 * 4;
   int64_t nseg = (target + nrun - 1) / nrun;
   if (nseg > ngroups) nseg = ngroups;
