@@ -291,6 +291,51 @@ def main():
                                  "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
                 log(f"variant {name:>22} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s (X read once: algorithmic)")
 
+    # ---- the SANA-like workload's Lloyd-Max path, beside the step: per layer the RPBH +
+    # per-token Lloyd-Max transform (4-bit sign-magnitude codes, one fp32 scale per token)
+    # and the W2A4 linear (2-bit weights with fp16 group scales, dequantized through LDS
+    # tables to fp16 for the matrix cores: its roofline is the fp16 peak), each an event
+    # pair around back-to-back launches over rotated copies of the input
+    sana = []
+    if not args.no_variants:
+        c2 = synth.CONFIGS[2]
+        M2 = c2["M"]
+        for li, (name, K, N) in enumerate(c2["layers"]):
+            X2 = torch.from_numpy(synth.activations(M2, K, 2, c2["sigma_mu"], c2["frames"])).to(dev)
+            nrot = max(2, math.ceil((1 << 30) / (X2.numel() * 2)))
+            X2s = [X2] + [X2.clone() for _ in range(nrot - 1)]
+            W2, _, _ = synth.weights(K, N, 2, li, 0)
+            perm, sign = synth.rpbh_params(K, 2, li)
+            xf2 = kq.Xform.rpbh(torch.from_numpy(perm).to(dev), torch.from_numpy(sign).to(dev))
+            wc2, ws2, _ = kq.fold_inverse_into_weights(torch.from_numpy(W2).to(dev), xf2, fmt="lm2")
+            codes2 = torch.empty((M2, K // 2), dtype=torch.uint8, device=dev)
+            scales2 = torch.empty((M2,), dtype=torch.float32, device=dev)
+            Y2 = torch.empty((M2, N), dtype=torch.float16, device=dev)
+
+            def timed(fn, n=20):
+                fn(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for i in range(n):
+                    fn(i + 1)
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / n
+
+            ms_tq = timed(lambda i: kq.transform_quantize(X2s[i % nrot], xf2, fmt="lm4", codes=codes2,
+                                                          scales=scales2))
+            ms_mm = timed(lambda i: kq.w4a4_linear(codes2, scales2, wc2, ws2, fmt="lm2", Y=Y2))
+            tb = M2 * K * 2 + M2 * K // 2 + M2 * 4
+            fl = 2 * M2 * N * K
+            sana.append({"layer": name, "M": M2, "K": K, "N": N,
+                         "transform_lm4_us": round(ms_tq * 1e3, 2), "transform_GBps": round(tb / ms_tq / 1e6, 1),
+                         "transform_frac_hbm": round(tb / ms_tq / 1e6 / PEAK_HBM_GBS, 4),
+                         "w2a4_gemm_us": round(ms_mm * 1e3, 2), "w2a4_TFLOPs": round(fl / ms_mm / 1e9, 1),
+                         "w2a4_frac_fp16_peak": round(fl / ms_mm / 1e9 / PEAK_FP16_TFLOPS, 4)})
+            log(f"sana-like {name}: RPBH+LM4 {ms_tq*1e3:7.2f} us {tb/ms_tq/1e6:8.1f} GB/s | "
+                f"W2A4 {ms_mm*1e3:7.2f} us {fl/ms_mm/1e9:8.1f} TFLOP/s")
+            del X2s
+
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference
         # dispatch for scaling the HBM byte counters
@@ -369,6 +414,7 @@ def main():
         "context": "KroQuant page: its quantization kernel up to 14% faster than SmoothQuant's on an MI350 "
                    "(relative only, other chip)",
         "transform_variants": variants,
+        "sana_like_lloyd_max": sana,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
