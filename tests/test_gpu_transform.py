@@ -118,9 +118,10 @@ def test_mxfp4_pts_matches_oracle(kq, kind, K, rows, which):
                                         (64, 1, False), (32, 17, False), (1152, 150, True), (3072, 48, True),
                                         (32, 3, True)])
 def test_mxfp4_kron_blocks_matches_oracle(kq, K, rows, pts):
-    """Per-block Kronecker factors (one (A_b, B_b) per block index) on the matrix-core
-    kernel that holds one block index per wavefront; ragged row counts, one row, and
-    power-of-two channel scaling ahead of it (random exponents 0..15)."""
+    """Per-block Kronecker factors (one (A_b, B_b) per block index) on their matrix-core
+    kernel (pairs of block indices per step, odd index counts included); ragged row
+    counts, one row, and power-of-two channel scaling ahead of it (random exponents
+    0..15)."""
     X16 = synth.activations(rows, K, 17, 2.0)
     A, B = synth.kron_block_factors(17, 0, K // 32)
     xf = {"kind": "kron_blocks", "A": A, "B": B}
@@ -224,6 +225,15 @@ def test_lm4_codes_match_oracle(kq, layer, rows):
     _, K, _ = c["layers"][layer]
     X16 = synth.activations(rows, K, 2, c["sigma_mu"])
     _lm4_check(kq, X16, synth.xform_for(2, layer, K), f"cfg2 layer{layer} M={rows} K={K}")
+
+
+@pytest.mark.parametrize("K,rows", [(32, 3), (4096, 9), (4128, 7), (16384, 5)])
+def test_lm4_row_group_widths(kq, K, rows):
+    """RPBH + per-token Lloyd-Max on the row-group kernel: four rows per group up to
+    K = 4096 and two above, one block per row, the widest row, odd row counts."""
+    X16 = synth.activations(rows, K, 25, 2.0)
+    perm, sign = synth.rpbh_params(K, 25, 0)
+    _lm4_check(kq, X16, {"kind": "rpbh", "perm": perm, "sign": sign}, f"lm4 K={K} M={rows}")
 
 
 def test_lm4_zero_row(kq):

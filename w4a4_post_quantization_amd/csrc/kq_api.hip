@@ -162,8 +162,9 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   std::memcpy(f.A, xf->A, sizeof f.A);
   std::memcpy(f.B, xf->B, sizeof f.B);
   // MXFP4 goes through the matrix-core transforms (streaming for Kronecker / identity
-  // without centring, row-staged for RPBH); the per-token Lloyd-Max format and centred
-  // Kronecker / identity use the row-staged vector kernel.
+  // without centring, row-staged for RPBH), and so does RPBH with the per-token Lloyd-Max
+  // format without centring; the other Lloyd-Max cases and centred Kronecker / identity
+  // use the row-staged vector kernel.
   // A dense P, per-block factors and power-of-two channel scaling run on the matrix-core
   // stream paths only (MXFP4, no centring).
   const bool mx = fmt == KQ_FMT_MXFP4;
@@ -179,6 +180,9 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   } else if (stream_path) {
     e = launch_kron_mx_mfma(xf->kind, static_cast<const __half*>(X), M * (K / 32), f, xf->P, xf->pts, K / 32,
                             codes, static_cast<uint8_t*>(scales), stream);
+  } else if (xf->kind == KQ_XFORM_RPBH_32 && fmt == KQ_FMT_LM4_TOKEN && !center) {
+    e = launch_rpbh_lm4_mfma(static_cast<const __half*>(X), M, K, xf->perm, xf->sign, codes,
+                             static_cast<float*>(scales), stream);
   } else if (rpbh_mfma) {
     e = launch_rpbh_mx_mfma(center != 0, static_cast<const __half*>(X), M, K, xf->perm, xf->sign, codes,
                             static_cast<uint8_t*>(scales), static_cast<__half*>(mu), stream);

@@ -103,6 +103,13 @@ __device__ __forceinline__ float add_f16x2(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pair), (h2){1.0f, 1.0f}, acc, false);
 }
 
+// acc + a.x^2 + a.y^2 for a pair of halves (exact products, float32 accumulation).
+__device__ __forceinline__ float sq_f16x2(uint32_t pair, float acc) {
+  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = __builtin_bit_cast(h2, pair);
+  return __builtin_amdgcn_fdot2(v, v, acc, false);
+}
+
 // Buffer resource over [base, base + bytes): loads past the end return zeros and stores
 // past the end are dropped, which handles ragged tiles and masked lanes without branches
 // (a masked lane uses an offset of at least KQ_OOB).

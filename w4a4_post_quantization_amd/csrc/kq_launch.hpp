@@ -36,6 +36,10 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
                                const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s);
+// RPBH + per-token Lloyd-Max 4-bit codes (no centring) on the row-group kernel: codes
+// [M][K/2], scales float [M] (s_t = ||x_t|| / sqrt(K)).
+hipError_t launch_rpbh_lm4_mfma(const __half* X, int64_t M, int64_t K, const int32_t* perm, const int8_t* sign,
+                                uint8_t* codes, float* scales, hipStream_t s);
 
 // Row-staged transform + quantize: any transform, optional centring, MXFP4 or LM4.
 // kind: 0 none, 1 kron, 2 rpbh; fmt: 0 MXFP4, 1 LM4.

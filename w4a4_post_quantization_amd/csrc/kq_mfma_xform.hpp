@@ -147,6 +147,28 @@ __device__ __forceinline__ void mx_pack_block(const float* y, int q, uint32_t& d
   scale_byte = sb;
 }
 
+// Per-token Lloyd-Max codes of the lane's eight outputs (same lanes and byte layout as
+// mx_pack_block): 4-bit sign-magnitude, magnitude = number of the scaled thresholds ts[]
+// (ascending) strictly below |y| (a value on a threshold takes the smaller magnitude),
+// found by a three-step binary search; sign bit for y < 0.  Inputs must not be -0.0.
+__device__ __forceinline__ void lm_pack_block(const float* y, int q, const float* ts, uint32_t& dword, int& byte_off) {
+  uint32_t h[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(y[i]);
+    uint32_t idx = a > ts[3] ? 4u : 0u;
+    const float t1 = idx ? ts[5] : ts[1];
+    idx += a > t1 ? 2u : 0u;
+    const float t0 = idx == 0 ? ts[0] : idx == 2 ? ts[2] : idx == 4 ? ts[4] : ts[6];
+    idx += a > t0 ? 1u : 0u;
+    h[i >> 2] |= (idx | (y[i] < 0.0f ? 8u : 0u)) << (4 * (i & 3));
+  }
+  // outputs 4q..4q+3 are bytes 2q, 2q+1 of the block; 16+4q..16+4q+3 bytes 8+2q, 8+2q+1
+  const auto sw = __builtin_amdgcn_permlane16_swap(h[0], h[1], false, false);
+  dword = sw[0] | (sw[1] << 16);
+  byte_off = (q & 1) ? 8 + 2 * (q - 1) : 2 * q;
+}
+
 // Eight fp16 values divided by 2^e (one exponent byte each, in order): v_ldexp_f16 rounds a
 // result below the normal range to nearest even, like a conversion would.
 __device__ __forceinline__ uint32_t pts_scale2(uint32_t x2, uint32_t e2) {

@@ -470,12 +470,19 @@ __device__ __forceinline__ GroupChunks<R> rg_load(const __half* X, int64_t row0,
 #define KQ_PERM_LO 0x05040100u   // (lo16 of s1, lo16 of s0)
 #define KQ_PERM_HI 0x07060302u   // (hi16 of s1, hi16 of s0)
 
-template <int R, bool CENTER>
-__global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
+// Wavefronts per workgroup at most, by variant: the four-row Lloyd-Max form needs more
+// registers and is only used up to K = 6144 (at most six wavefronts).
+template <int R, int FMT>
+constexpr int rg_maxw() { return (FMT == 1 && R == 4) ? 8 : RG_MAXW; }
+
+template <int R, bool CENTER, int FMT>
+__global__ __launch_bounds__((64 * rg_maxw<R, FMT>())) void rpbh_mx_group_kernel(
     const __half* X, int64_t M, int K, const int32_t* __restrict__ perm,
-    const int8_t* __restrict__ sign, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const int8_t* __restrict__ sign, LmTables lm, uint8_t* __restrict__ codes, void* __restrict__ scales,
     __half* __restrict__ mu) {
   static_assert(R == 2 || R == 4, "rows per group");
+  static_assert(FMT == 0 || !CENTER, "the Lloyd-Max output is offered without centring");
+  constexpr bool RSUM = CENTER || FMT == 1;     // a per-row reduction over the staged row
   extern __shared__ __align__(16) unsigned char smem[];
   const int t = threadIdx.x, T = blockDim.x, NW = T >> 6, lane = t & 63, wid = t >> 6;
   const int q = lane >> 4, bl = lane & 15;
@@ -559,18 +566,18 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
                         __builtin_amdgcn_perm(b[2 * m2 + 1], a[2 * m2 + 1], KQ_PERM_HI)};
         }
       }
-      if (CENTER) {
+      if (RSUM) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          float s8 = 0.0f;     // sum of the 8 halves
+          float s8 = 0.0f;     // sum of the 8 halves (centring) or of their squares (Lloyd-Max scale)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) s8 = add_f16x2(c.v[j][r][m], s8);
+          for (int m = 0; m < 4; ++m) s8 = FMT == 1 ? sq_f16x2(c.v[j][r][m], s8) : add_f16x2(c.v[j][r][m], s8);
           ps[r] += colv[j] ? s8 : 0.0f;     // a repeated column is not counted
         }
       }
     }
     if (g + gridDim.x < ngroups) raw = rg_load<R>(X, (g + gridDim.x) * R, M, K, col);   // prefetch the next group
-    if (CENTER) {
+    if (RSUM) {
       // wave sums of the R partial sums in registers: each lane-half / lane-row swap adds
       // the partner's copy of one value while halving the set (the swap returns, per lane,
       // its own value in one result and the partner's in the other), then a row sum;
@@ -593,10 +600,10 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
       if ((lane & 15) == 0 && (R == 4 || (lane & 16) == 0)) red[wid * 4 + (R == 4 ? (lane >> 4) : (lane >> 5))] = v;
     }
     lds_barrier();       // the group is staged (and the partial sums are visible)
-    float m32[R];
+    float m32[R], scr[R];          // the centring term, or the Lloyd-Max scale, per row
 #pragma unroll
-    for (int r = 0; r < R; ++r) m32[r] = 0.0f;
-    if (CENTER) {
+    for (int r = 0; r < R; ++r) m32[r] = scr[r] = 0.0f;
+    if (RSUM) {
       float tot[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) tot[r] = 0.0f;
@@ -611,15 +618,23 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const __half mh = __float2half_rn(tot[r] / (float)K);
-        m32[r] = 32.0f * __half2float(mh);
-        if (t == r && g * R + r < M) mu[g * R + r] = mh;
+        if (FMT == 1) {
+          // s_t = RMS of the rotated token = ||x_t|| / sqrt(K), the rotation being
+          // orthogonal
+          scr[r] = sqrtf(tot[r] / (float)K);
+          if (t == r && g * R + r < M) reinterpret_cast<float*>(scales)[g * R + r] = scr[r];
+        } else {
+          const __half mh = __float2half_rn(tot[r] / (float)K);
+          m32[r] = 32.0f * __half2float(mh);
+          if (t == r && g * R + r < M) mu[g * R + r] = mh;
+        }
       }
     }
     // the group's rows of codes and scales (rows past M are outside both ranges)
     const int64_t nrows = M - g * R < R ? M - g * R : R;
     const __amdgpu_buffer_rsrc_t rcodes = make_rsrc(codes + g * R * (int64_t)(K >> 1), nrows * (K >> 1));
-    const __amdgpu_buffer_rsrc_t rscales = make_rsrc(scales + g * R * (int64_t)nb, nrows * nb);
+    const __amdgpu_buffer_rsrc_t rscales =
+        make_rsrc(static_cast<uint8_t*>(scales) + (FMT == 0 ? g * R * (int64_t)nb : 0), FMT == 0 ? nrows * nb : 0);
 #pragma unroll 1
     for (int it = 0; it < 2; ++it) {
       const int ch = wid + NW * it;
@@ -675,14 +690,21 @@ __global__ __launch_bounds__(64 * RG_MAXW) void rpbh_mx_group_kernel(
         if (CENTER && q == 0) y[r][0] -= m32[r];      // output 0 of the block
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[r][i] = __builtin_fmaf(y[r][i], coef[i], 0.0f);   // +0 for an exact zero
-        mx_pack_block(y[r], q, w[r], off, sb[r]);
+        if (FMT == 1) {
+          float ts[7];                                  // the thresholds scaled by the row's s_t
+#pragma unroll
+          for (int i = 0; i < 7; ++i) ts[i] = lm.t16[i] * scr[r];
+          lm_pack_block(y[r], q, ts, w[r], off);
+        }
+        else mx_pack_block(y[r], q, w[r], off, sb[r]);
       }
       const int coff = bv ? 16 * blk + off : KQ_OOB;
       const int soff = (bv && q == 0) ? blk : KQ_OOB;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         __builtin_amdgcn_raw_buffer_store_b32(w[r], rcodes, coff + (coff == KQ_OOB ? 0 : r * (K >> 1)), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[r], rscales, soff + (soff == KQ_OOB ? 0 : r * nb), 0, 0);
+        if (FMT == 0)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[r], rscales, soff + (soff == KQ_OOB ? 0 : r * nb), 0, 0);
       }
     }
   }
@@ -739,23 +761,24 @@ hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const fl
   return hipGetLastError();
 }
 
-template <int R, bool CENTER>
+template <int R, bool CENTER, int FMT>
 static hipError_t rpbh_group_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
-                                    uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s) {
+                                    uint8_t* codes, void* scales, __half* mu, hipStream_t s) {
   // wavefronts: enough that each transforms at most two 16-block chunks of the group
   // (this also keeps the set-up at <= 4 perm chunks and the staging at <= 2 columns per
   // lane); persistent workgroups, as many as are resident at once
   const int nchunk = (K / 32 + 15) / 16;
   const int nw = (nchunk + 1) / 2;
-  if (nw > RG_MAXW) return hipErrorInvalidValue;
+  if (nw > rg_maxw<R, FMT>()) return hipErrorInvalidValue;
   const unsigned threads = 64u * (unsigned)nw;
   const size_t lds = rg_lds_bytes(R, K);
-  const auto kern = rpbh_mx_group_kernel<R, CENTER>;
+  const auto kern = rpbh_mx_group_kernel<R, CENTER, FMT>;
   int64_t grid = (M + R - 1) / R;
   const int64_t cap =
       (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), (int)threads, lds);
   if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, perm, sign, codes, scales, mu);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, perm, sign, lm_tables(), codes, scales,
+                     mu);
   return hipGetLastError();
 }
 
@@ -766,10 +789,19 @@ hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t 
   // workgroups share a compute unit (at K = 12288 that measured 13% faster than four rows
   // with one workgroup per compute unit)
   if (K <= 6144)
-    return center ? rpbh_group_launch<4, true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
-                  : rpbh_group_launch<4, false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
-  return center ? rpbh_group_launch<2, true>(X, M, (int)K, perm, sign, codes, scales, mu, s)
-                : rpbh_group_launch<2, false>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+    return center ? rpbh_group_launch<4, true, 0>(X, M, (int)K, perm, sign, codes, scales, mu, s)
+                  : rpbh_group_launch<4, false, 0>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+  return center ? rpbh_group_launch<2, true, 0>(X, M, (int)K, perm, sign, codes, scales, mu, s)
+                : rpbh_group_launch<2, false, 0>(X, M, (int)K, perm, sign, codes, scales, mu, s);
+}
+
+// Lloyd-Max form: four rows per group up to K = 4096, two above (at K = 5600 four rows
+// with their larger register set measured 37% slower than two).
+hipError_t launch_rpbh_lm4_mfma(const __half* X, int64_t M, int64_t K, const int32_t* perm, const int8_t* sign,
+                                uint8_t* codes, float* scales, hipStream_t s) {
+  if (K > 16384) return hipErrorInvalidValue;
+  if (K <= 4096) return rpbh_group_launch<4, false, 1>(X, M, (int)K, perm, sign, codes, scales, nullptr, s);
+  return rpbh_group_launch<2, false, 1>(X, M, (int)K, perm, sign, codes, scales, nullptr, s);
 }
 
 int resident_blocks_per_cu(const void* kernel, int threads, size_t lds) {
