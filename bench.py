@@ -12,11 +12,13 @@ Weights are folded once (offline, untimed).  Inputs are seeded synthetic activat
 resident in HBM; the activation buffers rotate over enough copies (>= 1 GiB) that no step
 reads them from the 256 MB last-level cache.
 
-Prints ONE JSON line (rank 0).  Per-kernel durations come from HIP events recorded on the
-stream the kernels run on, one after every launch of the timed steps (a launch's duration
-runs from the event before it to its own, so it includes the dispatch gap; averaged over
-the steps).  The "traffic" fields come from the HBM byte counters recorded in profiles/ for
-the same kernel source (null when the source has changed since).
+Prints ONE JSON line (rank 0).  The step time comes from two HIP events around the timed
+steps, on the stream the kernels run on, with no event between launches (each one would
+leave the GPU idle for several microseconds).  Per-launch durations come from a second
+timed pass: each call of the step launched K times back to back between two events, with
+the same arguments and rotated activations.  The "traffic" fields come from the HBM byte
+counters recorded in profiles/ for the same kernel source (null when the source has changed
+since).
 """
 
 import argparse
@@ -181,53 +183,57 @@ def main():
             Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
 
-    # one event after every launch of the timed steps, recorded on the current stream (the
-    # one the kernels run on); a launch's duration is the span from the event before it
-    # (the previous launch's, or the start of the timed region) to its own.  Per layer the
-    # order is low-rank projection, transform, GEMM (the first two are independent).
+    # The calls of one step, per layer: low-rank projection, transform, GEMM (the first two
+    # are independent).  Input set s % R feeds step s.
     nl = len(layers)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
 
-    def step(s, ev=None):
-        Xs = Xsets[s % R]
-        for li, L in enumerate(layers):
-            X = Xs[L["K"]]
+    def call(li, k, s):
+        L, X = layers[li], Xsets[s % R][layers[li]["K"]]
+        if k == 0:
             kq.lowrank_down(X, L["L1"], T=L["T"], workspace=L["lrws"])
-            if ev:
-                ev[3 * li].record()
+        elif k == 1:
             kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],
                                   mu=L["mu"])
-            if ev:
-                ev[3 * li + 1].record()
+        else:
             kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
                            wbar=L["wbar"], Y=L["Y"])
-            if ev:
-                ev[3 * li + 2].record()
+
+    def step(s):
+        for li in range(nl):
+            for k in range(3):
+                call(li, k, s)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps between two events, with one event after each launch
+    # ---- timed region: K whole steps between two events on the stream the kernels run
+    # on, with nothing between the launches (an event recorded between two launches
+    # leaves the GPU idle for several microseconds)
     t0 = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_start.record()
     for s in range(args.steps):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s)
     e_end.record()
     host_submit = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
-    # average duration of each launch over the timed steps: [transform, low-rank, GEMM] per layer
-    flat = [e_start] + [e for ev in evs for e in ev]
-    span = [flat[i].elapsed_time(flat[i + 1]) for i in range(len(flat) - 1)]
-    per = [[0.0, 0.0, 0.0] for _ in range(nl)]
-    for i, t in enumerate(span):
-        li, k = (i % (3 * nl)) // 3, i % 3
-        per[li][k] += t / args.steps
-    dur = [[p[1], p[0], p[2]] for p in per]
+    # ---- per-launch durations: each call of the step, K launches back to back between two
+    # events (the same arguments, the activations rotated as in the step), so a launch's
+    # figure is its kernels' time as the profiler's trace sees it
+    dur = [[0.0, 0.0, 0.0] for _ in range(nl)]   # [transform, low-rank, GEMM] per layer
+    for li in range(nl):
+        for k in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for s in range(args.steps):
+                call(li, k, args.warmup + s)
+            b.record()
+            torch.cuda.synchronize()
+            dur[li][(1, 0, 2)[k]] = a.elapsed_time(b) / args.steps
 
     # ---- transform variants beside the path (not part of the step): the Kronecker factors
     # and a dense 32x32 P on the same streaming matrix-core kernel, per-block factors on
