@@ -367,6 +367,31 @@ def test_w2a4_linear_matches_oracle(kq):
         assert err <= TOL
 
 
+@pytest.mark.parametrize("layer,M,Nr", [(0, 4096, 6720), (0, 4000, 6416), (2, 4096, 2240), (1, 1100, 5600)])
+def test_w2a4_full_size_forms(kq, layer, M, Nr):
+    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, and with M and N
+    ragged against it) and the 128 x 128 form (fc2, and fewer tokens); oracle on sampled rows
+    (the edges of the 256- and 128-row tiles) and all columns."""
+    import torch
+    c = synth.CONFIGS[2]
+    _, K, N = c["layers"][layer]
+    X16 = synth.activations(M, K, 2, c["sigma_mu"])
+    W16, _, _ = synth.weights(K, N, 2, layer, 0)
+    W16 = np.ascontiguousarray(W16[:Nr])
+    xf = synth.xform_for(2, layer, K)
+    dxf = _dev_xform(kq, torch, xf, K)
+    xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
+    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+    Y = kq.w4a4_linear(xc, xs, wc, ws, fmt="lm2")
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(0, M, 61)) | {0, 127, 128, 255, 256, M - 129, M - 128, M - 1} - {-1}))
+    rows = rows[(rows >= 0) & (rows < M)]
+    ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), rows=rows)
+    err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
+    print(f"W2A4 layer{layer} M={M} N={Nr} K={K}: {err:.3e}")
+    assert err <= TOL
+
+
 def test_w4a4_full_size_sampled(kq):
     """FLUX-like qkv at full size (M = 4608, K = 3072, N = 9216) in the bench's launch
     configuration; oracle on sampled rows and all columns."""
