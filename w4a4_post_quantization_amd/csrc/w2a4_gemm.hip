@@ -14,6 +14,26 @@ namespace kq {
 
 __device__ __forceinline__ int chunk_swz2(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
+// Dequantization tables in LDS, entry b for a byte of codes: lut16[b] = the fp16 levels of
+// its two 4-bit codes (low nibble first; bit 3 the sign), lut4[b] = those of its four 2-bit
+// codes (low pair first; bit 1 the sign).  Threads tid, tid + nt, ... fill the entries.
+__device__ __forceinline__ void build_lm_luts(const LmTables& lm, uint32_t* lut16, uint2* lut4, int tid, int nt) {
+  for (int b = tid; b < 256; b += nt) {
+    const int c0 = b & 15, c1 = b >> 4;
+    const float v0 = (c0 & 8) ? -lm.l16[c0 & 7] : lm.l16[c0 & 7];
+    const float v1 = (c1 & 8) ? -lm.l16[c1 & 7] : lm.l16[c1 & 7];
+    lut16[b] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v0, v1));
+    float w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = (b >> (2 * e)) & 3;
+      w[e] = (c & 2) ? -lm.l4[c & 1] : lm.l4[c & 1];
+    }
+    lut4[b] = make_uint2(__builtin_bit_cast(uint32_t, __floats2half2_rn(w[0], w[1])),
+                         __builtin_bit_cast(uint32_t, __floats2half2_rn(w[2], w[3])));
+  }
+}
+
 template <int BN, int BM, int WN, int WM>
 __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
     const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
@@ -31,21 +51,7 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
   const int wn = wid % WN, wm = wid / WN;
   const int lr = lane & 15, q = lane >> 4;
 
-  // build the tables: 4-bit sign-magnitude (bit 3 sign), 2-bit sign-magnitude (bit 1 sign)
-  for (int b = tid; b < 256; b += NT) {
-    const int c0 = b & 15, c1 = b >> 4;
-    const float v0 = (c0 & 8) ? -lm.l16[c0 & 7] : lm.l16[c0 & 7];
-    const float v1 = (c1 & 8) ? -lm.l16[c1 & 7] : lm.l16[c1 & 7];
-    lut16[b] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v0, v1));
-    float w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = (b >> (2 * e)) & 3;
-      w[e] = (c & 2) ? -lm.l4[c & 1] : lm.l4[c & 1];
-    }
-    lut4[b] = make_uint2(__builtin_bit_cast(uint32_t, __floats2half2_rn(w[0], w[1])),
-                         __builtin_bit_cast(uint32_t, __floats2half2_rn(w[2], w[3])));
-  }
+  build_lm_luts(lm, lut16, lut4, tid, NT);
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile_n = blockIdx.x % tiles_n, tile_m = blockIdx.x / tiles_n;
@@ -152,18 +158,17 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
 // Against 64 x 64 wave tiles of 16 x 16 products this reads half the LDS bytes per
 // product.  A k-step is two groups (64 k): a barrier then separates 64 products per
 // wavefront, and the global loads of the next step, issued before them, have that long
-// to land.  One row of each operand per thread is staged (threads past BM stage no token
-// row); LDS rows are 128 bytes, their 16-byte chunks XOR-swizzled by the row's low bits.
+// to land.  Thread t stages weight row t and token row t; LDS rows are 128 bytes, their
+// 16-byte chunks XOR-swizzled by the row's low bits.
 // What bounds it is LDS: per step the compute unit reads 128 KiB of fragments, makes
 // 12 K table lookups at random addresses and stores 64 KiB, about as long as the step's
 // matrix-core work.
 // A last step with one group left (K % 64 = 32) leaves the other group's values zero.
-template <int BM>
 __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
     const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales, int N, LmTables lm,
     __half* __restrict__ Y) {
-  constexpr int BN = 256, TN = 4, TM = BM / 64, RB = 128;   // RB: LDS bytes per row and step
+  constexpr int BN = 256, BM = 256, TN = 4, TM = 4, RB = 128;   // RB: LDS bytes per row and step
   constexpr int A_OFF = 0, B_OFF = BN * RB, BUF = (BN + BM) * RB;
   __shared__ __align__(16) uint8_t lds[2 * BUF];
   __shared__ uint32_t lut16[256];   // byte of two 4-bit codes -> two fp16 levels
@@ -173,21 +178,7 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   const int wn = wid & 1, wm = wid >> 1;
   const int l32 = lane & 31, h = lane >> 5;
 
-  {
-    const int b = tid;
-    const int c0 = b & 15, c1 = b >> 4;
-    const float v0 = (c0 & 8) ? -lm.l16[c0 & 7] : lm.l16[c0 & 7];
-    const float v1 = (c1 & 8) ? -lm.l16[c1 & 7] : lm.l16[c1 & 7];
-    lut16[b] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v0, v1));
-    float w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = (b >> (2 * e)) & 3;
-      w[e] = (c & 2) ? -lm.l4[c & 1] : lm.l4[c & 1];
-    }
-    lut4[b] = make_uint2(__builtin_bit_cast(uint32_t, __floats2half2_rn(w[0], w[1])),
-                         __builtin_bit_cast(uint32_t, __floats2half2_rn(w[2], w[3])));
-  }
+  build_lm_luts(lm, lut16, lut4, tid, 256);
 
   // tiles walked column by column in groups of 8 along M, die-contiguous (as the W4A4 form)
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -206,10 +197,9 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   const int n0 = tile_n * BN, m0 = tile_m * BM;
   const int ng = K >> 5, nks = (ng + 1) >> 1;             // groups, 64-wide steps
 
-  // staging rows of this thread: weight row tid, token row tid (if tid < BM); rows past the
-  // matrix repeat its last row (their results are never stored)
-  const bool has_x = tid < BM;
-  const int64_t wrow = min(n0 + tid, N - 1), xrow = min(m0 + (has_x ? tid : 0), M - 1);
+  // staging rows of this thread: weight row tid, token row tid; rows past the matrix repeat
+  // its last row (their results are never stored)
+  const int64_t wrow = min(n0 + tid, N - 1), xrow = min(m0 + tid, M - 1);
   const uint8_t* const gw = wcodes + wrow * (K >> 2);
   const __half* const gs = wscales + wrow * (K >> 5);
   const uint8_t* const gx = xcodes + xrow * (K >> 1);
@@ -232,10 +222,8 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     sg[0] = gs[2 * ks];
     rw[1] = two ? *reinterpret_cast<const uint2*>(gw + 16 * ks + 8) : make_uint2(0u, 0u);
     sg[1] = two ? gs[2 * ks + 1] : __float2half(0.0f);     // a zero scale zeroes the group
-    if (has_x) {
-      rx[0] = *reinterpret_cast<const uint4*>(gx + 32 * ks);
-      rx[1] = two ? *reinterpret_cast<const uint4*>(gx + 32 * ks + 16) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    rx[0] = *reinterpret_cast<const uint4*>(gx + 32 * ks);
+    rx[1] = two ? *reinterpret_cast<const uint4*>(gx + 32 * ks + 16) : make_uint4(0u, 0u, 0u, 0u);
   };
   auto lstore = [&](int buf, bool two) {
     uint8_t* const base = lds + buf * BUF;
@@ -257,26 +245,24 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
             make_uint4(hw[0], hw[1], hw[2], hw[3]);
       }
     }
-    if (has_x) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t xv[4] = {rx[q].x, rx[q].y, rx[q].z, rx[q].w};
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t xv[4] = {rx[q].x, rx[q].y, rx[q].z, rx[q].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t hx[4];
+      for (int c = 0; c < 4; ++c) {
+        uint32_t hx[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int bI = 4 * c + u;
-            hx[u] = (q == 0 || two) ? lut16[(xv[bI >> 2] >> (8 * (bI & 3))) & 0xFF] : 0u;
-          }
-          *reinterpret_cast<uint4*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) =
-              make_uint4(hx[0], hx[1], hx[2], hx[3]);
+        for (int u = 0; u < 4; ++u) {
+          const int bI = 4 * c + u;
+          hx[u] = (q == 0 || two) ? lut16[(xv[bI >> 2] >> (8 * (bI & 3))) & 0xFF] : 0u;
         }
+        *reinterpret_cast<uint4*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) =
+            make_uint4(hx[0], hx[1], hx[2], hx[3]);
       }
     }
   };
 
-  const int wrow_a = wn * 128, wrow_b = wm * (BM / 2);
+  const int wrow_a = wn * 128, wrow_b = wm * 128;
   gload(0);
   __syncthreads();  // tables ready
   lstore(0, 1 < ng);
@@ -338,7 +324,7 @@ hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t
   const int64_t cus = device_cu_count();
   const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
   if (2 * t256 >= 3 * cus) {
-    hipLaunchKernelGGL((w2a4_gemm_big_kernel<256>), dim3((unsigned)t256), dim3(256), 0, s, xcodes, xscales, (int)M,
+    hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3((unsigned)t256), dim3(256), 0, s, xcodes, xscales, (int)M,
                        (int)K, wcodes, wscales, (int)N, lm_tables(), Y);
     return hipGetLastError();
   }
