@@ -422,6 +422,19 @@ def test_w4a4_large_tile_form_ragged(kq, rank, with_mu):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("cfg,layer", [(1, 0), (1, 3), (4, 0), (4, 1)])
+def test_w4a4_full_size_other_configs(kq, cfg, layer):
+    """The PixArt-like (M = 8192; qkv K = 1152 on the register-staged form, fc2 K = 4608 on
+    the large-tile form) and CogVideoX-like (M = 17550, ragged against 256-row tiles) linears
+    at full size: oracle on sampled rows and all columns."""
+    M = synth.CONFIGS[cfg]["M"]
+    d = _linear_case(kq, cfg, layer, M)
+    rows = _sampled_rows(M)
+    err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
+    print(f"cfg{cfg} layer{layer} full size M={M}: sampled rel frobenius {err:.3e}")
+    assert err <= TOL
+
+
 def test_w4a4_full_size_fc2_sampled(kq):
     """FLUX-like fc2 at full size (M = 4608, K = 12288, N = 3072): oracle on sampled rows and
     all columns."""
