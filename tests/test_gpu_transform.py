@@ -227,10 +227,10 @@ def test_lm4_codes_match_oracle(kq, layer, rows):
     _lm4_check(kq, X16, synth.xform_for(2, layer, K), f"cfg2 layer{layer} M={rows} K={K}")
 
 
-@pytest.mark.parametrize("K,rows", [(32, 3), (4096, 9), (4128, 7), (16384, 5)])
+@pytest.mark.parametrize("K,rows", [(32, 3), (2048, 9), (2080, 7), (16384, 5)])
 def test_lm4_row_group_widths(kq, K, rows):
     """RPBH + per-token Lloyd-Max on the row-group kernel: four rows per group up to
-    K = 4096 and two above, one block per row, the widest row, odd row counts."""
+    K = 2048 and two above, one block per row, the widest row, odd row counts."""
     X16 = synth.activations(rows, K, 25, 2.0)
     perm, sign = synth.rpbh_params(K, 25, 0)
     _lm4_check(kq, X16, {"kind": "rpbh", "perm": perm, "sign": sign}, f"lm4 K={K} M={rows}")

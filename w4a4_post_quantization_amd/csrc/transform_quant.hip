@@ -795,12 +795,12 @@ hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t 
                 : rpbh_group_launch<2, false, 0>(X, M, (int)K, perm, sign, codes, scales, mu, s);
 }
 
-// Lloyd-Max form: four rows per group up to K = 4096, two above (at K = 5600 four rows
-// with their larger register set measured 37% slower than two).
+// Lloyd-Max form: four rows per group up to K = 2048, two above (with their larger
+// register set four rows measured 4% slower than two at K = 2240 and 37% at K = 5600).
 hipError_t launch_rpbh_lm4_mfma(const __half* X, int64_t M, int64_t K, const int32_t* perm, const int8_t* sign,
                                 uint8_t* codes, float* scales, hipStream_t s) {
   if (K > 16384) return hipErrorInvalidValue;
-  if (K <= 4096) return rpbh_group_launch<4, false, 1>(X, M, (int)K, perm, sign, codes, scales, nullptr, s);
+  if (K <= 2048) return rpbh_group_launch<4, false, 1>(X, M, (int)K, perm, sign, codes, scales, nullptr, s);
   return rpbh_group_launch<2, false, 1>(X, M, (int)K, perm, sign, codes, scales, nullptr, s);
 }
 
