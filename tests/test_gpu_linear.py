@@ -443,3 +443,26 @@ def test_w4a4_full_size_fc2_sampled(kq):
     err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
     print(f"fc2 full-size sampled rel frobenius {err:.3e}")
     assert err <= TOL
+
+
+def test_repeated_calls_bit_identical(kq):
+    """The centred RPBH transform and the W4A4 linear at the FLUX-like qkv size give the same
+    bytes on every call (no atomics, fixed summation order)."""
+    import torch
+    d = _linear_case(kq, 3, 0, 4608)
+    X = torch.from_numpy(d["X16"]).cuda()
+    dxf = _dev_xform(kq, torch, d["xf"], X.shape[1])
+    ops = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (d["xc"], d["xs"], d["wc"], d["ws"], d["T"], d["L2"],
+                                                                       d["mu"], d["wbar"])]
+    outs, codes = [], []
+    for _ in range(3):
+        xc, xs, mu = kq.transform_quantize(X, dxf, fmt="mxfp4", center=True)
+        codes.append((xc.cpu().numpy(), xs.cpu().numpy(), mu.cpu().numpy().view(np.uint16)))
+        Y = kq.w4a4_linear(*ops[:4], T=ops[4], L2=ops[5], mu=ops[6], wbar=ops[7])
+        outs.append(Y.cpu().numpy().view(np.uint16))
+    torch.cuda.synchronize()
+    for c in codes[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(codes[0], c))
+    for y in outs[1:]:
+        assert np.array_equal(outs[0], y)
+    assert np.array_equal(outs[0], d["Y"].view(np.uint16))
