@@ -171,7 +171,7 @@ def main():
         W, L1, L2 = synth.weights(K, N, CFG, li, r)
         perm, sign = synth.rpbh_params(K, CFG, li)
         xf = kq.Xform.rpbh(torch.from_numpy(perm).to(dev), torch.from_numpy(sign).to(dev))
-        wc, ws, wbar = kq.fold_inverse_into_weights(torch.from_numpy(W).to(dev), xf, fmt="mxfp4")
+        wc, ws, wbar = kq.fold_inverse_into_weights_nk(torch.from_numpy(W).to(dev), xf, fmt="mxfp4")
         layers.append(dict(
             name=name, K=K, N=N, xf=xf, wc=wc, ws=ws, wbar=wbar,
             L1=torch.from_numpy(L1).to(dev), L2=torch.from_numpy(L2).to(dev),
@@ -197,7 +197,7 @@ def main():
             kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],
                                   mu=L["mu"])
         else:
-            kq.w4a4_linear(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
+            kq.w4a4_linear_t(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
                            wbar=L["wbar"], Y=L["Y"])
 
     def step(s):
@@ -315,7 +315,7 @@ def main():
             W2, _, _ = synth.weights(K, N, 2, li, 0)
             perm, sign = synth.rpbh_params(K, 2, li)
             xf2 = kq.Xform.rpbh(torch.from_numpy(perm).to(dev), torch.from_numpy(sign).to(dev))
-            wc2, ws2, _ = kq.fold_inverse_into_weights(torch.from_numpy(W2).to(dev), xf2, fmt="lm2")
+            wc2, ws2, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W2).to(dev), xf2, fmt="lm2")
             codes2 = torch.empty((M2, K // 2), dtype=torch.uint8, device=dev)
             scales2 = torch.empty((M2,), dtype=torch.float32, device=dev)
             Y2 = torch.empty((M2, N), dtype=torch.float16, device=dev)
@@ -332,7 +332,7 @@ def main():
 
             ms_tq = timed(lambda i: kq.transform_quantize(X2s[i % nrot], xf2, fmt="lm4", codes=codes2,
                                                           scales=scales2))
-            ms_mm = timed(lambda i: kq.w4a4_linear(codes2, scales2, wc2, ws2, fmt="lm2", Y=Y2))
+            ms_mm = timed(lambda i: kq.w4a4_linear_t(codes2, scales2, wc2, ws2, fmt="lm2", Y=Y2))
             tb = M2 * K * 2 + M2 * K // 2 + M2 * 4
             fl = 2 * M2 * N * K
             sana.append({"layer": name, "M": M2, "K": K, "N": N,

@@ -13,8 +13,8 @@
  *     inverse folded offline as W' = R^-1 W, one Lloyd-Max codebook for all
  *     rotated coordinates.
  *   - CentriQ (Calibration-Free Quantization of DiTs via Exact Mean Centering),
- *     arXiv abstract: centre each token before the rotation, restore the mean
- *     exactly through a rank-1 full-precision branch; closed-form per-token scale.
+ *     arXiv abstract: tokens are centred before the rotation and their means come
+ *     back as a rank-1 fp16 term mu wbar^T; the per-token scale has a closed form.
  *   - SVDQuant explainer, §3: a 16-bit low-rank branch L1 L2 added to the 4-bit
  *     product, fused into the 4-bit kernel so it costs no separate pass; the branch
  *     holds the weight's leading singular directions, the residual is quantized.
@@ -27,12 +27,17 @@
  *   MXFP4 scales u8 [M][K/32]   E8M0 bytes (e + 127), one per 32 consecutive values
  *   LM4 scales  f32 [M]         per-token scale
  *   mu    fp16 [M]              per-token mean (centring)
- *   W     fp16 [N][K]           weights in the [out][in] layout (row n = column n of
- *                               the W in Y = XW)
+ *   W     fp16 [K][N]           weights as in Y = X W (kq_fold_inverse_into_weights);
+ *   Wt    fp16 [N][K]           the same weights in the [out][in] layout
+ *                               (kq_fold_inverse_into_weights_nk, kq_svd_lowrank)
  *   wcodes u8 [N][K/2] (MXFP4) or [N][K/4] (2-bit, element 4i in bits 0-1)
  *   wscales u8 [N][K/32] (MXFP4) or fp16 [N][K/32] (2-bit group scales)
  *   wbar  fp16 [N]              column sums of W (rank-1 mean restore)
- *   L1    fp16 [r][K], L2 fp16 [N][r]   low-rank factors, [out][in] layout
+ *   L1    fp16 [r][K], L2 fp16 [N][r]   low-rank factors in the [out][in] layout
+ *                               (X L1^T is the down-projection, T L2^T the up-projection:
+ *                               the transposes of an L1 [K][r], L2 [r][N] written as
+ *                               X L1 L2; rows are contiguous along the contracted
+ *                               dimension, which is how the matrix cores take them)
  *   Y     fp16 [M][N]
  *
  * Ownership: the caller allocates and owns every buffer; the library never
@@ -58,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 5
+#define KQ_ABI_VERSION 6
 
 typedef int32_t kq_status;
 enum {
@@ -68,7 +73,8 @@ enum {
   KQ_ERR_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
   KQ_ERR_UNSUPPORTED = 4,  /* unknown enum, or a size outside the supported range */
   KQ_ERR_VALUE = 5,        /* a transform factor is singular or not finite */
-  KQ_ERR_HIP = 6           /* a HIP launch failed */
+  KQ_ERR_HIP = 6,          /* a HIP launch failed */
+  KQ_ERR_WORKSPACE = 7     /* the workspace is missing or smaller than the call needs */
 };
 
 /* transform kinds */
@@ -151,21 +157,31 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
 
 /* Offline fold (KroQuant §01; OrbitQuant §03 W' = R^-1 W; CentriQ abstract):
  *   W' = P^-1 W (KRON: blockdiag(A^-1 (x) B^-1), the inverses computed on the host in
- *   double precision; RPBH: R^T), computed in float32 on the device, then each
- *   row n of W'^T quantized along K: fmt MXFP4 with the activation rule, or
- *   LM2_G32: s_g = fp16(RMS of the 32-group), 2-bit sign-magnitude code of w / s_g in
- *   the 4-level Lloyd-Max codebook.  wbar[n] = fp16(sum_k W[n][k]) if wbar != NULL.
- * W fp16 [N][K]; wcodes u8 [N][K/2] (MXFP4) or [N][K/4] (LM2); wscales u8 [N][K/32]
- * (MXFP4) or fp16 [N][K/32] (LM2).  Returns KQ_ERR_VALUE if A or B is singular. */
+ *   double precision; RPBH: R^T; DENSE_32 / KRON_4X8_BLOCKS: inverted on the device),
+ *   computed in float32 on the device, then each column n of W' (the weights of
+ *   output n) quantized along K: fmt MXFP4 with the activation rule, or LM2_G32:
+ *   s_g = fp16(RMS of the 32-group), 2-bit sign-magnitude code of w / s_g in the
+ *   4-level Lloyd-Max codebook.  wbar[n] = fp16(sum_k W[k][n]) (float64 sum) if
+ *   wbar != NULL: the column sums for the rank-1 mean restore.
+ * W fp16 [K][N] (row-major: W[k][n] at k*N + n); wcodes u8 [N][K/2] (MXFP4) or [N][K/4]
+ * (LM2); wscales u8 [N][K/32] (MXFP4) or fp16 [N][K/32] (LM2); wbar fp16 [N].
+ * Untimed: runs once per layer.  Returns KQ_ERR_VALUE if A or B is singular. */
 kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt,
-                                       const void* W, int64_t N, int64_t K,
+                                       const void* W, int64_t K, int64_t N,
                                        uint8_t* wcodes, void* wscales, void* wbar,
                                        hipStream_t stream);
+
+/* The same fold for weights given as Wt fp16 [N][K] (the [out][in] layout, Wt[n][k] =
+ * W[k][n]); outputs identical to kq_fold_inverse_into_weights on the same weights. */
+kq_status kq_fold_inverse_into_weights_nk(const kq_xform* xf, int32_t fmt,
+                                          const void* Wt, int64_t N, int64_t K,
+                                          uint8_t* wcodes, void* wscales, void* wbar,
+                                          hipStream_t stream);
 
 /* Low-rank down-projection of the 16-bit branch (SVDQuant explainer §3):
  *   T = fp16(X L1^T), fp32 accumulation on the fp16 matrix cores.
  * X fp16 [M][K] (the original activations: not centred, not transformed), L1 fp16 [r][K],
- * T fp16 [M][r] (caller-owned).  r in {16, 32, 64}; K % 32 == 0, K <= 2^20.
+ * T fp16 [M][r] (caller-owned).  r in {16, 32, 48, 64}; K % 32 == 0, K <= 2^20.
  * workspace (optional, caller-owned device memory, 16-byte aligned): when M is small
  *   against the device, K is split over several workgroups whose fp32 partials go to the
  *   workspace, and a second kernel sums them in a fixed order (results do not depend on
@@ -211,24 +227,49 @@ kq_status kq_svd_lowrank(const void* W, int64_t N, int64_t K, int32_t r, const f
                          int32_t iters, void* L1, void* L2, void* R, float* sigma, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
-/* The 4-bit linear with its full-precision branches, one kernel:
- *   Y = Xq . Wq^T  +  T L2^T  +  mu wbar^T            (fp32 accumulate, fp16 out)
+/* The 4-bit linear with its full-precision branches (KroQuant §01: Y = (XP)(P^-1 W);
+ * SVDQuant explainer §3: plus the 16-bit low-rank branch X L1 L2; CentriQ abstract: plus
+ * the rank-1 mean restore):
+ *   Y = Xq . Wq^T  +  (X L1^T) L2^T  +  mu wbar^T          (fp32 accumulate, fp16 out)
  * fmt MXFP4: Xq, Wq MXFP4 (xscales u8 [M][K/32], wscales u8 [N][K/32]); products on
  *   the scaled-FP4 matrix cores, each block pair scaled by 2^(ex+ew).  K % 128 == 0.
  * fmt LM2_G32 (W2A4): Xq per-token Lloyd-Max 4-bit (xscales f32 [M]), Wq 2-bit groups
  *   (wcodes u8 [N][K/4], wscales fp16 [N][K/32]); the codebooks are the library's own
  *   (kq_lloyd_max_levels).  K % 32 == 0.  No low-rank or rank-1 branch (r must be 0).
- * Low-rank branch (SVDQuant §3): T fp16 [M][r] from kq_lowrank_down, L2 fp16 [N][r],
- *   r in {0, 16, 32, 64} (0: T and L2 ignored); T L2^T enters the fp32 accumulators
- *   before the 4-bit product, so the branch costs no extra pass over Y.
- * Rank-1 restore (CentriQ): mu fp16 [M] and wbar fp16 [N], both or neither.
- * N % 16 == 0; M <= 2^30, N and K <= 2^20.  Y fp16 [M][N]. */
+ * Low-rank branch: X fp16 [M][K] (the original activations, neither centred nor
+ *   transformed), L1 fp16 [r][K], L2 fp16 [N][r], r in {0, 16, 32, 48, 64} (0: X, L1,
+ *   L2 ignored and may be NULL).  The down-projection T = X L1^T runs first on the
+ *   stream (as kq_lowrank_down, T held in the workspace), then one GEMM kernel whose
+ *   accumulators start from T L2^T, so the branch adds no pass over Y.
+ *   T is rounded to fp16 (the up-projection is an fp16 matrix-core product; the
+ *   explainer keeps the branch in 16 bits): the branch then carries a relative error
+ *   of at most 2^-11 per T entry, far below the 4-bit product's.
+ * Rank-1 restore: mu fp16 [M] and wbar fp16 [N], both or neither.
+ * workspace: caller-owned device memory, 256-byte aligned, of at least
+ *   kq_w4a4_linear_workspace_bytes(M, r) bytes (0 when r == 0; NULL allowed then).  It
+ *   holds T and the split-K partial sums of the down-projection.  The library
+ *   allocates nothing.  Calls that share a workspace must not overlap.
+ * N % 16 == 0; M <= 2^30, N and K <= 2^20.  Y fp16 [M][N].  Pointers 16-byte aligned,
+ *   except xscales and wscales (4) and mu (2).
+ * Errors: KQ_ERR_WORKSPACE if r > 0 and the workspace is NULL or too small. */
+size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r);
 kq_status kq_w4a4_linear(int32_t fmt,
                          const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
                          const uint8_t* wcodes, const void* wscales, int64_t N,
-                         const void* T, const void* L2, int32_t r,
+                         const void* X, const void* L1, const void* L2, int32_t r,
                          const void* mu, const void* wbar,
-                         void* Y, hipStream_t stream);
+                         void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same linear with the down-projection already done: T fp16 [M][r] from
+ * kq_lowrank_down or kq_transform_quantize_lowrank (caller-owned), L2 fp16 [N][r],
+ * r in {0, 16, 32, 48, 64} (0: T and L2 ignored).  One kernel launch; no workspace.
+ * Other arguments and rules as kq_w4a4_linear. */
+kq_status kq_w4a4_linear_t(int32_t fmt,
+                           const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                           const uint8_t* wcodes, const void* wscales, int64_t N,
+                           const void* T, const void* L2, int32_t r,
+                           const void* mu, const void* wbar,
+                           void* Y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,10 @@ U = 2.0 ** -24
 #      float32, the centring applied to output 0 of each block afterwards (subtracting
 #      32 mu), then the rounded 1/sqrt(32) and the final product;
 #  RPBH, Lloyd-Max (vector units): five butterfly stages, 1/sqrt(32), the product, and
-#      the centring subtraction.
+#      the centring subtraction;
+#  identity without centring (matrix cores, with or without the power-of-two shift): each
+#      output is one fp16 input times 1.0 plus exact zeros, so the float32 value is exact
+#      and no tie is allowed (n = 0).
 def _path(kind, center, fmt):
     if kind in ("dense", "kron_blocks"):
         return ("uncentred", 80)
@@ -25,7 +28,7 @@ def _path(kind, center, fmt):
         return ("uncentred", 80) if (not center and fmt == "mxfp4") else ("centred", 14)
     if kind == "rpbh":
         return ("uncentred", 36) if fmt == "mxfp4" else ("centred", 9)
-    return ("uncentred", 2) if (not center and fmt == "mxfp4") else ("centred", 2)
+    return ("uncentred", 0) if (not center and fmt == "mxfp4") else ("centred", 2)
 
 
 def abs_transform(x_abs, xform):

@@ -31,7 +31,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert {"kq_transform_quantize", "kq_w4a4_linear", "kq_fold_inverse_into_weights"} <= set(names)
+    assert {"kq_transform_quantize", "kq_w4a4_linear", "kq_fold_inverse_into_weights",
+            "kq_w4a4_linear_workspace_bytes", "kq_w4a4_linear_t", "kq_fold_inverse_into_weights_nk",
+            "kq_abi_version", "kq_status_str"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", kq.lib_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (kq_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -41,8 +43,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 5
-    for s in range(0, 7):
+    assert kq.abi_version() == 6
+    for s in range(0, 8):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
 
@@ -100,14 +102,14 @@ def test_pts_validation(lib):
     xf = _xf()
     xf.pts = 0x100008
     assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 3          # misaligned pts
-    assert g(ctypes.byref(xf), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 3
+    assert g(ctypes.byref(xf), 0, FAKE, 64, 8, FAKE, FAKE, None, None) == 3
     xf.pts = 0x100000
     assert f(ctypes.byref(xf), 0, 1, FAKE, 4, 64, FAKE, FAKE, FAKE, None) == 4          # with centring
     assert f(ctypes.byref(xf), 1, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with LM4
     rp = _xf(kind=2)
     rp.perm, rp.sign, rp.pts = 0x100000, 0x100000, 0x100000
     assert f(ctypes.byref(rp), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4          # with RPBH
-    assert g(ctypes.byref(rp), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 4
+    assert g(ctypes.byref(rp), 0, FAKE, 64, 8, FAKE, FAKE, None, None) == 4
 
 
 def test_kron_blocks_validation(lib):
@@ -116,7 +118,7 @@ def test_kron_blocks_validation(lib):
     f, g = lib.kq_transform_quantize, lib.kq_fold_inverse_into_weights
     xf = _xf(kind=4)
     assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 1          # NULL AB
-    assert g(ctypes.byref(xf), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 1
+    assert g(ctypes.byref(xf), 0, FAKE, 64, 8, FAKE, FAKE, None, None) == 1
     xf.AB = 0x100008
     assert f(ctypes.byref(xf), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 3          # misaligned
     xf.AB = 0x100000
@@ -126,11 +128,19 @@ def test_kron_blocks_validation(lib):
     assert f(ctypes.byref(bad), 0, 0, FAKE, 4, 64, FAKE, FAKE, None, None) == 4
 
 
-def test_fold_validation(lib):
-    f = lib.kq_fold_inverse_into_weights
+@pytest.mark.parametrize("which", ["kq_fold_inverse_into_weights", "kq_fold_inverse_into_weights_nk"])
+def test_fold_validation(lib, which):
+    """Both weight layouts: W [K][N] takes (K, N), Wt [N][K] takes (N, K)."""
+    g = getattr(lib, which)
+
+    def f(xf, fmt, W, N, K, *rest):
+        return g(xf, fmt, W, K, N, *rest) if which == "kq_fold_inverse_into_weights" else g(xf, fmt, W, N, K, *rest)
     xf = _xf()
     assert f(ctypes.byref(xf), 0, None, 8, 64, FAKE, FAKE, None, None) == 1
     assert f(ctypes.byref(xf), 1, FAKE, 8, 64, FAKE, FAKE, None, None) == 4             # LM4 is not a weight format
+    assert f(ctypes.byref(xf), 0, FAKE, 8, 48, FAKE, FAKE, None, None) == 2             # K % 32
+    assert f(ctypes.byref(xf), 0, FAKE, 0, 64, FAKE, FAKE, None, None) == 2             # N < 1
+    assert f(ctypes.byref(xf), 0, FAKE_ODD, 8, 64, FAKE, FAKE, None, None) == 3
     sing = _xf()
     for i in range(16):
         sing.A[i] = 0.0
@@ -142,15 +152,10 @@ def test_fold_validation(lib):
     assert f(ctypes.byref(rank1), 0, FAKE, 8, 64, FAKE, FAKE, None, None) == 5
 
 
-def test_linear_validation(lib):
-    f = lib.kq_w4a4_linear
-    args = dict(fmt=0, xc=FAKE, xs=FAKE, M=16, K=256, wc=FAKE, wsc=FAKE, N=32, T=None, L2=None, r=0,
-                mu=None, wbar=None, Y=FAKE)
+_LIN = dict(fmt=0, xc=FAKE, xs=FAKE, M=16, K=256, wc=FAKE, wsc=FAKE, N=32, r=0, mu=None, wbar=None, Y=FAKE)
 
-    def call(**kw):
-        a = dict(args, **kw)
-        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["T"], a["L2"],
-                 a["r"], a["mu"], a["wbar"], a["Y"], None)
+
+def _common_linear_checks(call):
     assert call(Y=None) == 1
     assert call(N=0) == 2
     assert call(r=24) == 2
@@ -158,10 +163,57 @@ def test_linear_validation(lib):
     assert call(K=96) == 4                             # MXFP4 needs K % 128
     assert call(N=40) == 4                             # N % 16
     assert call(fmt=5) == 4
+    assert call(xc=FAKE_ODD) == 3
+    assert call(mu=FAKE, wbar=FAKE_ODD) == 3           # the column sums are 16-byte aligned
+
+
+def test_linear_t_validation(lib):
+    f = lib.kq_w4a4_linear_t
+
+    def call(**kw):
+        a = {**_LIN, "T": None, "L2": None, **kw}
+        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["T"], a["L2"],
+                 a["r"], a["mu"], a["wbar"], a["Y"], None)
+    _common_linear_checks(call)
     assert call(r=32) == 1                             # low rank without T/L2
     assert call(fmt=2, r=32, T=FAKE, L2=FAKE) == 4     # W2A4 has no low-rank branch
-    assert call(xc=FAKE_ODD) == 3
     assert call(r=32, T=FAKE_ODD, L2=FAKE) == 3
+
+
+def test_linear_validation(lib):
+    """The linear that runs the down-projection itself: X, L1, L2 and a workspace of at
+    least kq_w4a4_linear_workspace_bytes(M, r) bytes, 256-byte aligned."""
+    f = lib.kq_w4a4_linear
+    need = kq.w4a4_linear_workspace_bytes(16, 32)
+
+    def call(**kw):
+        a = {**_LIN, "X": None, "L1": None, "L2": None, "ws": None, "wn": 0, **kw}
+        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["X"], a["L1"], a["L2"],
+                 a["r"], a["mu"], a["wbar"], a["Y"], a["ws"], a["wn"], None)
+    _common_linear_checks(call)
+    lr = dict(r=32, X=FAKE, L1=FAKE, L2=FAKE, ws=FAKE, wn=need)
+    assert call(**dict(lr, X=None)) == 1               # low rank without X
+    assert call(**dict(lr, L2=None)) == 1
+    assert call(**dict(lr, ws=None)) == 7              # no workspace
+    assert call(**dict(lr, wn=need - 1)) == 7          # too small
+    assert call(**dict(lr, ws=ctypes.c_void_p(0x100010))) == 3
+    assert call(**dict(lr, L1=FAKE_ODD)) == 3
+    assert call(**dict(lr, fmt=2)) == 4                # W2A4 has no low-rank branch
+
+
+def test_linear_workspace_size(lib):
+    """T (fp16, padded to 256 bytes) plus the split-K partial sums; 0 without a branch;
+    every rank the linear takes, 48 included; 0 for an invalid one."""
+    for M in (1, 300, 4608, 17550):
+        assert kq.w4a4_linear_workspace_bytes(M, 0) == 0
+        for r in (16, 32, 48, 64):
+            n = kq.w4a4_linear_workspace_bytes(M, r)
+            assert n >= M * r * 2 and n % 256 == 0 or n >= M * r * 2
+        assert kq.w4a4_linear_workspace_bytes(M, 24) == 0
+    assert kq.w4a4_linear_workspace_bytes(0, 32) == 0
+    # at least what the split down-projection alone uses at any K
+    for K in (128, 3072, 12288):
+        assert kq.w4a4_linear_workspace_bytes(4608, 32) >= kq.lowrank_down_workspace_bytes(4608, K, 32) + 4608 * 32 * 2
 
 
 def test_lowrank_validation(lib):
@@ -229,6 +281,7 @@ def test_lowrank_workspace_size(lib):
     assert n > 0 and n % (4608 * 32 * 4) == 0
     assert kq.lowrank_down_workspace_bytes(4608, 128, 32) == 0          # one chunk of K: nothing to split
     assert kq.lowrank_down_workspace_bytes(4608, 3072, 8) == 0          # invalid rank
+    assert kq.lowrank_down_workspace_bytes(4608, 3072, 48) % (4608 * 48 * 4) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -90,8 +90,8 @@ def test_fused_linear(kq):
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, T = kq.transform_quantize_lowrank(X, dxf, torch.from_numpy(L1).cuda())
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()
     ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
                              None, None)

@@ -24,20 +24,17 @@ def _fold(kq, W16, xf, fmt):
     import torch
     W = torch.from_numpy(W16).cuda()
     dxf = _dev_xform(kq, torch, xf, W16.shape[1])
-    wc, ws, wbar = kq.fold_inverse_into_weights(W, dxf, fmt=fmt)
+    wc, ws, wbar = kq.fold_inverse_into_weights_nk(W, dxf, fmt=fmt)
     torch.cuda.synchronize()
     return wc, ws, wbar
 
 
 def _wbar_check(W16, wbar_gpu):
+    """The fold's column sums against the oracle's: the device sums in float64 and rounds
+    once, so they must be the same fp16 values (a float64 summation-order difference could
+    only matter for a sum within 2^-40 of an fp16 rounding midpoint; none is allowed)."""
     ref = pipeline.column_sums_f16(W16)
-    exact = W16.astype(np.float64).sum(axis=1)
-    bad = np.flatnonzero(ref.view(np.uint16) != wbar_gpu.view(np.uint16))
-    for n in bad:   # only adjacent fp16 roundings of a sum within float32 error of their midpoint
-        a, b = float(ref[n]), float(wbar_gpu[n])
-        mid = 0.5 * (a + b)
-        bound = float(ties.gamma_tau(64 + W16.shape[1] // 64, np.sum(np.abs(W16[n].astype(np.float64)))))
-        assert abs(exact[n] - mid) <= bound and np.nextafter(np.float16(min(a, b)), np.float16(np.inf)) == max(a, b)
+    assert np.array_equal(ref.view(np.uint16), wbar_gpu.view(np.uint16))
 
 
 @pytest.mark.parametrize("cfg,layer,nrows", [(0, 0, 1152), (1, 1, 200), (3, 2, 96), (4, 0, 160), (1, 3, 80)])
@@ -86,9 +83,9 @@ def test_w4a4_dense_block_linear(kq):
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
     T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()
     ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
                              None, None)
@@ -143,9 +140,9 @@ def test_w4a4_pts_linear(kq, kind):
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
     T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()
     ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
                              None, None)
@@ -188,9 +185,9 @@ def test_w4a4_kron_blocks_linear(kq):
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, _ = kq.transform_quantize(X, dxf, fmt="mxfp4")
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
     T = kq.lowrank_down(X, torch.from_numpy(L1).cuda())
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()
     ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
                              None, None)
@@ -248,11 +245,11 @@ def _linear_case(kq, cfg, layer, M, N=None, rank=None, with_mu=None, K=None, see
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, mu = kq.transform_quantize(X, dxf, fmt="mxfp4", center=center)
-    wc, ws, wbar = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+    wc, ws, wbar = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
     L1d = None if L1 is None else torch.from_numpy(np.ascontiguousarray(L1)).cuda()
     L2d = None if L2 is None else torch.from_numpy(L2).cuda()
     T = kq.lowrank_down(X, L1d) if r else None
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=L2d, mu=mu, wbar=wbar if center else None)
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=L2d, mu=mu, wbar=wbar if center else None)
     torch.cuda.synchronize()
     return dict(X16=X16, W16=W16, L1=L1, L2=L2, xc=xc.cpu().numpy(), xs=xs.cpu().numpy(), wc=wc.cpu().numpy(),
                 ws=ws.cpu().numpy(), mu=None if mu is None else mu.cpu().numpy(),
@@ -304,7 +301,7 @@ def _check_lowrank(kq, M, K, r, seed=7, workspace="default"):
 
 @pytest.mark.parametrize("M,K,r", [(1, 128, 32), (77, 1152, 16), (301, 3072, 32), (40, 12288, 64), (19, 2240, 32),
                                    (1000, 3072, 64), (4608, 3072, 16), (4608, 12288, 32), (4096, 3072, 64),
-                                   (4103, 96, 32), (17550, 3072, 32)])
+                                   (4103, 96, 32), (17550, 3072, 32), (300, 3072, 48), (4608, 12288, 48)])
 def test_lowrank_down_matches_oracle(kq, M, K, r):
     """Ranks 16, 32, 64; one row to the video workload's 17550 rows; K from 96 (one
     partial chunk) to 12288; ragged last row blocks."""
@@ -358,8 +355,8 @@ def test_w2a4_linear_matches_oracle(kq):
         xf = synth.xform_for(2, layer, K)
         dxf = _dev_xform(kq, torch, xf, K)
         xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
-        wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
-        Y = kq.w4a4_linear(xc, xs, wc, ws, fmt="lm2")
+        wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+        Y = kq.w4a4_linear_t(xc, xs, wc, ws, fmt="lm2")
         torch.cuda.synchronize()
         ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy())
         err = linear.rel_frobenius(Y.cpu().numpy(), ref)
@@ -381,8 +378,8 @@ def test_w2a4_full_size_forms(kq, layer, M, Nr):
     xf = synth.xform_for(2, layer, K)
     dxf = _dev_xform(kq, torch, xf, K)
     xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
-    Y = kq.w4a4_linear(xc, xs, wc, ws, fmt="lm2")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, fmt="lm2")
     torch.cuda.synchronize()
     rows = np.array(sorted(set(range(0, M, 61)) | {0, 127, 128, 255, 256, M - 129, M - 128, M - 1} - {-1}))
     rows = rows[(rows >= 0) & (rows < M)]
@@ -458,7 +455,7 @@ def test_repeated_calls_bit_identical(kq):
     for _ in range(3):
         xc, xs, mu = kq.transform_quantize(X, dxf, fmt="mxfp4", center=True)
         codes.append((xc.cpu().numpy(), xs.cpu().numpy(), mu.cpu().numpy().view(np.uint16)))
-        Y = kq.w4a4_linear(*ops[:4], T=ops[4], L2=ops[5], mu=ops[6], wbar=ops[7])
+        Y = kq.w4a4_linear_t(*ops[:4], T=ops[4], L2=ops[5], mu=ops[6], wbar=ops[7])
         outs.append(Y.cpu().numpy().view(np.uint16))
     torch.cuda.synchronize()
     for c in codes[1:]:
@@ -466,3 +463,160 @@ def test_repeated_calls_bit_identical(kq):
     for y in outs[1:]:
         assert np.array_equal(outs[0], y)
     assert np.array_equal(outs[0], d["Y"].view(np.uint16))
+
+
+# ----------------------------------------------------------------- the boundary's own forms
+
+def test_fold_kn_layout_matches_nk(kq):
+    """kq_fold_inverse_into_weights takes W [K][N] (Y = X W); its codes, scales and column
+    sums are byte-identical to the [N][K] form on the same weights, and match the oracle."""
+    import torch
+    for cfg, layer, nrows in ((3, 0, 200), (4, 0, 96), (1, 3, 80)):
+        c = synth.CONFIGS[cfg]
+        _, K, N = c["layers"][layer]
+        W16, _, _ = synth.weights(K, N, cfg, layer, 0)
+        W16 = np.ascontiguousarray(W16[:nrows])                 # [N][K]
+        xf = synth.xform_for(cfg, layer, K)
+        dxf = _dev_xform(kq, torch, xf, K)
+        a = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="mxfp4")
+        b = kq.fold_inverse_into_weights(torch.from_numpy(np.ascontiguousarray(W16.T)).cuda(), dxf, fmt="mxfp4")
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u, v)
+        _wbar_check(W16, b[2].cpu().numpy())
+    # and the 2-bit weight format
+    c = synth.CONFIGS[2]
+    _, K, N = c["layers"][0]
+    W16 = np.ascontiguousarray(synth.weights(K, N, 2, 0, 0)[0][:64])
+    dxf = _dev_xform(kq, torch, synth.xform_for(2, 0, K), K)
+    a = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="lm2")
+    b = kq.fold_inverse_into_weights(torch.from_numpy(np.ascontiguousarray(W16.T)).cuda(), dxf, fmt="lm2")
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def _x_form_case(kq, cfg, layer, M, r, with_mu, K=None, N=None):
+    """Operands for the linear that runs its own down-projection: the activation path on
+    the GPU, weights folded from [K][N]."""
+    import torch
+    c = synth.CONFIGS[cfg]
+    _, K0, N0 = c["layers"][layer]
+    K = K0 if K is None else K
+    N = N0 if N is None else N
+    X16 = synth.activations(M, K, cfg, c["sigma_mu"], c["frames"])
+    W16, L1, L2 = synth.weights(K, N, cfg, layer, max(r, 1))
+    xf = synth.xform_for(cfg, layer, K) if K == K0 else {"kind": "kron", "A": synth.kron_factors(cfg, layer)[0],
+                                                          "B": synth.kron_factors(cfg, layer)[1]}
+    dxf = _dev_xform(kq, torch, xf, K)
+    X = torch.from_numpy(X16).cuda()
+    xc, xs, mu = kq.transform_quantize(X, dxf, fmt="mxfp4", center=with_mu)
+    wc, ws, wbar = kq.fold_inverse_into_weights(torch.from_numpy(np.ascontiguousarray(W16.T)).cuda(), dxf)
+    L1d = torch.from_numpy(np.ascontiguousarray(L1[:r])).cuda() if r else None
+    L2d = torch.from_numpy(np.ascontiguousarray(L2[:, :r])).cuda() if r else None
+    return dict(X16=X16, X=X, L1=L1[:r] if r else None, L2=np.ascontiguousarray(L2[:, :r]) if r else None,
+                L1d=L1d, L2d=L2d, xc=xc, xs=xs, wc=wc, ws=ws, mu=mu, wbar=wbar if with_mu else None)
+
+
+@pytest.mark.parametrize("cfg,layer,M,r,with_mu", [(3, 0, 150, 32, True), (3, 2, 70, 48, True), (1, 1, 201, 16, False),
+                                                     (4, 0, 97, 64, False), (0, 0, 256, 0, False), (1, 3, 77, 48, False)])
+def test_w4a4_linear_x_form_matches_oracle(kq, cfg, layer, M, r, with_mu):
+    """kq_w4a4_linear with X, L1, L2 and a workspace: the down-projection runs inside the
+    call; every rank the boundary takes (0, 16, 32, 48, 64); against the oracle within
+    2e-3, and byte-identical to the down-projection call followed by the T form."""
+    import torch
+    d = _x_form_case(kq, cfg, layer, M, r, with_mu)
+    Y = kq.w4a4_linear(d["xc"], d["xs"], d["wc"], d["ws"], X=d["X"] if r else None, L1=d["L1d"], L2=d["L2d"],
+                       mu=d["mu"], wbar=d["wbar"])
+    T = kq.lowrank_down(d["X"], d["L1d"]) if r else None
+    Y2 = kq.w4a4_linear_t(d["xc"], d["xs"], d["wc"], d["ws"], T=T, L2=d["L2d"], mu=d["mu"], wbar=d["wbar"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    ref = linear.w4a4_linear(d["xc"].cpu().numpy(), d["xs"].cpu().numpy(), d["wc"].cpu().numpy(),
+                             d["ws"].cpu().numpy(), d["X16"] if r else None, d["L1"], d["L2"],
+                             None if d["mu"] is None else d["mu"].cpu().numpy(),
+                             None if d["wbar"] is None else d["wbar"].cpu().numpy())
+    err = linear.rel_frobenius(Y.cpu().numpy(), ref)
+    print(f"x-form cfg{cfg} layer{layer} M={M} r={r} mu={with_mu}: {err:.3e}")
+    assert err <= TOL
+
+
+def test_w4a4_linear_x_form_full_size_sampled(kq):
+    """The FLUX-like qkv at full size through the boundary's own form (M = 4608, K = 3072,
+    N = 9216, centred, rank 32), in the bench's launch configuration; sampled rows."""
+    import torch
+    d = _x_form_case(kq, 3, 0, 4608, 32, True)
+    ws = torch.empty((kq.w4a4_linear_workspace_bytes(4608, 32),), dtype=torch.uint8, device="cuda")
+    Y = kq.w4a4_linear(d["xc"], d["xs"], d["wc"], d["ws"], X=d["X"], L1=d["L1d"], L2=d["L2d"], mu=d["mu"],
+                       wbar=d["wbar"], workspace=ws)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(4608)
+    ref = linear.w4a4_linear(d["xc"].cpu().numpy(), d["xs"].cpu().numpy(), d["wc"].cpu().numpy(),
+                             d["ws"].cpu().numpy(), d["X16"], d["L1"], d["L2"], d["mu"].cpu().numpy(),
+                             d["wbar"].cpu().numpy(), rows=rows)
+    err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
+    print(f"x-form full size sampled: {err:.3e}")
+    assert err <= TOL
+
+
+def test_w4a4_linear_x_form_workspace_errors(kq):
+    """A workspace smaller than kq_w4a4_linear_workspace_bytes is refused before anything is
+    launched (KQ_ERR_WORKSPACE), and a sufficient one works."""
+    import torch
+    d = _x_form_case(kq, 3, 0, 64, 32, False)
+    need = kq.w4a4_linear_workspace_bytes(64, 32)
+    small = torch.empty((need - 256,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kq.KQError) as e:
+        kq.w4a4_linear(d["xc"], d["xs"], d["wc"], d["ws"], X=d["X"], L1=d["L1d"], L2=d["L2d"], workspace=small)
+    assert e.value.status == 7
+    ok = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    kq.w4a4_linear(d["xc"], d["xs"], d["wc"], d["ws"], X=d["X"], L1=d["L1d"], L2=d["L2d"], workspace=ok)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1801, 1807])
+def test_w4a4_large_tile_ragged_means(kq, M):
+    """The large-tile form with the rank-1 restore when the last 256-row tile holds a number
+    of rows that is not a multiple of 8 (odd, too): the means of the last rows reach the
+    epilogue; also with mu given as an offset view (2-byte aligned, not 16)."""
+    import torch
+    N, K = 4624, 1024
+    d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=32, with_mu=True)
+    rows = np.array(sorted(set(_sampled_rows(M)) | set(range(M - 9, M))))
+    err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
+    print(f"M={M}: {err:.3e}")
+    assert err <= TOL
+    # the same call with mu at an odd fp16 offset inside a larger buffer
+    buf = torch.zeros((M + 1,), dtype=torch.float16, device="cuda")
+    buf[1:] = torch.from_numpy(d["mu"]).cuda()
+    mu_view = buf[1:]
+    assert mu_view.data_ptr() % 16 != 0
+    ops = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (d["xc"], d["xs"], d["wc"], d["ws"], d["T"],
+                                                                       d["L2"], d["wbar"])]
+    Y2 = kq.w4a4_linear_t(*ops[:4], T=ops[4], L2=ops[5], mu=mu_view, wbar=ops[6])
+    torch.cuda.synchronize()
+    assert np.array_equal(Y2.cpu().numpy().view(np.uint16), d["Y"].view(np.uint16))
+
+
+def test_calls_on_a_non_current_stream(kq):
+    """Calls given another stream than torch's current one: their internally allocated
+    workspaces and outputs are kept alive for that stream (record_stream), and the
+    results equal those of the same calls on the current stream."""
+    import torch
+    M, K, r = 300, 3072, 32
+    X16 = synth.activations(M, K, 7, 2.0)
+    _, L1, _ = synth.weights(K, 16, 7, 0, r)
+    X = torch.from_numpy(X16).cuda()
+    L1d = torch.from_numpy(L1).cuda()
+    ref = kq.lowrank_down(X, L1d)
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        outs.append(kq.lowrank_down(X, L1d, stream=s))
+        # churn torch's allocator on the current stream meanwhile
+        junk = [torch.empty((1 << 20,), dtype=torch.uint8, device="cuda").fill_(7) for _ in range(8)]
+        del junk
+    s.synchronize()
+    torch.cuda.synchronize()
+    for t in outs:
+        assert torch.equal(t, ref)

@@ -75,8 +75,8 @@ def test_svd_then_fold_and_linear(kq):
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
     xc, xs, T = kq.transform_quantize_lowrank(X, dxf, torch.from_numpy(L1).cuda())
-    wc, ws, _ = kq.fold_inverse_into_weights(torch.from_numpy(R).cuda(), dxf, fmt="mxfp4")
-    Y = kq.w4a4_linear(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(R).cuda(), dxf, fmt="mxfp4")
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()
     ref = linear.w4a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), X16, L1, L2,
                              None, None)
@@ -84,8 +84,8 @@ def test_svd_then_fold_and_linear(kq):
     exact = X16.astype(np.float64) @ Wt16.astype(np.float64).T
     e_svd = linear.rel_frobenius(Y.cpu().numpy(), exact)
     # without extraction: all of W quantized, no branch
-    wc2, ws2, _ = kq.fold_inverse_into_weights(torch.from_numpy(Wt16).cuda(), dxf, fmt="mxfp4")
-    Y2 = kq.w4a4_linear(xc, xs, wc2, ws2)
+    wc2, ws2, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(Wt16).cuda(), dxf, fmt="mxfp4")
+    Y2 = kq.w4a4_linear_t(xc, xs, wc2, ws2)
     torch.cuda.synchronize()
     e_plain = linear.rel_frobenius(Y2.cpu().numpy(), exact)
     print(f"4-bit error against exact X W: with extraction {e_svd:.3e}, without {e_plain:.3e}")

@@ -192,6 +192,75 @@ def test_edge_rows(kq):
     assert float(mu[0]) == 3.25 and np.all(codes == 0) and np.all(scales == 0)
 
 
+def _crafted_e2m1_rows():
+    """fp16 rows whose values land exactly on the E2M1 decision points once divided by the
+    block's shared scale 2^e (e = floor(log2 max|x|) - 2): every rounding midpoint 0.25,
+    0.75, 1.25, 1.75, 2.5, 3.5, 5 with both signs, values in the saturation band (6, 8),
+    negative values that round to zero (code 0x8 by the sign rule), signed zeros, blocks
+    whose maximum is exactly 2^k and one fp16 step below 2^k, and an all-zero block; at
+    shared exponents from the fp16 subnormal range to near its top."""
+    rng = np.random.default_rng(41)
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    sat = [6.5, 7.0, 7.5, 7.9921875]
+    grid = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    blocks = []
+    for e in (-14, -9, -1, 0, 3, 12) * 6:
+        base = [4.0] + mids + [-m for m in mids] + sat[:2] + [-v for v in sat[2:]] + \
+               [-0.125, -0.25, -0.0, 0.0, -0.2421875, 0.125] + [-g for g in grid]
+        assert len(base) == 32
+        for _ in range(3):
+            blocks.append(np.ldexp(np.array(rng.permutation(base), dtype=np.float64), e))
+        k = e + 2
+        top = np.float16(np.ldexp(1.0, k))
+        below = np.nextafter(top, np.float16(0))
+        for mx in (float(top), float(below)):           # block maximum 2^k and one fp16 step below
+            b = np.ldexp(np.array(rng.permutation(mids + [-m for m in mids] + grid + [-g for g in grid] +
+                                                   [0.0, -0.0, 0.25, -0.25]), dtype=np.float64), e - 1)
+            b[rng.integers(32)] = -mx if rng.integers(2) else mx
+            blocks.append(b)
+    blocks.append(np.zeros(32))
+    blocks.append(np.array([-0.0] * 32))
+    while len(blocks) % 8:
+        blocks.append(np.ldexp(np.array(rng.permutation([4.0] + mids + [-m for m in mids] + [0.0] * 17)), 2))
+    rows = np.concatenate(blocks).reshape(-1, 256)
+    x16 = rows.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), rows)      # every value is an fp16 number
+    return x16
+
+
+def test_e2m1_conversion_at_its_decision_points(kq):
+    """The hardware E2M1 conversion on the identity path (exact float32 inputs, so no tie
+    is allowed): codes and E8M0 bytes bit-equal to the oracle's round-to-nearest-even,
+    saturating, sign-preserving rule at every decision point."""
+    X16 = _crafted_e2m1_rows()
+    xf = {"kind": "none"}
+    codes, scales, _ = _run(kq, X16, xf, "mxfp4", False)
+    ref = pipeline.transform_quantize(X16, xf, "mxfp4")
+    got = mxfp4.unpack_nibbles(codes)
+    bad = np.argwhere(got != ref["codes_unpacked"])
+    print("crafted E2M1 blocks:", X16.shape, "mismatches", len(bad),
+          [(int(m), int(k), float(X16[m, k]), int(got[m, k]), int(ref["codes_unpacked"][m, k])) for m, k in bad[:8]])
+    assert len(bad) == 0
+    assert np.array_equal(scales, ref["scales"])
+    # the contract's corner cases, read off directly
+    nib = got.reshape(-1, 32)
+    xs = X16.astype(np.float64).reshape(-1, 32)
+    sb = scales.reshape(-1).astype(np.int64)
+    for b in range(len(xs)):
+        e = sb[b] - 127
+        s = np.ldexp(xs[b], -int(e)) if sb[b] else xs[b] * 0
+        for v, c in zip(s, nib[b]):
+            if v == 0.0:
+                assert c == 0                               # exact zeros of either sign: code 0
+            elif -0.25 <= v < 0:
+                assert c == 0x8                             # negative, rounds to zero
+            elif abs(v) >= 6.0:
+                assert c & 7 == 7                           # saturates at 6
+        amax = float(np.max(np.abs(xs[b])))
+        if amax > 0:
+            assert sb[b] == 127 + int(np.floor(np.log2(amax))) - 2
+
+
 def test_single_row_and_ragged_block_count(kq):
     """M*K/32 not a multiple of 16 blocks (streaming kernel's ragged last chunk)."""
     A, B = synth.kron_factors(2, 0)

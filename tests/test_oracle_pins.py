@@ -632,6 +632,99 @@ def test_tie_classifier_catches_planted_errors():
     assert any(err[0] == "scale" for err in rep["errors"])
 
 
+def test_lm4_tie_classifier_catches_planted_errors():
+    """The Lloyd-Max classifier: exact codes pass; a code flipped on a value far from every
+    threshold is an error; a scale outside its bound is an error; a value on a threshold
+    with a "kernel" code on either side is a tie only when the error budget reaches it;
+    and the budget is not wider than the bound it is given (a value a few budgets away
+    from the threshold, flipped across it, is an error)."""
+    rng = np.random.default_rng(31)
+    y = rng.standard_normal((3, 256))
+    codes, s = lloyd_max.lm4_token_quantize(y)
+    thr = lloyd_max.thresholds(lloyd_max.LEVELS16)
+    tau = np.full(y.shape, 1e-9)
+    rel = 1e-7
+    rep = ties.classify_lm4(codes, s, y, tau, rel)
+    assert rep["errors"] == [] and rep["code_mismatch"] == 0 and rep["scale_errors"] == 0
+    # a non-tie flip: the value with the largest distance to any threshold, moved one level
+    v = y / s.astype(np.float64)[:, None]
+    dist = np.min(np.abs(np.abs(v)[..., None] - thr), axis=-1)
+    m, k = np.unravel_index(np.argmax(dist), v.shape)
+    bad = codes.copy()
+    bad[m, k] = (bad[m, k] & 8) | ((bad[m, k] & 7) ^ 1)
+    rep = ties.classify_lm4(bad, s, y, tau, rel)
+    assert len(rep["errors"]) == 1 and rep["errors"][0][0] == "code" and rep["code_ties"] == 0
+    # a scale off by far more than its bound
+    s_bad = s.copy()
+    s_bad[1] *= np.float32(1.001)
+    rep = ties.classify_lm4(codes, s_bad, y, tau, rel)
+    assert any(e[0] == "scale" and e[1] == 1 for e in rep["errors"])
+    # a value exactly on a threshold: the oracle takes the smaller magnitude; a kernel that
+    # took the larger one is a tie with an error budget, an error without one
+    y2 = rng.standard_normal((1, 64))
+    i = 5
+    for _ in range(50):           # y_i moves s_t: iterate to the fixed point of the stored scale
+        c2, s2v = lloyd_max.lm4_token_quantize(y2)
+        on = float(thr[3]) * float(s2v[0])
+        if y2[0, i] == on:
+            break
+        y2[0, i] = on
+    c2, s2v = lloyd_max.lm4_token_quantize(y2)
+    v_i = y2[0, i] / float(s2v[0])
+    assert abs(v_i - thr[3]) <= 4e-16 * thr[3]
+    alt = c2.copy()
+    alt[0, i] = 4 if int(c2[0, i]) == 3 else 3
+    rep = ties.classify_lm4(alt, s2v, y2, np.full(y2.shape, 1e-9), 1e-7)
+    assert rep["errors"] == [] and rep["code_ties"] == 1
+    rep = ties.classify_lm4(alt, s2v, y2, np.zeros(y2.shape), 0.0)
+    if abs(v_i - thr[3]) > 0:                       # off the threshold by rounding: an error
+        assert len(rep["errors"]) == 1
+    # a value five budgets beyond the threshold, coded on the other side: an error
+    t_abs = 1e-7
+    y3 = y2.copy()
+    d = float(s2v[0]) * (t_abs / float(s2v[0]) + abs(thr[3]) * (1e-7 + 2 * ties.U32))
+    y3[0, i] = on + 5 * d
+    c3, s3 = lloyd_max.lm4_token_quantize(y3)
+    alt3 = c3.copy()
+    alt3[0, i] = 3 if int(c3[0, i]) == 4 else 4
+    rep = ties.classify_lm4(alt3, s3, y3, np.full(y3.shape, t_abs), 1e-7)
+    assert len(rep["errors"]) == 1 and rep["code_ties"] == 0
+
+
+@pytest.mark.parametrize("kind", ["rpbh", "kron"])
+def test_fold_wbar_restores_the_mean(kind):
+    """CentriQ abstract: with x centred by its stored fp16 mean, the fold's own outputs --
+    W'^T and the fp16 column sums wbar -- give back x W:
+        (x - mu 1^T) P . (P^-1 W) + mu wbar^T = x W
+    up to the fp16 rounding of wbar, which bounds the residual by |mu| |wbar - 1^T W|.
+    A wbar taken from the folded W' (a plausible slip) breaks the identity."""
+    rng = np.random.default_rng(32)
+    K, N, M = 256, 48, 10
+    X = (rng.standard_normal((M, K)) + rng.normal(0, 4, (M, 1))).astype(np.float16)
+    Wt = (rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float16)
+    if kind == "rpbh":
+        xf = {"kind": "rpbh", "perm": rng.permutation(K), "sign": rng.choice([-1, 1], K)}
+    else:
+        A = rng.standard_normal((4, 4)) + 2 * np.eye(4)
+        B = rng.standard_normal((8, 8)) + 3 * np.eye(8)
+        xf = {"kind": "kron", "A": A.astype(np.float32), "B": B.astype(np.float32)}
+    fw = pipeline.fold_weights(Wt, xf, "mxfp4")
+    a = pipeline.transform_quantize(X, xf, "mxfp4", center=True)
+    mu = a["mu"].astype(np.float64)
+    rhs = X.astype(np.float64) @ Wt.astype(np.float64).T
+    lhs = a["y"] @ fw["wt"].T + mu[:, None] * fw["wbar"].astype(np.float64)[None, :]
+    exact_wbar = Wt.astype(np.float64).sum(axis=1)
+    bound = np.abs(mu)[:, None] * np.abs(fw["wbar"].astype(np.float64) - exact_wbar)[None, :]
+    assert np.all(np.abs(lhs - rhs) <= bound + 1e-9 * np.max(np.abs(rhs)))
+    # the same identity with exact wbar holds to fp64 rounding
+    lhs64 = a["y"] @ fw["wt"].T + mu[:, None] * exact_wbar[None, :]
+    assert np.linalg.norm(lhs64 - rhs) <= 1e-12 * np.linalg.norm(rhs)
+    # wbar from the folded weights: fails by far more than the fp16 rounding
+    wrong = fw["wt"].sum(axis=1).astype(np.float16).astype(np.float64)
+    lhs_bad = a["y"] @ fw["wt"].T + mu[:, None] * wrong[None, :]
+    assert np.max(np.abs(lhs_bad - rhs)) > 100 * (np.max(bound) + 1e-9 * np.max(np.abs(rhs)))
+
+
 def test_mean_tie_rule():
     x = np.array([1.0, np.float16(1.0) + np.float16(2.0 ** -10)], dtype=np.float16)
     exact = float(np.mean(x.astype(np.float64)))     # the fp16 midpoint of 1 and 1+2^-10

@@ -7,17 +7,25 @@ library is missing: there is no fallback.
 
     xf = kq.Xform.kron(A, B, K)                     # or Xform.rpbh(perm, sign), Xform.none(K)
     codes, scales, mu = kq.transform_quantize(X, xf, fmt="mxfp4", center=False)
-    wcodes, wscales, wbar = kq.fold_inverse_into_weights(W, xf, fmt="mxfp4")
+    wcodes, wscales, wbar = kq.fold_inverse_into_weights(W, xf, fmt="mxfp4")     # W [K][N]
+    Y = kq.w4a4_linear(codes, scales, wcodes, wscales, X=X, L1=L1, L2=L2, mu=mu, wbar=wbar)
+    # or, with the down-projection done separately (or fused into the transform):
     T = kq.lowrank_down(X, L1)
-    Y = kq.w4a4_linear(codes, scales, wcodes, wscales, T=T, L2=L2, mu=mu, wbar=wbar)
+    Y = kq.w4a4_linear_t(codes, scales, wcodes, wscales, T=T, L2=L2, mu=mu, wbar=wbar)
+
+Outputs and workspaces that the binding allocates itself are marked as used on the stream
+the call runs on (``record_stream``), so torch's allocator does not hand their memory to
+another stream's work before the call has finished there.
 """
 
 import ctypes
 import os
 
 __all__ = ["load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
-           "transform_quantize", "fold_inverse_into_weights", "w4a4_linear",
-           "lowrank_down", "lowrank_down_workspace_bytes", "KQError"]
+           "transform_quantize", "fold_inverse_into_weights", "fold_inverse_into_weights_nk",
+           "w4a4_linear", "w4a4_linear_t", "w4a4_linear_workspace_bytes",
+           "lowrank_down", "lowrank_down_workspace_bytes", "transform_quantize_lowrank",
+           "svd_lowrank", "svd_lowrank_workspace_bytes", "KQError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -65,6 +73,8 @@ def load():
     lib.kq_transform_quantize.argtypes = [ctypes.POINTER(_XformC), i32, i32, vp, i64, i64, vp, vp, vp, vp]
     lib.kq_fold_inverse_into_weights.restype = i32
     lib.kq_fold_inverse_into_weights.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp]
+    lib.kq_fold_inverse_into_weights_nk.restype = i32
+    lib.kq_fold_inverse_into_weights_nk.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp]
     lib.kq_lowrank_down.restype = i32
     lib.kq_lowrank_down.argtypes = [vp, vp, i64, i64, i32, vp, vp, ctypes.c_size_t, vp]
     lib.kq_lowrank_down_workspace_bytes.restype = ctypes.c_size_t
@@ -76,8 +86,13 @@ def load():
     lib.kq_svd_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.kq_svd_lowrank.restype = i32
     lib.kq_svd_lowrank.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kq_w4a4_linear_workspace_bytes.restype = ctypes.c_size_t
+    lib.kq_w4a4_linear_workspace_bytes.argtypes = [i64, i32]
     lib.kq_w4a4_linear.restype = i32
-    lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
+    lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
+    lib.kq_w4a4_linear_t.restype = i32
+    lib.kq_w4a4_linear_t.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib
     return lib
 
@@ -114,6 +129,21 @@ def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_stream(stream, *made):
+    """Tensors this binding allocated on torch's current stream but handed to a call on
+    another stream: record that stream on them, so their memory is not reused before the
+    call has finished there (torch's caching allocator otherwise only waits for the
+    stream they were allocated on)."""
+    if stream is None:
+        return
+    torch = _torch()
+    if stream == torch.cuda.current_stream():
+        return
+    for t in made:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _check(t, name, dtype, shape=None):
@@ -225,19 +255,27 @@ def transform_quantize(X, xform, fmt="mxfp4", center=False, codes=None, scales=N
     if f not in (FMT_MXFP4, FMT_LM4):
         raise ValueError("fmt must be 'mxfp4' or 'lm4'")
     dev = X.device
-    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    made = []
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        made.append(codes)
     _check(codes, "codes", torch.uint8, (M, K // 2))
+    if scales is None:
+        scales = torch.empty((M, K // 32) if f == FMT_MXFP4 else (M,),
+                             dtype=torch.uint8 if f == FMT_MXFP4 else torch.float32, device=dev)
+        made.append(scales)
     if f == FMT_MXFP4:
-        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if scales is None else scales
         _check(scales, "scales", torch.uint8, (M, K // 32))
     else:
-        scales = torch.empty((M,), dtype=torch.float32, device=dev) if scales is None else scales
         _check(scales, "scales", torch.float32, (M,))
     if center:
-        mu = torch.empty((M,), dtype=torch.float16, device=dev) if mu is None else mu
+        if mu is None:
+            mu = torch.empty((M,), dtype=torch.float16, device=dev)
+            made.append(mu)
         _check(mu, "mu", torch.float16, (M,))
     else:
         mu = None
+    _on_stream(stream, *made)
     s = load().kq_transform_quantize(xform.c(), f, int(bool(center)), _ptr(X), M, K, _ptr(codes), _ptr(scales),
                                      _ptr(mu), _stream(stream))
     if s != KQ_OK:
@@ -245,12 +283,8 @@ def transform_quantize(X, xform, fmt="mxfp4", center=False, codes=None, scales=N
     return codes, scales, mu
 
 
-def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None):
-    """Offline: W' = P^-1 W, quantized along K.  W is fp16 [N][K] ([out][in]).
-    Returns (wcodes, wscales, wbar or None)."""
+def _fold(name, W, N, K, xform, fmt, with_wbar, stream):
     torch = _torch()
-    _check(W, "W", torch.float16)
-    N, K = W.shape
     f = _FMT[fmt]
     dev = W.device
     if f == FMT_MXFP4:
@@ -262,11 +296,36 @@ def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None
     else:
         raise ValueError("fmt must be 'mxfp4' or 'lm2'")
     wbar = torch.empty((N,), dtype=torch.float16, device=dev) if with_wbar else None
-    s = load().kq_fold_inverse_into_weights(xform.c(), f, _ptr(W), N, K, _ptr(wcodes), _ptr(wscales), _ptr(wbar),
-                                            _stream(stream))
+    _on_stream(stream, wcodes, wscales, wbar)
+    fn = getattr(load(), name)
+    if name == "kq_fold_inverse_into_weights":
+        s = fn(xform.c(), f, _ptr(W), K, N, _ptr(wcodes), _ptr(wscales), _ptr(wbar), _stream(stream))
+    else:
+        s = fn(xform.c(), f, _ptr(W), N, K, _ptr(wcodes), _ptr(wscales), _ptr(wbar), _stream(stream))
     if s != KQ_OK:
-        raise KQError(s, "kq_fold_inverse_into_weights")
+        raise KQError(s, name)
     return wcodes, wscales, wbar
+
+
+def fold_inverse_into_weights(W, xform, fmt="mxfp4", with_wbar=True, stream=None):
+    """Offline: W' = P^-1 W, quantized along K.  W is fp16 [K][N] (Y = X W).
+    Returns (wcodes [N][K/2], wscales [N][K/32], wbar [N] or None)."""
+    torch = _torch()
+    _check(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [K, N]")
+    K, N = W.shape
+    return _fold("kq_fold_inverse_into_weights", W, N, K, xform, fmt, with_wbar, stream)
+
+
+def fold_inverse_into_weights_nk(Wt, xform, fmt="mxfp4", with_wbar=True, stream=None):
+    """The same fold for weights in the [out][in] layout: Wt is fp16 [N][K]."""
+    torch = _torch()
+    _check(Wt, "Wt", torch.float16)
+    if Wt.dim() != 2:
+        raise ValueError("Wt must be 2-D [N, K]")
+    N, K = Wt.shape
+    return _fold("kq_fold_inverse_into_weights_nk", Wt, N, K, xform, fmt, with_wbar, stream)
 
 
 def lowrank_down_workspace_bytes(M, K, r):
@@ -283,13 +342,18 @@ def lowrank_down(X, L1, T=None, workspace=None, stream=None):
     M, K = X.shape
     r = L1.shape[0]
     _check(L1, "L1", torch.float16, (r, K))
-    T = torch.empty((M, r), dtype=torch.float16, device=X.device) if T is None else T
+    made = []
+    if T is None:
+        T = torch.empty((M, r), dtype=torch.float16, device=X.device)
+        made.append(T)
     _check(T, "T", torch.float16, (M, r))
     if workspace is None:
         nb = lowrank_down_workspace_bytes(M, K, r)
         workspace = torch.empty((nb,), dtype=torch.uint8, device=X.device) if nb else None
+        made.append(workspace)
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
+    _on_stream(stream, *made)
     wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     s = load().kq_lowrank_down(_ptr(X), _ptr(L1), M, K, r, _ptr(T), wp, wn, _stream(stream))
     if s != KQ_OK:
@@ -308,17 +372,26 @@ def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, wo
     r = L1.shape[0]
     _check(L1, "L1", torch.float16, (r, K))
     dev = X.device
-    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    made = []
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        made.append(codes)
     _check(codes, "codes", torch.uint8, (M, K // 2))
-    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        made.append(scales)
     _check(scales, "scales", torch.uint8, (M, K // 32))
-    T = torch.empty((M, r), dtype=torch.float16, device=dev) if T is None else T
+    if T is None:
+        T = torch.empty((M, r), dtype=torch.float16, device=dev)
+        made.append(T)
     _check(T, "T", torch.float16, (M, r))
     if workspace is None:
         nb = lowrank_down_workspace_bytes(M, K, r)
         workspace = torch.empty((nb,), dtype=torch.uint8, device=dev) if nb else None
+        made.append(workspace)
     if workspace is not None:
         _check(workspace, "workspace", torch.uint8)
+    _on_stream(stream, *made)
     wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     s = load().kq_transform_quantize_lowrank(xform.c(), _ptr(X), M, K, _ptr(codes), _ptr(scales), _ptr(L1), r,
                                              _ptr(T), wp, wn, _stream(stream))
@@ -342,18 +415,25 @@ def svd_lowrank(W, r, omega, iters=4, L1=None, L2=None, R=None, sigma=None, work
         raise ValueError("omega must be [K, l]")
     l = omega.shape[1]
     dev = W.device
-    L1 = torch.empty((r, K), dtype=torch.float16, device=dev) if L1 is None else L1
-    L2 = torch.empty((N, r), dtype=torch.float16, device=dev) if L2 is None else L2
-    R = torch.empty((N, K), dtype=torch.float16, device=dev) if R is None else R
-    sigma = torch.empty((r,), dtype=torch.float32, device=dev) if sigma is None else sigma
+    made = []
+
+    def _new(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        made.append(t)
+        return t
+    L1 = _new((r, K), torch.float16) if L1 is None else L1
+    L2 = _new((N, r), torch.float16) if L2 is None else L2
+    R = _new((N, K), torch.float16) if R is None else R
+    sigma = _new((r,), torch.float32) if sigma is None else sigma
     _check(L1, "L1", torch.float16, (r, K))
     _check(L2, "L2", torch.float16, (N, r))
     _check(R, "R", torch.float16, (N, K))
     _check(sigma, "sigma", torch.float32, (r,))
     nb = svd_lowrank_workspace_bytes(N, K, r, l)
     if workspace is None:
-        workspace = torch.empty((max(nb, 256),), dtype=torch.uint8, device=dev)
+        workspace = _new((max(nb, 256),), torch.uint8)
     _check(workspace, "workspace", torch.uint8)
+    _on_stream(stream, *made)
     s = load().kq_svd_lowrank(_ptr(W), N, K, r, _ptr(omega), l, int(iters), _ptr(L1), _ptr(L2), _ptr(R),
                               _ptr(sigma), _ptr(workspace), workspace.numel(), _stream(stream))
     if s != KQ_OK:
@@ -361,9 +441,7 @@ def svd_lowrank(W, r, omega, iters=4, L1=None, L2=None, R=None, sigma=None, work
     return L1, L2, R, sigma
 
 
-def w4a4_linear(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar=None,
-                fmt="mxfp4", Y=None, stream=None):
-    """Y = Xq Wq^T + T L2^T + mu wbar^T (fp16 [M][N]).  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4)."""
+def _linear_operands(xcodes, xscales, wcodes, wscales, fmt):
     torch = _torch()
     f = _FMT[fmt]
     _check(xcodes, "xcodes", torch.uint8)
@@ -377,18 +455,74 @@ def w4a4_linear(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar
     else:
         _check(xscales, "xscales", torch.float32, (M,))
         _check(wscales, "wscales", torch.float16, (N, K // 32))
+    return f, M, K, N
+
+
+def _linear_tail(M, N, mu, wbar, Y, dev):
+    torch = _torch()
+    if mu is not None:
+        _check(mu, "mu", torch.float16, (M,))
+        _check(wbar, "wbar", torch.float16, (N,))
+    made = Y is None
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev) if Y is None else Y
+    _check(Y, "Y", torch.float16, (M, N))
+    return Y, made
+
+
+def w4a4_linear_workspace_bytes(M, r):
+    """Workspace bytes kq_w4a4_linear needs for M tokens and rank r (0 when r == 0)."""
+    return int(load().kq_w4a4_linear_workspace_bytes(M, r))
+
+
+def w4a4_linear(xcodes, xscales, wcodes, wscales, X=None, L1=None, L2=None, mu=None, wbar=None,
+                fmt="mxfp4", Y=None, workspace=None, stream=None):
+    """Y = Xq Wq^T + (X L1^T) L2^T + mu wbar^T (fp16 [M][N]): the down-projection of the
+    low-rank branch runs inside the call (its result held in the workspace).  X fp16
+    [M][K], L1 fp16 [r][K], L2 fp16 [N][r].  workspace: a uint8 device tensor of at least
+    w4a4_linear_workspace_bytes(M, r) bytes (256-byte aligned); by default one is taken
+    from torch's allocator.  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4, no branches)."""
+    torch = _torch()
+    f, M, K, N = _linear_operands(xcodes, xscales, wcodes, wscales, fmt)
+    r = 0
+    if L1 is not None:
+        r = L1.shape[0]
+        _check(X, "X", torch.float16, (M, K))
+        _check(L1, "L1", torch.float16, (r, K))
+        _check(L2, "L2", torch.float16, (N, r))
+    Y, made_y = _linear_tail(M, N, mu, wbar, Y, xcodes.device)
+    made = [Y] if made_y else []
+    if r and workspace is None:
+        workspace = torch.empty((w4a4_linear_workspace_bytes(M, r),), dtype=torch.uint8, device=xcodes.device)
+        made.append(workspace)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8)
+    _on_stream(stream, *made)
+    wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    s = load().kq_w4a4_linear(f, _ptr(xcodes), _ptr(xscales), M, K, _ptr(wcodes), _ptr(wscales), N,
+                              _ptr(X if r else None), _ptr(L1 if r else None), _ptr(L2 if r else None), r,
+                              _ptr(mu), _ptr(wbar), _ptr(Y), wp, wn, _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_w4a4_linear")
+    return Y
+
+
+def w4a4_linear_t(xcodes, xscales, wcodes, wscales, T=None, L2=None, mu=None, wbar=None,
+                  fmt="mxfp4", Y=None, stream=None):
+    """Y = Xq Wq^T + T L2^T + mu wbar^T (fp16 [M][N]) with the down-projection T (fp16
+    [M][r]) already computed.  fmt 'mxfp4' (W4A4) or 'lm2' (W2A4)."""
+    torch = _torch()
+    f, M, K, N = _linear_operands(xcodes, xscales, wcodes, wscales, fmt)
     r = 0
     if T is not None:
         r = T.shape[1]
         _check(T, "T", torch.float16, (M, r))
         _check(L2, "L2", torch.float16, (N, r))
-    if mu is not None:
-        _check(mu, "mu", torch.float16, (M,))
-        _check(wbar, "wbar", torch.float16, (N,))
-    Y = torch.empty((M, N), dtype=torch.float16, device=xcodes.device) if Y is None else Y
-    _check(Y, "Y", torch.float16, (M, N))
-    s = load().kq_w4a4_linear(f, _ptr(xcodes), _ptr(xscales), M, K, _ptr(wcodes), _ptr(wscales), N,
-                              _ptr(T), _ptr(L2 if r else None), r, _ptr(mu), _ptr(wbar), _ptr(Y), _stream(stream))
+    Y, made_y = _linear_tail(M, N, mu, wbar, Y, xcodes.device)
+    if made_y:
+        _on_stream(stream, Y)
+    s = load().kq_w4a4_linear_t(f, _ptr(xcodes), _ptr(xscales), M, K, _ptr(wcodes), _ptr(wscales), N,
+                                _ptr(T), _ptr(L2 if r else None), r, _ptr(mu), _ptr(wbar), _ptr(Y),
+                                _stream(stream))
     if s != KQ_OK:
-        raise KQError(s, "kq_w4a4_linear")
+        raise KQError(s, "kq_w4a4_linear_t")
     return Y

@@ -63,8 +63,12 @@ __device__ void invert32(const float* __restrict__ P, const float* __restrict__ 
 // KIND 4: w'_b = (A_b (x) B_b)^-1 w_b with per-block factors (P = AB, float [nb][80]); the
 //         grid is 2-D, blockIdx.y = b, so a workgroup inverts one block's P.
 // FMT 0: MXFP4 (16 code bytes + 1 E8M0 byte); FMT 2: 2-bit Lloyd-Max + fp16 group scale.
+// W element (n, k) sits at n * sn + k * sk: sn = K, sk = 1 for [N][K] weights, sn = 1,
+// sk = N for [K][N].  With [K][N] weights consecutive threads take consecutive n (the
+// reads of a warp then cover contiguous memory).
 template <int KIND, int FMT>
-__global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, KronFactors fi,
+__global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W, int64_t N, int64_t K, int64_t sn,
+                                                   int64_t sk, KronFactors fi,
                                                    const int32_t* __restrict__ perm, const int8_t* __restrict__ sign,
                                                    const float* __restrict__ P, const int8_t* __restrict__ pts,
                                                    float t4, uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
@@ -74,14 +78,16 @@ __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W,
   const int64_t nb = K >> 5;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (KIND == 4 ? id >= N : id >= N * nb) return;
-  const int64_t n = KIND == 4 ? id : id / nb, b = KIND == 4 ? (int64_t)blockIdx.y : id % nb;
-  const __half* wr = W + n * K;
+  const bool nfast = sn == 1;
+  const int64_t n = KIND == 4 ? id : (nfast ? id % N : id / nb);
+  const int64_t b = KIND == 4 ? (int64_t)blockIdx.y : (nfast ? id / N : id % nb);
+  const __half* wr = W + n * sn;
   float w[32], y[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int64_t k = 32 * b + i;
     const int64_t src = KIND == 2 ? (int64_t)perm[k] : k;
-    w[i] = __half2float(wr[src]);
+    w[i] = __half2float(wr[src * sk]);
     if (pts) w[i] = ldexpf(w[i], (int)pts[src]);   // W' = P^-1 D W with D = diag(2^pts), exact
   }
   if (KIND == 1) {
@@ -162,44 +168,72 @@ __global__ __launch_bounds__(256) void fold_kernel(const __half* __restrict__ W,
   }
 }
 
-// wbar[n] = fp16(sum_k W[n][k]); one wavefront per row n.
+// wbar[n] = fp16(sum_k W(n, k)), summed in float64 (one rounding at the end, so wbar is
+// the fp16 rounding of the column sum up to float64 summation error).  The conversion is
+// LLVM's direct f64 -> f16 truncation, a single round-to-nearest-even.
+__device__ __forceinline__ __half f64_to_f16(double v) {
+  return __builtin_bit_cast(__half, (_Float16)v);
+}
+// [N][K] weights: one wavefront per n, lanes striding over k, then a wavefront sum.
 __global__ __launch_bounds__(256) void colsum_kernel(const __half* __restrict__ W, int64_t N, int64_t K,
                                                      __half* __restrict__ wbar) {
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (n >= N) return;
-  float acc = 0.0f;
-  for (int64_t k = lane; k < K; k += 64) acc += __half2float(W[n * K + k]);
-  acc = wave_sum(acc);
-  if (lane == 0) wbar[n] = __float2half_rn(acc);
+  double acc = 0.0;
+  for (int64_t k = lane; k < K; k += 64) acc += (double)__half2float(W[n * K + k]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) wbar[n] = f64_to_f16(acc);
+}
+
+// [K][N] weights: one thread per n walking down its column (a warp reads contiguous rows).
+__global__ __launch_bounds__(256) void colsum_kn_kernel(const __half* __restrict__ W, int64_t N, int64_t K,
+                                                        __half* __restrict__ wbar) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  double acc = 0.0;
+  for (int64_t k = 0; k < K; ++k) acc += (double)__half2float(W[k * N + n]);
+  wbar[n] = f64_to_f16(acc);
 }
 
 template <int KIND>
-static void fold_fmt(int fmt, dim3 g, dim3 b, hipStream_t s, const __half* W, int64_t N, int64_t K,
-                     const KronFactors& fi, const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts,
-                     float t4, uint8_t* wc, void* ws) {
-  if (fmt == 0) hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, fi, perm, sign, P, pts, t4, wc, ws);
-  else hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, fi, perm, sign, P, pts, t4, wc, ws);
+static void fold_fmt(int fmt, dim3 g, dim3 b, hipStream_t s, const __half* W, int64_t N, int64_t K, int64_t sn,
+                     int64_t sk, const KronFactors& fi, const int32_t* perm, const int8_t* sign, const float* P,
+                     const int8_t* pts, float t4, uint8_t* wc, void* ws) {
+  if (fmt == 0)
+    hipLaunchKernelGGL((fold_kernel<KIND, 0>), g, b, 0, s, W, N, K, sn, sk, fi, perm, sign, P, pts, t4, wc, ws);
+  else
+    hipLaunchKernelGGL((fold_kernel<KIND, 2>), g, b, 0, s, W, N, K, sn, sk, fi, perm, sign, P, pts, t4, wc, ws);
 }
 
-hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
+hipError_t launch_fold(int kind, int fmt, bool kn, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
                        const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts, uint8_t* wcodes,
                        void* wscales, hipStream_t s) {
   const int64_t total = N * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const float t4 = lm_tables().t4;
+  const int64_t sn = kn ? 1 : K, sk = kn ? N : 1;
   if (kind == 4) {
     const dim3 g2((unsigned)((N + 255) / 256), (unsigned)(K / 32));
-    fold_fmt<4>(fmt, g2, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
-  } else if (kind == 1) fold_fmt<1>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
-  else if (kind == 2) fold_fmt<2>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
-  else if (kind == 3) fold_fmt<3>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
-  else fold_fmt<0>(fmt, grid, block, s, W, N, K, finv, perm, sign, P, pts, t4, wcodes, wscales);
+    fold_fmt<4>(fmt, g2, block, s, W, N, K, sn, sk, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  } else if (kind == 1) {
+    fold_fmt<1>(fmt, grid, block, s, W, N, K, sn, sk, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  } else if (kind == 2) {
+    fold_fmt<2>(fmt, grid, block, s, W, N, K, sn, sk, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  } else if (kind == 3) {
+    fold_fmt<3>(fmt, grid, block, s, W, N, K, sn, sk, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  } else {
+    fold_fmt<0>(fmt, grid, block, s, W, N, K, sn, sk, finv, perm, sign, P, pts, t4, wcodes, wscales);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, wbar);
+hipError_t launch_colsum(bool kn, const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s) {
+  if (kn)
+    hipLaunchKernelGGL(colsum_kn_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, W, N, K, wbar);
+  else
+    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, wbar);
   return hipGetLastError();
 }
 

@@ -138,6 +138,7 @@ const char* kq_status_str(kq_status s) {
     case KQ_ERR_UNSUPPORTED: return "KQ_ERR_UNSUPPORTED: unknown enum or size outside the supported range";
     case KQ_ERR_VALUE: return "KQ_ERR_VALUE: transform factor singular or not finite";
     case KQ_ERR_HIP: return "KQ_ERR_HIP: a HIP launch failed";
+    case KQ_ERR_WORKSPACE: return "KQ_ERR_WORKSPACE: workspace missing or smaller than the call needs";
     default: return "KQ_ERR_UNKNOWN: unknown status code";
   }
 }
@@ -193,8 +194,8 @@ kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center,
   return hip_status(e);
 }
 
-kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const void* W, int64_t N, int64_t K,
-                                       uint8_t* wcodes, void* wscales, void* wbar, hipStream_t stream) {
+static kq_status fold(const kq_xform* xf, int32_t fmt, bool kn, const void* W, int64_t N, int64_t K,
+                      uint8_t* wcodes, void* wscales, void* wbar, hipStream_t stream) {
   if (!W || !wcodes || !wscales) return KQ_ERR_NULL;
   if (N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (fmt != KQ_FMT_MXFP4 && fmt != KQ_FMT_LM2_G32) return KQ_ERR_UNSUPPORTED;
@@ -208,16 +209,28 @@ kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const vo
   if (xf->kind == KQ_XFORM_KRON_4X8) {
     if (!invert(xf->A, 4, finv.A) || !invert(xf->B, 8, finv.B)) return KQ_ERR_VALUE;
   }
-  hipError_t e = launch_fold(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 2, static_cast<const __half*>(W), N, K, finv,
+  hipError_t e = launch_fold(xf->kind, fmt == KQ_FMT_MXFP4 ? 0 : 2, kn, static_cast<const __half*>(W), N, K, finv,
                              xf->perm, xf->sign, xf->kind == KQ_XFORM_KRON_4X8_BLOCKS ? xf->AB : xf->P, xf->pts,
                              wcodes, wscales, stream);
   if (e != hipSuccess) return KQ_ERR_HIP;
-  if (wbar) e = launch_colsum(static_cast<const __half*>(W), N, K, static_cast<__half*>(wbar), stream);
+  if (wbar) e = launch_colsum(kn, static_cast<const __half*>(W), N, K, static_cast<__half*>(wbar), stream);
   return hip_status(e);
 }
 
+kq_status kq_fold_inverse_into_weights(const kq_xform* xf, int32_t fmt, const void* W, int64_t K, int64_t N,
+                                       uint8_t* wcodes, void* wscales, void* wbar, hipStream_t stream) {
+  return fold(xf, fmt, true, W, N, K, wcodes, wscales, wbar, stream);
+}
+
+kq_status kq_fold_inverse_into_weights_nk(const kq_xform* xf, int32_t fmt, const void* Wt, int64_t N, int64_t K,
+                                          uint8_t* wcodes, void* wscales, void* wbar, hipStream_t stream) {
+  return fold(xf, fmt, false, Wt, N, K, wcodes, wscales, wbar, stream);
+}
+
+static bool lr_rank(int32_t r) { return r == 16 || r == 32 || r == 48 || r == 64; }
+
 size_t kq_lowrank_down_workspace_bytes(int64_t M, int64_t K, int32_t r) {
-  if (M < 1 || K < 32 || K % 32 != 0 || (r != 16 && r != 32 && r != 64)) return 0;
+  if (M < 1 || K < 32 || K % 32 != 0 || !lr_rank(r)) return 0;
   return lowrank_workspace_bytes(M, K, r);
 }
 
@@ -225,7 +238,7 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!X || !L1 || !T) return KQ_ERR_NULL;
   if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
-  if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if (!lr_rank(r)) return KQ_ERR_SHAPE;
   if (M > (1LL << 31) - 64 || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16)) return KQ_ERR_ALIGN;
   if (workspace_bytes && !workspace) return KQ_ERR_NULL;
@@ -240,7 +253,7 @@ kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64
                                         size_t workspace_bytes, hipStream_t stream) {
   if (!X || !codes || !scales || !L1 || !T) return KQ_ERR_NULL;
   if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
-  if (r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if (!lr_rank(r)) return KQ_ERR_SHAPE;
   kq_status st = check_xform(xf, K);
   if (st != KQ_OK) return st;
   if (xf->kind != KQ_XFORM_NONE && xf->kind != KQ_XFORM_KRON_4X8 && xf->kind != KQ_XFORM_DENSE_32)
@@ -281,12 +294,14 @@ kq_status kq_svd_lowrank(const void* W, int64_t N, int64_t K, int32_t r, const f
                                        sigma, workspace, stream));
 }
 
-kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
-                         const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
-                         int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {
+// Arguments of the 4-bit product and its epilogue, shared by both linear forms (the
+// low-rank operands are checked by the callers).
+static kq_status check_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                              const uint8_t* wcodes, const void* wscales, int64_t N, int32_t r, const void* mu,
+                              const void* wbar, const void* Y) {
   if (!xcodes || !xscales || !wcodes || !wscales || !Y) return KQ_ERR_NULL;
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
-  if (r != 0 && r != 16 && r != 32 && r != 64) return KQ_ERR_SHAPE;
+  if (r != 0 && !lr_rank(r)) return KQ_ERR_SHAPE;
   if ((mu == nullptr) != (wbar == nullptr)) return KQ_ERR_SHAPE;
   if (M > (1LL << 30) || N > (1LL << 20) || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (N % 16 != 0) return KQ_ERR_UNSUPPORTED;
@@ -297,24 +312,62 @@ kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales
   } else {
     return KQ_ERR_UNSUPPORTED;
   }
+  if (!aligned(xcodes, 16) || !aligned(wcodes, 16) || !aligned(Y, 16)) return KQ_ERR_ALIGN;
+  if (!aligned(xscales, 4) || !aligned(wscales, 4)) return KQ_ERR_ALIGN;
+  if (mu && (!aligned(mu, 2) || !aligned(wbar, 16))) return KQ_ERR_ALIGN;
+  return KQ_OK;
+}
+
+static hipError_t run_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                             const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
+                             int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {
+  if (fmt == KQ_FMT_MXFP4)
+    return launch_w4a4_gemm(xcodes, static_cast<const uint8_t*>(xscales), M, K, wcodes,
+                            static_cast<const uint8_t*>(wscales), N, r ? static_cast<const __half*>(T) : nullptr,
+                            static_cast<const __half*>(L2), r, static_cast<const __half*>(mu),
+                            static_cast<const __half*>(wbar), static_cast<__half*>(Y), stream);
+  return launch_w2a4_gemm(xcodes, static_cast<const float*>(xscales), M, K, wcodes,
+                          static_cast<const __half*>(wscales), N, static_cast<__half*>(Y), stream);
+}
+
+size_t kq_w4a4_linear_workspace_bytes(int64_t M, int32_t r) {
+  if (M < 1 || M > (1LL << 30) || (r != 0 && !lr_rank(r))) return 0;
+  return lowrank_linear_workspace_bytes(M, r);
+}
+
+kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                         const uint8_t* wcodes, const void* wscales, int64_t N, const void* X, const void* L1,
+                         const void* L2, int32_t r, const void* mu, const void* wbar, void* Y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  kq_status st = check_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, r, mu, wbar, Y);
+  if (st != KQ_OK) return st;
+  if (r > 0) {
+    if (!X || !L1 || !L2) return KQ_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(L2, 16)) return KQ_ERR_ALIGN;
+    const size_t tb = lowrank_t_bytes(M, r);
+    if (!workspace || workspace_bytes < lowrank_linear_workspace_bytes(M, r)) return KQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KQ_ERR_ALIGN;
+    __half* T = static_cast<__half*>(workspace);
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tb);
+    hipError_t e = launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r, T, part,
+                                       workspace_bytes - tb, stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, stream));
+  }
+  return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, nullptr, nullptr, 0, mu, wbar, Y,
+                               stream));
+}
+
+kq_status kq_w4a4_linear_t(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                           const uint8_t* wcodes, const void* wscales, int64_t N, const void* T, const void* L2,
+                           int32_t r, const void* mu, const void* wbar, void* Y, hipStream_t stream) {
+  kq_status st = check_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, r, mu, wbar, Y);
+  if (st != KQ_OK) return st;
   if (r > 0) {
     if (!T || !L2) return KQ_ERR_NULL;
     if (!aligned(T, 16) || !aligned(L2, 16)) return KQ_ERR_ALIGN;
   }
-  if (!aligned(xcodes, 16) || !aligned(wcodes, 16) || !aligned(Y, 16)) return KQ_ERR_ALIGN;
-  if (!aligned(xscales, 4) || !aligned(wscales, 4)) return KQ_ERR_ALIGN;
-  if (mu && (!aligned(mu, 2) || !aligned(wbar, 2))) return KQ_ERR_ALIGN;
-  hipError_t e;
-  if (fmt == KQ_FMT_MXFP4) {
-    e = launch_w4a4_gemm(xcodes, static_cast<const uint8_t*>(xscales), M, K, wcodes,
-                         static_cast<const uint8_t*>(wscales), N, r ? static_cast<const __half*>(T) : nullptr,
-                         static_cast<const __half*>(L2), r, static_cast<const __half*>(mu),
-                         static_cast<const __half*>(wbar), static_cast<__half*>(Y), stream);
-  } else {
-    e = launch_w2a4_gemm(xcodes, static_cast<const float*>(xscales), M, K, wcodes,
-                         static_cast<const __half*>(wscales), N, static_cast<__half*>(Y), stream);
-  }
-  return hip_status(e);
+  return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, stream));
 }
 
 }  // extern "C"

@@ -52,14 +52,20 @@ hipError_t launch_row_quant(int kind, int fmt, bool center, const __half* X, int
 // kind 3: P (device, row-major) is inverted on the device; kind 4: P is the per-block
 // factor table (float [K/32][80]) and each block's A (x) B is inverted on the device.  pts (optional): weight input
 // channel k is multiplied by 2^pts[k] before the inverse transform.
-hipError_t launch_fold(int kind, int fmt, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
+// kn: W is [K][N] (element (n, k) at k * N + n); else [N][K] (at n * K + k).
+hipError_t launch_fold(int kind, int fmt, bool kn, const __half* W, int64_t N, int64_t K, const KronFactors& finv,
                        const int32_t* perm, const int8_t* sign, const float* P, const int8_t* pts, uint8_t* wcodes,
                        void* wscales, hipStream_t s);
-hipError_t launch_colsum(const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
+// wbar[n] = fp16(sum_k W(n, k)), summed in float64; layout as launch_fold.
+hipError_t launch_colsum(bool kn, const __half* W, int64_t N, int64_t K, __half* wbar, hipStream_t s);
 
 // T[M][r] = fp16(X L1^T), fp32 accumulation; split over K into `part` (fp32 partials,
 // part_bytes long, may be null) when that helps and fits.
 size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r);
+// The linear's workspace: T fp16 [M][r] (lowrank_t_bytes, 256-byte padded) then split-K
+// partials for any K.
+size_t lowrank_t_bytes(int64_t M, int r);
+size_t lowrank_linear_workspace_bytes(int64_t M, int r);
 hipError_t launch_lowrank_down(const __half* X, const __half* L1, int64_t M, int64_t K, int r,
                                __half* T, float* part, size_t part_bytes, hipStream_t s);
 // The same down-projection fused with the block transform (kind 0 identity, 1 Kronecker,

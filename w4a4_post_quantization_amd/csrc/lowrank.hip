@@ -202,6 +202,16 @@ size_t lowrank_workspace_bytes(int64_t M, int64_t K, int r) {
   return s > 1 ? (size_t)s * (size_t)M * (size_t)r * 4 : 0;
 }
 
+// Workspace of the linear that runs the down-projection itself: T (fp16 [M][r], padded to
+// 256 bytes) followed by the partial sums of as many slices as any K could use (the slice
+// count is capped by the compute-unit count against the row blocks, not by K).
+size_t lowrank_t_bytes(int64_t M, int r) { return ((size_t)M * (size_t)r * 2 + 255) & ~(size_t)255; }
+size_t lowrank_linear_workspace_bytes(int64_t M, int r) {
+  if (r == 0) return 0;
+  const int s = lr_slices(M, INT64_MAX / 4, r, ~(size_t)0);
+  return lowrank_t_bytes(M, r) + (s > 1 ? (size_t)s * (size_t)M * (size_t)r * 4 : 0);
+}
+
 template <int RR, int XK>
 static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, int64_t K, __half* T, float* part,
                                  hipStream_t s, int slices, const KronFactors& fk, const float* P, uint8_t* codes,
@@ -228,6 +238,7 @@ static hipError_t lowrank_rank(const __half* X, const __half* L1, int64_t M, int
   switch (r) {
     case 16: return lowrank_launch<16, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
     case 32: return lowrank_launch<32, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
+    case 48: return lowrank_launch<48, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
     case 64: return lowrank_launch<64, XK>(X, L1, M, K, T, part, s, slices, fk, P, codes, scales);
     default: return hipErrorInvalidValue;
   }

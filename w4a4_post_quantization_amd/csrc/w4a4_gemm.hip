@@ -309,8 +309,8 @@ constexpr int DMA_CODE_LOADS = 8;   // code load instructions per wave per k-ste
 constexpr int DMA_STAGE_BYTES = Tile256::BN * 64 + Tile256::BM * 64;                  // 32 KiB of codes
 constexpr int DMA_SC_OFF = DMA_STAGES * DMA_STAGE_BYTES;                       // scale groups
 constexpr int DMA_SC_BYTES = (Tile256::BN + Tile256::BM) * 16;                        // one group, both operands
-constexpr int DMA_MU_OFF = DMA_SC_OFF + 2 * DMA_SC_BYTES;                     // wbar, mu of the tile
-constexpr int DMA_LDS = DMA_MU_OFF + 2048;                                    // 149504 bytes
+constexpr int DMA_MU_OFF = DMA_SC_OFF + 2 * DMA_SC_BYTES;                     // wbar of the tile
+constexpr int DMA_LDS = DMA_MU_OFF + 1024;   // 148480 bytes (the wbar load writes 64 lanes x 16 bytes)
 
 template <bool LR, bool MU>
 __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
@@ -451,14 +451,23 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
         for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ll[i], lt[j], acc[i][j], 0, 0, 0);
     }
   };
+  // Rank-1 restore operands.  The token means of this lane's four rows go straight into
+  // registers (rows past M repeat the last mean; they are never stored).  They are the
+  // oldest loads of the wave, so the k-loop's counted waits cover them.  The tile's 256
+  // column sums go to LDS with one 16-byte load per lane of lanes 0..31 (the others read
+  // past the range and write zeros): N is a multiple of 16, so a piece is wholly inside
+  // or wholly outside the row of sums, never cut by the range check.
+  float mu_r[TM];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) mu_r[j] = 0.0f;
+  if (MU) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) mu_r[j] = __half2float(mu[min(m0 + wm * 128 + 32 * j + l32, M - 1)]);
+  }
   if (MU && wid == 0) {
-    // the tile's 256 column sums and 256 token means: one load each, lanes 0..31 carry
-    // 16 bytes (8 values) apiece, lanes 32..63 read past the range and write zeros
     const v4i rW = rsrc_words(wbar + n0, (int64_t)(N - n0) * 2);
-    const v4i rM = rsrc_words(mu + m0, (int64_t)(M - m0) * 2);
     const int off = lane < 32 ? 16 * lane : KQ_OOB;
     lds_load16(rW, lds0 + DMA_MU_OFF, off);
-    lds_load16(rM, lds0 + DMA_MU_OFF + 1024, off);
   }
   if (LR) lr_load(0);
   scale_loads(0, 0);
@@ -564,11 +573,10 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
 
   const __amdgpu_buffer_rsrc_t rY = make_rsrc(Y + (int64_t)m0 * N, (int64_t)(M - m0) * N * 2);
   const __half* const wbar_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF);
-  const __half* const mu_t = reinterpret_cast<const __half*>(lds + DMA_MU_OFF + 1024);
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int ml = wrow_b + 32 * j + l32;
-    const float mm = MU ? __half2float(mu_t[ml]) : 0.0f;
+    const float mm = mu_r[j];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -650,7 +658,6 @@ static hipError_t gemm_launch(const uint8_t* xcodes, const uint8_t* xscales, int
   return hipGetLastError();
 }
 
-#ifndef KQ_GEMM_TUNING
 hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64_t M, int64_t K,
                             const uint8_t* wcodes, const uint8_t* wscales, int64_t N, const __half* T,
                             const __half* L2, int r, const __half* mu, const __half* wbar, __half* Y,
@@ -664,6 +671,5 @@ hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64
     return gemm_launch<Big>(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
   return gemm_launch<Small>(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
 }
-#endif
 
 }  // namespace kq
