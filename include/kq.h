@@ -260,6 +260,25 @@ kq_status kq_w4a4_linear(int32_t fmt,
                          const void* mu, const void* wbar,
                          void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): kq_w4a4_linear without a workspace argument.  T and the
+ * down-projection's split-K partial sums live in a fixed device array of
+ * KQ_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the process ends);
+ * the call allocates nothing and calls no allocating routine.  Rejected with
+ * KQ_ERR_WORKSPACE when T alone (M * r * 2 bytes, rounded up to 256) exceeds that size;
+ * when T fits but the partial sums of the full split do not, fewer K slices are used
+ * (results then differ from kq_w4a4_linear's only in float32 summation order).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and give undefined results.  Arguments otherwise as
+ * kq_w4a4_linear. */
+#define KQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kq_status kq_w4a4_linear_noalloc(int32_t fmt,
+                                 const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                                 const uint8_t* wcodes, const void* wscales, int64_t N,
+                                 const void* X, const void* L1, const void* L2, int32_t r,
+                                 const void* mu, const void* wbar,
+                                 void* Y, hipStream_t stream);
+
 /* The same linear with the down-projection already done: T fp16 [M][r] from
  * kq_lowrank_down or kq_transform_quantize_lowrank (caller-owned), L2 fp16 [N][r],
  * r in {0, 16, 32, 48, 64} (0: T and L2 ignored).  One kernel launch; no workspace.

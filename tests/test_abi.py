@@ -201,6 +201,23 @@ def test_linear_validation(lib):
     assert call(**dict(lr, fmt=2)) == 4                # W2A4 has no low-rank branch
 
 
+def test_noalloc_linear_validation(lib):
+    """The allocation-free linear refuses, before anything is launched, a T that would not
+    fit its fixed scratch (KQ_ERR_WORKSPACE), and checks the other arguments like the
+    workspace form."""
+    f = lib.kq_w4a4_linear_noalloc
+
+    def call(**kw):
+        a = {**_LIN, "X": None, "L1": None, "L2": None, **kw}
+        return f(a["fmt"], a["xc"], a["xs"], a["M"], a["K"], a["wc"], a["wsc"], a["N"], a["X"], a["L1"], a["L2"],
+                 a["r"], a["mu"], a["wbar"], a["Y"], None)
+    _common_linear_checks(call)
+    lr = dict(r=64, X=FAKE, L1=FAKE, L2=FAKE)
+    assert call(**dict(lr, X=None)) == 1
+    assert call(**dict(lr, L1=FAKE_ODD)) == 3
+    assert call(**dict(lr, M=(32 << 20) // 128 + 1)) == 7        # T of M x 64 fp16 beyond 32 MiB
+
+
 def test_linear_workspace_size(lib):
     """T (fp16, padded to 256 bytes) plus the split-K partial sums; 0 without a branch;
     every rank the linear takes, 48 included; 0 for an invalid one."""

@@ -91,6 +91,8 @@ def load():
     lib.kq_w4a4_linear.restype = i32
     lib.kq_w4a4_linear.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    lib.kq_w4a4_linear_noalloc.restype = i32
+    lib.kq_w4a4_linear_noalloc.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, vp, i32, vp, vp, vp, vp]
     lib.kq_w4a4_linear_t.restype = i32
     lib.kq_w4a4_linear_t.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, vp, i32, vp, vp, vp, vp]
     _LIB = lib

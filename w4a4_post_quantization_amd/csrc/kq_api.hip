@@ -294,6 +294,30 @@ kq_status kq_svd_lowrank(const void* W, int64_t N, int64_t K, int32_t r, const f
                                        sigma, workspace, stream));
 }
 
+// ---- Scratch of the allocation-free linear (kq_w4a4_linear_noalloc): a file-scope device
+// array that holds T and the down-projection's split-K partial sums.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[KQ_NOALLOC_SCRATCH_BYTES];
+
+static void* scratch_device_ptr(int dev) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mtx;
+  static void* ptrs[kMaxDevices] = {};
+  static bool done[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mtx);
+  if (!done[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+    done[dev] = true;
+  }
+  return ptrs[dev];
+}
+
 // Arguments of the 4-bit product and its epilogue, shared by both linear forms (the
 // low-rank operands are checked by the callers).
 static kq_status check_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
@@ -356,6 +380,34 @@ kq_status kq_w4a4_linear(int32_t fmt, const uint8_t* xcodes, const void* xscales
   }
   return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, nullptr, nullptr, 0, mu, wbar, Y,
                                stream));
+}
+
+kq_status kq_w4a4_linear_noalloc(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
+                                 const uint8_t* wcodes, const void* wscales, int64_t N, const void* X,
+                                 const void* L1, const void* L2, int32_t r, const void* mu, const void* wbar, void* Y,
+                                 hipStream_t stream) {
+  kq_status st = check_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, r, mu, wbar, Y);
+  if (st != KQ_OK) return st;
+  if (r == 0)
+    return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, nullptr, nullptr, 0, mu, wbar, Y,
+                                 stream));
+  if (!X || !L1 || !L2) return KQ_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(L2, 16)) return KQ_ERR_ALIGN;
+  const size_t tb = lowrank_t_bytes(M, r);
+  if (tb > KQ_NOALLOC_SCRATCH_BYTES) return KQ_ERR_WORKSPACE;   // T alone would not fit the scratch
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+  uint8_t* base = static_cast<uint8_t*>(scratch_device_ptr(dev));
+  if (!base) return KQ_ERR_HIP;
+  // T first, then as many split-K slices of partial sums as the rest holds (fewer slices
+  // than the workspace form would take only when the scratch is the limit; every slice and
+  // T are written in full before they are read, so nothing needs clearing)
+  __half* T = reinterpret_cast<__half*>(base);
+  float* part = reinterpret_cast<float*>(base + tb);
+  hipError_t e = launch_lowrank_down(static_cast<const __half*>(X), static_cast<const __half*>(L1), M, K, r, T, part,
+                                     KQ_NOALLOC_SCRATCH_BYTES - tb, stream);
+  if (e != hipSuccess) return KQ_ERR_HIP;
+  return hip_status(run_linear(fmt, xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, stream));
 }
 
 kq_status kq_w4a4_linear_t(int32_t fmt, const uint8_t* xcodes, const void* xscales, int64_t M, int64_t K,
