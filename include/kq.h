@@ -196,14 +196,21 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
 /* The online activation path and the low-rank down-projection in one pass over X
  * (SVDQuant explainer §3: the 16-bit branch and the 4-bit branch read the same input, and
  * running the branch separately costs an extra read of it):
- *   codes, scales = MXFP4 of x . P per 32-block (as kq_transform_quantize, fmt MXFP4, no
- *                   centring; kinds NONE, KRON_4X8 and DENSE_32, no pts),
- *   T = fp16(X L1^T) (as kq_lowrank_down).
+ *   codes, scales[, mu] = MXFP4 of the (optionally centred) block-transformed X, as
+ *                   kq_transform_quantize with fmt MXFP4;
+ *   T = fp16(X L1^T) from the original X (neither centred nor transformed), as
+ *                   kq_lowrank_down.
+ * Kinds NONE, KRON_4X8 and DENSE_32 (no centring) and RPBH_32 (centring optional; mu fp16
+ * [M], required iff center != 0); no pts.  For RPBH the pass is one kernel when
+ * K r <= 3072 x 32 and r is 16 or 32 (L1 is held on chip for the whole launch); otherwise the
+ * call runs the transform and then the down-projection (X is read twice).
  * Shapes, layouts, alignment and the workspace rule are those of the two calls it
- * replaces; kq_lowrank_down_workspace_bytes(M, K, r) gives the workspace size.  Codes may
- * differ from kq_transform_quantize's only at rounding ties of the float32 transform. */
-kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64_t M, int64_t K,
-                                        uint8_t* codes, void* scales, const void* L1, int32_t r, void* T,
+ * replaces; kq_lowrank_down_workspace_bytes(M, K, r) gives the workspace size.  Codes and
+ * means may differ from kq_transform_quantize's only at rounding ties of the float32
+ * arithmetic (sums of a different length per thread), and T from kq_lowrank_down's only by
+ * float32 summation order. */
+kq_status kq_transform_quantize_lowrank(const kq_xform* xf, int32_t center, const void* X, int64_t M, int64_t K,
+                                        uint8_t* codes, void* scales, void* mu, const void* L1, int32_t r, void* T,
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Offline rank-r extraction of the 16-bit branch (SVDQuant explainer §3: the weight's

@@ -245,12 +245,13 @@ def test_lowrank_validation(lib):
 
 
 def test_transform_quantize_lowrank_validation(lib):
-    """The fused pass: both calls' argument rules, and only the streaming transform kinds
-    (no RPBH, no per-block factors, no power-of-two scaling)."""
+    """The fused pass: both calls' argument rules; the streaming kinds without centring and
+    RPBH with or without it; no per-block factors, no power-of-two scaling."""
     f = lib.kq_transform_quantize_lowrank
     xf = _xf()
-    args = lambda **kw: [kw.get("X", FAKE), kw.get("M", 4), kw.get("K", 64), kw.get("codes", FAKE), FAKE,
-                         kw.get("L1", FAKE), kw.get("r", 32), FAKE, kw.get("ws", None), kw.get("wn", 0), None]
+    args = lambda **kw: [kw.get("center", 0), kw.get("X", FAKE), kw.get("M", 4), kw.get("K", 64),
+                         kw.get("codes", FAKE), FAKE, kw.get("mu", None), kw.get("L1", FAKE), kw.get("r", 32), FAKE,
+                         kw.get("ws", None), kw.get("wn", 0), None]
     assert f(ctypes.byref(xf), *args(X=None)) == 1
     assert f(ctypes.byref(xf), *args(L1=None)) == 1
     assert f(None, *args()) == 1
@@ -260,9 +261,12 @@ def test_transform_quantize_lowrank_validation(lib):
     assert f(ctypes.byref(xf), *args(codes=FAKE_ODD)) == 3
     assert f(ctypes.byref(xf), *args(wn=1024)) == 1
     assert f(ctypes.byref(xf), *args(ws=FAKE_ODD, wn=1024)) == 3
+    assert f(ctypes.byref(xf), *args(center=1, mu=FAKE)) == 4          # centring: RPBH only
     rp = _xf(kind=2)
+    assert f(ctypes.byref(rp), *args()) == 1                            # RPBH without perm / sign
     rp.perm, rp.sign = 0x100000, 0x100000
-    assert f(ctypes.byref(rp), *args()) == 4
+    assert f(ctypes.byref(rp), *args(center=1)) == 1                    # centring without mu
+    assert f(ctypes.byref(rp), *args(center=1, mu=ctypes.c_void_p(0x100001))) == 3
     kb = _xf(kind=4)
     kb.AB = 0x100000
     assert f(ctypes.byref(kb), *args()) == 4

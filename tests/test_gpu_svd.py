@@ -74,7 +74,7 @@ def test_svd_then_fold_and_linear(kq):
     xf = {"kind": "kron", "A": A, "B": B}
     dxf = _dev_xform(kq, torch, xf, K)
     X = torch.from_numpy(X16).cuda()
-    xc, xs, T = kq.transform_quantize_lowrank(X, dxf, torch.from_numpy(L1).cuda())
+    xc, xs, _, T = kq.transform_quantize_lowrank(X, dxf, torch.from_numpy(L1).cuda())
     wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(R).cuda(), dxf, fmt="mxfp4")
     Y = kq.w4a4_linear_t(xc, xs, wc, ws, T=T, L2=torch.from_numpy(np.ascontiguousarray(L2)).cuda())
     torch.cuda.synchronize()

@@ -80,8 +80,8 @@ def load():
     lib.kq_lowrank_down_workspace_bytes.restype = ctypes.c_size_t
     lib.kq_lowrank_down_workspace_bytes.argtypes = [i64, i64, i32]
     lib.kq_transform_quantize_lowrank.restype = i32
-    lib.kq_transform_quantize_lowrank.argtypes = [ctypes.POINTER(_XformC), vp, i64, i64, vp, vp, vp, i32, vp, vp,
-                                                  ctypes.c_size_t, vp]
+    lib.kq_transform_quantize_lowrank.argtypes = [ctypes.POINTER(_XformC), i32, vp, i64, i64, vp, vp, vp, vp, i32,
+                                                  vp, vp, ctypes.c_size_t, vp]
     lib.kq_svd_lowrank_workspace_bytes.restype = ctypes.c_size_t
     lib.kq_svd_lowrank_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.kq_svd_lowrank.restype = i32
@@ -363,9 +363,11 @@ def lowrank_down(X, L1, T=None, workspace=None, stream=None):
     return T
 
 
-def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, workspace=None, stream=None):
-    """One pass over X: MXFP4 codes and scales of the block-transformed X (no centring)
-    and the low-rank down-projection T = fp16(X L1^T).  Returns (codes, scales, T)."""
+def transform_quantize_lowrank(X, xform, L1, center=False, codes=None, scales=None, mu=None, T=None, workspace=None,
+                               stream=None):
+    """One pass over X: MXFP4 codes and scales of the (optionally centred, RPBH only)
+    block-transformed X and the low-rank down-projection T = fp16(X L1^T).
+    Returns (codes, scales, mu or None, T)."""
     torch = _torch()
     _check(X, "X", torch.float16)
     if X.dim() != 2:
@@ -383,6 +385,13 @@ def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, wo
         scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
         made.append(scales)
     _check(scales, "scales", torch.uint8, (M, K // 32))
+    if center:
+        if mu is None:
+            mu = torch.empty((M,), dtype=torch.float16, device=dev)
+            made.append(mu)
+        _check(mu, "mu", torch.float16, (M,))
+    else:
+        mu = None
     if T is None:
         T = torch.empty((M, r), dtype=torch.float16, device=dev)
         made.append(T)
@@ -395,11 +404,11 @@ def transform_quantize_lowrank(X, xform, L1, codes=None, scales=None, T=None, wo
         _check(workspace, "workspace", torch.uint8)
     _on_stream(stream, *made)
     wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
-    s = load().kq_transform_quantize_lowrank(xform.c(), _ptr(X), M, K, _ptr(codes), _ptr(scales), _ptr(L1), r,
-                                             _ptr(T), wp, wn, _stream(stream))
+    s = load().kq_transform_quantize_lowrank(xform.c(), int(bool(center)), _ptr(X), M, K, _ptr(codes), _ptr(scales),
+                                             _ptr(mu), _ptr(L1), r, _ptr(T), wp, wn, _stream(stream))
     if s != KQ_OK:
         raise KQError(s, "kq_transform_quantize_lowrank")
-    return codes, scales, T
+    return codes, scales, mu, T
 
 
 def svd_lowrank_workspace_bytes(N, K, r, l):

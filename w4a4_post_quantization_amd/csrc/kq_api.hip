@@ -248,28 +248,47 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
                                         workspace ? workspace_bytes : 0, stream));
 }
 
-kq_status kq_transform_quantize_lowrank(const kq_xform* xf, const void* X, int64_t M, int64_t K, uint8_t* codes,
-                                        void* scales, const void* L1, int32_t r, void* T, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
+kq_status kq_transform_quantize_lowrank(const kq_xform* xf, int32_t center, const void* X, int64_t M, int64_t K,
+                                        uint8_t* codes, void* scales, void* mu, const void* L1, int32_t r, void* T,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!X || !codes || !scales || !L1 || !T) return KQ_ERR_NULL;
+  if (center && !mu) return KQ_ERR_NULL;
   if (M < 1 || K < 32 || K % 32 != 0) return KQ_ERR_SHAPE;
   if (!lr_rank(r)) return KQ_ERR_SHAPE;
   kq_status st = check_xform(xf, K);
   if (st != KQ_OK) return st;
-  if (xf->kind != KQ_XFORM_NONE && xf->kind != KQ_XFORM_KRON_4X8 && xf->kind != KQ_XFORM_DENSE_32)
+  const bool rpbh = xf->kind == KQ_XFORM_RPBH_32;
+  if (!rpbh && xf->kind != KQ_XFORM_NONE && xf->kind != KQ_XFORM_KRON_4X8 && xf->kind != KQ_XFORM_DENSE_32)
     return KQ_ERR_UNSUPPORTED;
   if (xf->pts) return KQ_ERR_UNSUPPORTED;
+  if (center && !rpbh) return KQ_ERR_UNSUPPORTED;
+  if (rpbh && K > 16384) return KQ_ERR_UNSUPPORTED;
   if (M > (1LL << 31) - 64 || K > (1LL << 20)) return KQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(L1, 16) || !aligned(T, 16) || !aligned(codes, 16)) return KQ_ERR_ALIGN;
+  if (center && !aligned(mu, 2)) return KQ_ERR_ALIGN;
   if (workspace_bytes && !workspace) return KQ_ERR_NULL;
   if (workspace && !aligned(workspace, 16)) return KQ_ERR_ALIGN;
+  const __half* Xh = static_cast<const __half*>(X);
+  __half* Th = static_cast<__half*>(T);
+  if (rpbh) {
+    // one pass where L1 fits the workgroup's registers; otherwise the transform, then the
+    // split-K down-projection (two launches, X read twice)
+    if (rpbh_lowrank_fusable(K, r))
+      return hip_status(launch_rpbh_mx_lowrank(center != 0, Xh, M, K, xf->perm, xf->sign,
+                                               static_cast<const __half*>(L1), r, Th, codes,
+                                               static_cast<uint8_t*>(scales), static_cast<__half*>(mu), stream));
+    hipError_t e = launch_rpbh_mx_mfma(center != 0, Xh, M, K, xf->perm, xf->sign, codes, static_cast<uint8_t*>(scales),
+                                       static_cast<__half*>(mu), stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    return hip_status(launch_lowrank_down(Xh, static_cast<const __half*>(L1), M, K, r, Th,
+                                          static_cast<float*>(workspace), workspace ? workspace_bytes : 0, stream));
+  }
   KronFactors f;
   std::memcpy(f.A, xf->A, sizeof f.A);
   std::memcpy(f.B, xf->B, sizeof f.B);
-  return hip_status(launch_lowrank_xform_mx(xf->kind, static_cast<const __half*>(X), static_cast<const __half*>(L1),
-                                            M, K, r, static_cast<__half*>(T), static_cast<float*>(workspace),
-                                            workspace ? workspace_bytes : 0, f, xf->P, codes,
-                                            static_cast<uint8_t*>(scales), stream));
+  return hip_status(launch_lowrank_xform_mx(xf->kind, Xh, static_cast<const __half*>(L1), M, K, r, Th,
+                                            static_cast<float*>(workspace), workspace ? workspace_bytes : 0, f, xf->P,
+                                            codes, static_cast<uint8_t*>(scales), stream));
 }
 
 size_t kq_svd_lowrank_workspace_bytes(int64_t N, int64_t K, int32_t r, int32_t l) {
