@@ -200,15 +200,14 @@ kq_status kq_lowrank_down(const void* X, const void* L1, int64_t M, int64_t K, i
  *                   kq_transform_quantize with fmt MXFP4;
  *   T = fp16(X L1^T) from the original X (neither centred nor transformed), as
  *                   kq_lowrank_down.
- * Kinds NONE, KRON_4X8 and DENSE_32 (no centring) and RPBH_32 (centring optional; mu fp16
- * [M], required iff center != 0); no pts.  For RPBH the pass is one kernel when
- * K r <= 3072 x 32 and r is 16 or 32 (L1 is held on chip for the whole launch); otherwise the
- * call runs the transform and then the down-projection (X is read twice).
+ * Kinds NONE, KRON_4X8 and DENSE_32 (no centring): one kernel, X read once.  RPBH_32
+ * (centring optional; mu fp16 [M], required iff center != 0): the permutation spans the
+ * whole row, so the call runs the row-staged transform and then the down-projection
+ * (X is read twice; results equal those of the two separate calls).  No pts.
  * Shapes, layouts, alignment and the workspace rule are those of the two calls it
- * replaces; kq_lowrank_down_workspace_bytes(M, K, r) gives the workspace size.  Codes and
- * means may differ from kq_transform_quantize's only at rounding ties of the float32
- * arithmetic (sums of a different length per thread), and T from kq_lowrank_down's only by
- * float32 summation order. */
+ * replaces; kq_lowrank_down_workspace_bytes(M, K, r) gives the workspace size.  For the
+ * one-kernel kinds, codes may differ from kq_transform_quantize's only at rounding ties of
+ * the float32 arithmetic, and T from kq_lowrank_down's only by float32 summation order. */
 kq_status kq_transform_quantize_lowrank(const kq_xform* xf, int32_t center, const void* X, int64_t M, int64_t K,
                                         uint8_t* codes, void* scales, void* mu, const void* L1, int32_t r, void* T,
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);

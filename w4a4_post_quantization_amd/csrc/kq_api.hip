@@ -271,12 +271,9 @@ kq_status kq_transform_quantize_lowrank(const kq_xform* xf, int32_t center, cons
   const __half* Xh = static_cast<const __half*>(X);
   __half* Th = static_cast<__half*>(T);
   if (rpbh) {
-    // one pass where L1 fits the workgroup's registers; otherwise the transform, then the
-    // split-K down-projection (two launches, X read twice)
-    if (rpbh_lowrank_fusable(K, r))
-      return hip_status(launch_rpbh_mx_lowrank(center != 0, Xh, M, K, xf->perm, xf->sign,
-                                               static_cast<const __half*>(L1), r, Th, codes,
-                                               static_cast<uint8_t*>(scales), static_cast<__half*>(mu), stream));
+    // the permutation spans the whole row, so the quantizer stages full rows while the
+    // projection streams k-chunks of 64-row blocks: the transform, then the split-K
+    // down-projection (two launches; X is read twice)
     hipError_t e = launch_rpbh_mx_mfma(center != 0, Xh, M, K, xf->perm, xf->sign, codes, static_cast<uint8_t*>(scales),
                                        static_cast<__half*>(mu), stream);
     if (e != hipSuccess) return KQ_ERR_HIP;

@@ -36,12 +36,6 @@ hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const
                                const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_rpbh_mx_mfma(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
                                const int8_t* sign, uint8_t* codes, uint8_t* scales, __half* mu, hipStream_t s);
-// RPBH + optional centring + MXFP4 and the down-projection T = fp16(X L1^T) in one pass
-// (L1 [r][K], T [M][r]); only where rpbh_lowrank_fusable(K, r).
-bool rpbh_lowrank_fusable(int64_t K, int r);
-hipError_t launch_rpbh_mx_lowrank(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
-                                  const int8_t* sign, const __half* L1, int r, __half* T, uint8_t* codes,
-                                  uint8_t* scales, __half* mu, hipStream_t s);
 // RPBH + per-token Lloyd-Max 4-bit codes (no centring) on the row-group kernel: codes
 // [M][K/2], scales float [M] (s_t = ||x_t|| / sqrt(K)).
 hipError_t launch_rpbh_lm4_mfma(const __half* X, int64_t M, int64_t K, const int32_t* perm, const int8_t* sign,

@@ -441,16 +441,11 @@ __global__ __launch_bounds__(256) void kron_blocks_mx_kernel(const uint4* __rest
 constexpr int RG_MAXW = 16;   // wavefronts per workgroup, at most
 constexpr int RG_COLS = 2;    // 16-byte columns of a row per lane, at most (64 NW >= K / 16)
 constexpr int RG_PV = 4;      // 16-byte perm chunks per lane in the set-up, at most
-constexpr int LR_NW = 8;      // wavefronts per workgroup with the fused low-rank branch
 
 __host__ __device__ constexpr size_t rg_red_offset(int R, int K) {
   return ((size_t)R * K * 2 + (size_t)K * 2 + (size_t)(K / 32) * 4 + 15) & ~(size_t)15;
 }
 __host__ __device__ constexpr size_t rg_lds_bytes(int R, int K) { return rg_red_offset(R, K) + RG_MAXW * 16; }
-// ... plus, with the low-rank branch, the waves' partial T tiles: [LR_NW][R][r] floats
-__host__ __device__ constexpr size_t rg_lr_lds_bytes(int R, int K, int r) {
-  return rg_lds_bytes(R, K) + (size_t)LR_NW * R * r * 4;
-}
 
 template <int R>
 struct GroupChunks {
@@ -480,24 +475,13 @@ __device__ __forceinline__ GroupChunks<R> rg_load(const __half* X, int64_t row0,
 template <int R, int FMT>
 constexpr int rg_maxw() { return (FMT == 1 && R == 4) ? 8 : RG_MAXW; }
 
-// With the low-rank down-projection (RT = r / 16 > 0; SVDQuant explainer §3: the 16-bit
-// branch reads the same X as the 4-bit one, and a separate pass would read it again): the
-// staged rows of each group are also contracted with L1 on the matrix cores,
-// T = fp16(X L1^T) from the original X (neither centred nor rotated).  L1 stays in the
-// registers of the workgroup's waves for the whole launch (wave w holds the A fragments of
-// k-steps SPW w .. SPW w + SPW - 1, 32 k each, SPW = 24 / RT), so it is read
-// once per workgroup instead of once per group; each wave contracts its k-steps of the
-// group (v_mfma_f32_16x16x32_f16, L1 rows as A, the group's rows as B columns 0..R-1), and
-// the waves' partial tiles are summed through LDS in wave order.
-template <int R, bool CENTER, int FMT, int RT = 0>
-__global__ __launch_bounds__((RT > 0 ? 64 * LR_NW : 64 * rg_maxw<R, FMT>())) void rpbh_mx_group_kernel(
+template <int R, bool CENTER, int FMT>
+__global__ __launch_bounds__((64 * rg_maxw<R, FMT>())) void rpbh_mx_group_kernel(
     const __half* X, int64_t M, int K, const int32_t* __restrict__ perm,
     const int8_t* __restrict__ sign, LmTables lm, uint8_t* __restrict__ codes, void* __restrict__ scales,
-    __half* __restrict__ mu, const __half* __restrict__ L1, __half* __restrict__ Tout) {
+    __half* __restrict__ mu) {
   static_assert(R == 2 || R == 4, "rows per group");
   static_assert(FMT == 0 || !CENTER, "the Lloyd-Max output is offered without centring");
-  static_assert(RT == 0 || (R == 4 && FMT == 0), "the low-rank branch is fused with four-row MXFP4 groups");
-  constexpr int SPW = RT > 0 ? 24 / RT : 1;    // this wave's k-steps of L1
   constexpr bool RSUM = CENTER || FMT == 1;     // a per-row reduction over the staged row
   extern __shared__ __align__(16) unsigned char smem[];
   const int t = threadIdx.x, T = blockDim.x, NW = T >> 6, lane = t & 63, wid = t >> 6;
@@ -555,24 +539,6 @@ __global__ __launch_bounds__((RT > 0 ? 64 * LR_NW : 64 * rg_maxw<R, FMT>())) voi
     smask[sbk] = m;
   }
   const MfmaXform xf = mfma_xform_hadamard(lane);
-
-  // low-rank branch: this wave's L1 fragments (A operand of 16x16x32: lane l holds row
-  // 16 jt + l % 16 of L1, k = 32 s + 8 (l / 16) .. + 7); steps past K/32 are zero
-  constexpr int RR = 16 * RT;
-  v8h l1f[RT > 0 ? RT : 1][SPW];
-  const int nsteps = K >> 5;
-  const int s0 = wid * SPW;
-  if (RT > 0) {
-#pragma unroll
-    for (int jt = 0; jt < RT; ++jt)
-#pragma unroll
-      for (int st = 0; st < SPW; ++st) {
-        const int k = 32 * (s0 + st) + 8 * q;
-        l1f[jt][st] = s0 + st < nsteps ? *reinterpret_cast<const v8h*>(L1 + (int64_t)(16 * jt + bl) * K + k)
-                                       : v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-  }
-  float* const tpart = reinterpret_cast<float*>(smem + rg_lds_bytes(R, K));   // [LR_NW][R][RR]
 
   for (; g < ngroups; g += gridDim.x) {
     lds_barrier();       // the previous group's gathers are done (and the table is written)
@@ -634,43 +600,6 @@ __global__ __launch_bounds__((RT > 0 ? 64 * LR_NW : 64 * rg_maxw<R, FMT>())) voi
       if ((lane & 15) == 0 && (R == 4 || (lane & 16) == 0)) red[wid * 4 + (R == 4 ? (lane >> 4) : (lane >> 5))] = v;
     }
     lds_barrier();       // the group is staged (and the partial sums are visible)
-    if (RT > 0) {
-      // this wave's k-steps of T = X L1^T for the group's rows: B operand lane l = row
-      // l % 16 (rows 0..R-1 real, the others zero), k = 32 s + 8 (l / 16) .. + 7, read from
-      // the interleaved staging (position k holds the R rows' halves) and de-interleaved
-      const int n = bl & 3;
-      const uint32_t psel = (n & 1) ? KQ_PERM_HI : KQ_PERM_LO;
-      v4f tacc[RT > 0 ? RT : 1];
-#pragma unroll
-      for (int jt = 0; jt < RT; ++jt) tacc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < SPW; ++st) {
-        const int k = 32 * min(s0 + st, nsteps - 1) + 8 * q;       // past the end: a real position, A is zero
-        const v4u* src = reinterpret_cast<const v4u*>(slot + (size_t)k * (R * 2));
-        v4u d[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) d[u] = src[u];                  // positions k .. k + 7, all four rows
-        // d[m] = positions k + 2m (dwords 0, 1: rows 0 1, rows 2 3) and k + 2m + 1 (dwords
-        // 2, 3); row n's halves of the two positions form dword m of the operand
-        v4u bw;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t x0 = (n >> 1) ? d[m][1] : d[m][0];
-          const uint32_t x1 = (n >> 1) ? d[m][3] : d[m][2];
-          bw[m] = bl < R ? __builtin_amdgcn_perm(x1, x0, psel) : 0u;
-        }
-        const v8h b = __builtin_bit_cast(v8h, bw);
-#pragma unroll
-        for (int jt = 0; jt < RT; ++jt) tacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(l1f[jt][st], b, tacc[jt], 0, 0, 0);
-      }
-      // tacc[jt][i] = partial T[row l % 16][16 jt + 4 (l / 16) + i]
-      if (bl < R) {
-#pragma unroll
-        for (int jt = 0; jt < RT; ++jt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tpart[(wid * R + bl) * RR + 16 * jt + 4 * q + i] = tacc[jt][i];
-      }
-    }
     float m32[R], scr[R];          // the centring term, or the Lloyd-Max scale, per row
 #pragma unroll
     for (int r = 0; r < R; ++r) m32[r] = scr[r] = 0.0f;
@@ -778,16 +707,6 @@ __global__ __launch_bounds__((RT > 0 ? 64 * LR_NW : 64 * rg_maxw<R, FMT>())) voi
           __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb[r], rscales, soff + (soff == KQ_OOB ? 0 : r * nb), 0, 0);
       }
     }
-    if (RT > 0) {
-      // T of the group's rows: the waves' partial tiles summed in wave order
-      lds_barrier();
-      if (t < R * RR) {
-        const int n = t / RR, j = t % RR;
-        float v = 0.0f;
-        for (int w = 0; w < NW; ++w) v += tpart[(w * R + n) * RR + j];
-        if (g * R + n < M) Tout[(g * R + n) * (int64_t)RR + j] = __float2half_rn(v);
-      }
-    }
   }
 }
 
@@ -842,37 +761,6 @@ hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const fl
   return hipGetLastError();
 }
 
-// RPBH + centring (optional) + MXFP4 + the rank-16/32 down-projection T = X L1^T in one pass
-// (the fused form above): LR_NW wavefronts, persistent workgroups; K r <= 3072 x 32.
-template <bool CENTER, int RT>
-static hipError_t rpbh_lr_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
-                                 const __half* L1, __half* T, uint8_t* codes, uint8_t* scales, __half* mu,
-                                 hipStream_t s) {
-  constexpr int R = 4;
-  const unsigned threads = 64u * LR_NW;
-  const size_t lds = rg_lr_lds_bytes(R, K, 16 * RT);
-  const auto kern = rpbh_mx_group_kernel<R, CENTER, 0, RT>;
-  int64_t grid = (M + R - 1) / R;
-  const int64_t cap =
-      (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), (int)threads, lds);
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, perm, sign, lm_tables(), codes,
-                     scales, mu, L1, T);
-  return hipGetLastError();
-}
-
-bool rpbh_lowrank_fusable(int64_t K, int r) { return (r == 16 || r == 32) && K * r <= 3072 * 32 && K >= 32; }
-
-hipError_t launch_rpbh_mx_lowrank(bool center, const __half* X, int64_t M, int64_t K, const int32_t* perm,
-                                  const int8_t* sign, const __half* L1, int r, __half* T, uint8_t* codes,
-                                  uint8_t* scales, __half* mu, hipStream_t s) {
-  if (!rpbh_lowrank_fusable(K, r)) return hipErrorInvalidValue;
-  if (r == 32)
-    return center ? rpbh_lr_launch<true, 2>(X, M, (int)K, perm, sign, L1, T, codes, scales, mu, s)
-                  : rpbh_lr_launch<false, 2>(X, M, (int)K, perm, sign, L1, T, codes, scales, mu, s);
-  return center ? rpbh_lr_launch<true, 1>(X, M, (int)K, perm, sign, L1, T, codes, scales, mu, s)
-                : rpbh_lr_launch<false, 1>(X, M, (int)K, perm, sign, L1, T, codes, scales, mu, s);
-}
 
 template <int R, bool CENTER, int FMT>
 static hipError_t rpbh_group_launch(const __half* X, int64_t M, int K, const int32_t* perm, const int8_t* sign,
@@ -891,7 +779,7 @@ static hipError_t rpbh_group_launch(const __half* X, int64_t M, int K, const int
       (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), (int)threads, lds);
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, s, X, M, K, perm, sign, lm_tables(), codes, scales,
-                     mu, nullptr, nullptr);
+                     mu);
   return hipGetLastError();
 }
 
