@@ -4,21 +4,26 @@ FLUX.1-like joint-block shape, on one MI355X.
 
 One step = the whole hot path over one batch, for each of the block's three linears
 (qkv 3072->9216, fc1 3072->12288, fc2 12288->3072, M = 4608 tokens):
-    kq_transform_quantize   centre each token, RPBH-32 rotation, MXFP4 quantize + pack
-    kq_lowrank_down         T = X L1^T (rank 32, fp16)
-    kq_w4a4_linear          Y = Xq Wq^T + T L2^T + mu wbar^T (scaled-FP4 MFMA, fp16 out)
+    kq_transform_quantize_lowrank   centre each token, RPBH-32 rotation, MXFP4 quantize +
+                                    pack, and T = X L1^T (rank 32, fp16)
+    kq_w4a4_linear_t                Y = Xq Wq^T + T L2^T + mu wbar^T (scaled-FP4 MFMA, fp16 out)
 Weights are folded once (offline, untimed).  Inputs are seeded synthetic activations
 (Gaussian + per-token adaLN-like shift N(0, 4^2) + 12 outlier channels x50) already
 resident in HBM; the activation buffers rotate over enough copies (>= 1 GiB) that no step
 reads them from the 256 MB last-level cache.
 
-Prints ONE JSON line (rank 0).  The step time comes from two HIP events around the timed
-steps, on the stream the kernels run on, with no event between launches (each one would
-leave the GPU idle for several microseconds).  Per-launch durations come from a second
-timed pass: each call of the step launched K times back to back between two events, with
-the same arguments and rotated activations.  The "traffic" fields come from the HBM byte
-counters recorded in profiles/ for the same kernel source (null when the source has changed
-since).
+Prints ONE JSON line.  The step time comes from two HIP events around the timed steps, on
+the stream the kernels run on, with nothing between the launches.  Per-launch durations:
+10 untimed launches, then 50 timed ones in 5 groups of 10 back to back between two events,
+each group queued behind a short device-side sleep so that the GPU never waits for the
+host (a launch through the binding costs about 11 us of host time, more than some of the
+kernels); the figure is the median of the group means, which matches the profiler's kernel
+durations.  Activations (and, for the GEMM, the packed activation codes, T and mu) rotate
+over >= 1 GiB of copies in these passes too.  The other configurations (CogVideoX-like,
+PixArt-like, SANA-like) are timed the same way, per launch.  The "traffic" fields come
+from the HBM byte counters recorded in profiles/ for the same kernel source (null when the
+source has changed since).  The GPU clock is sampled through the SMI library while GEMMs
+run, and the matrix-core peak is also given at that clock.
 """
 
 import argparse
@@ -28,6 +33,7 @@ import math
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -36,8 +42,10 @@ if ROOT not in sys.path:
 
 METRIC = "act transform+quant GB/s and W4A4+LR linear TFLOPS at FLUX shape, % of roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
-PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA at the 2.4 GHz peak engine clock
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA at 2.4 GHz
+PEAK_CLOCK_MHZ = 2400.0
+SLEEP_CYCLES = 2_000_000       # device-side sleep that lets the host queue a group of launches
 
 
 def log(*a):
@@ -52,6 +60,12 @@ def layer_flops(M, K, N, r, center):
 def gemm_flops(M, K, N, r, center):
     """Flops inside the W4A4 kernel launch: 4-bit product, low-rank up-projection, rank-1."""
     return 2 * M * N * K + 2 * M * N * r + (2 * M * N if center else 0)
+
+
+def composite_floor_s(M, K, N, r):
+    """Time of the linear (down-projection + GEMM) at the peaks: the 4-bit product at the
+    MXFP4 peak plus both fp16 low-rank projections at the fp16 peak."""
+    return 2 * M * N * K / (PEAK_FP4_TFLOPS * 1e12) + 2 * M * r * (K + N) / (PEAK_FP16_TFLOPS * 1e12)
 
 
 def transform_bytes(M, K, center, fmt="mxfp4"):
@@ -97,7 +111,8 @@ def recorded_traffic(kind):
 
 def cpu_baseline(cfg_idx, rows, col_frac=4):
     """Time the float64 oracle (as it stands) on a bounded sample of the workload: `rows`
-    tokens and 1/col_frac of the output columns of every linear."""
+    tokens and 1/col_frac of the output columns of every linear; the transform+quantize and
+    the linear are timed separately."""
     import synth
     from oracle import linear, pipeline
     try:
@@ -106,8 +121,8 @@ def cpu_baseline(cfg_idx, rows, col_frac=4):
     except Exception:
         threads = os.cpu_count() or 1
     cfg = synth.CONFIGS[cfg_idx]
-    flops = 0
-    secs = 0.0
+    flops = tq_bytes = 0
+    t_tq = t_lin = 0.0
     for li, (name, K, N) in enumerate(cfg["layers"]):
         Ns = N // col_frac
         X = synth.activations(rows, K, cfg_idx, cfg["sigma_mu"], cfg["frames"])
@@ -117,14 +132,161 @@ def cpu_baseline(cfg_idx, rows, col_frac=4):
         fw = pipeline.fold_weights(W, xf, cfg["wfmt"])          # offline, not timed
         t0 = time.perf_counter()
         a = pipeline.transform_quantize(X, xf, cfg["fmt"], cfg["center"])
+        t1 = time.perf_counter()
         linear.w4a4_linear(a["codes"], a["scales"], fw["wcodes"], fw["wscales"], X, L1, L2,
                            a["mu"], fw["wbar"] if cfg["center"] else None)
-        secs += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_tq += t1 - t0
+        t_lin += t2 - t1
         flops += layer_flops(rows, K, Ns, cfg["rank"], cfg["center"])
+        tq_bytes += transform_bytes(rows, K, cfg["center"])
+    secs = t_tq + t_lin
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "transform_quant_s": round(t_tq, 3), "transform_quant_GBps": round(tq_bytes / t_tq / 1e9, 4),
+            "linear_s": round(t_lin, 3), "linear_TFLOPs": flops / t_lin / 1e12,
             "sample": f"{rows} tokens x 1/{col_frac} of the output columns of each of the "
-                      f"{len(cfg['layers'])} linears (full K): float64 transform+quantize and "
-                      f"dequantize+matmul linear, weight fold excluded; {secs:.1f} s of CPU time"}
+                      f"{len(cfg['layers'])} linears (full K): float64 transform+quantize ({t_tq:.1f} s) and "
+                      f"dequantize+matmul linear ({t_lin:.1f} s), weight fold excluded"}
+
+
+class Timer:
+    """Per-launch durations that the host cannot bias (see the module docstring)."""
+
+    def __init__(self, torch, n=50, warm=10, groups=5):
+        self.torch, self.n, self.warm, self.groups = torch, n, warm, groups
+
+    def __call__(self, fn):
+        torch = self.torch
+        for i in range(self.warm):
+            fn(i)
+        torch.cuda.synchronize()
+        per = self.n // self.groups
+        means = []
+        k = self.warm
+        for _ in range(self.groups):
+            torch.cuda._sleep(SLEEP_CYCLES)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(per):
+                fn(k)
+                k += 1
+            b.record()
+            torch.cuda.synchronize()
+            means.append(a.elapsed_time(b) / per)
+        means.sort()
+        return means[len(means) // 2]          # ms
+
+
+def _clock_reader(torch):
+    """A function returning the current graphics clock in MHz (the median over the compute
+    dies where the SMI library reports them one by one), or None when there is no SMI."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            per_die = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and v > 0]
+            if per_die:
+                return sorted(per_die)[len(per_die) // 2]
+            v = m.get("current_gfxclk")
+            return float(v) if isinstance(v, (int, float)) else None
+        read()
+        return read
+    except Exception as e:                      # noqa: BLE001 -- no SMI access on this host
+        log(f"SMI clock unavailable ({e}); trying torch.cuda.clock_rate")
+    try:
+        torch.cuda.clock_rate(0)
+        return lambda: float(torch.cuda.clock_rate(0))
+    except Exception as e:                      # noqa: BLE001
+        log(f"clock sampling unavailable: {e}")
+        return None
+
+
+def sample_clock(torch, run, seconds=0.25):
+    """Median GPU (graphics) clock in MHz while `run()` keeps the device busy; None when it
+    cannot be read."""
+    read = _clock_reader(torch)
+    if read is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                v = read()
+                if v:
+                    samples.append(v)
+            except Exception:                   # noqa: BLE001
+                pass
+            time.sleep(0.002)
+
+    th = threading.Thread(target=poll, daemon=True)
+    run()
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    samples.sort()
+    return samples[len(samples) // 2] if samples else None
+
+
+def rotation_count(set_bytes):
+    return max(2, math.ceil((1 << 30) / set_bytes))
+
+
+def kron_config(torch, kq, synth, timer, cfg_idx, dev):
+    """Per-launch timings of a Kronecker-transform MXFP4 configuration (no centring): the
+    transform alone, the transform fused with the rank-32 down-projection (one kernel, X
+    read once), and the W4A4 GEMM with the up-projection in its epilogue."""
+    cfg = synth.CONFIGS[cfg_idx]
+    M, r = cfg["M"], cfg["rank"]
+    widths = sorted({K for _, K, _ in cfg["layers"]})
+    X0 = {K: torch.from_numpy(synth.activations(M, K, cfg_idx, cfg["sigma_mu"], cfg["frames"])).to(dev) for K in widths}
+    R = rotation_count(sum(x.numel() * 2 for x in X0.values()))
+    Xs = [X0] + [{K: x.clone() for K, x in X0.items()} for _ in range(R - 1)]
+    out = []
+    for li, (name, K, N) in enumerate(cfg["layers"]):
+        W, L1, L2 = synth.weights(K, N, cfg_idx, li, r)
+        A, B = synth.kron_factors(cfg_idx, li)
+        xf = kq.Xform.kron(A, B, K)
+        wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W).to(dev), xf, fmt="mxfp4", with_wbar=False)
+        L1d, L2d = torch.from_numpy(L1).to(dev), torch.from_numpy(L2).to(dev)
+        wsp = torch.empty((max(kq.lowrank_down_workspace_bytes(M, K, r), 16),), dtype=torch.uint8, device=dev)
+        # one set of activation codes and T per rotated input, for the GEMM pass
+        acts = []
+        for s in range(R):
+            c, sc, _, T = kq.transform_quantize_lowrank(Xs[s][K], xf, L1d, workspace=wsp)
+            acts.append((c, sc, T))
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        c0, s0 = acts[0][0], acts[0][1]
+        T0 = torch.empty_like(acts[0][2])
+        t_tq = timer(lambda i: kq.transform_quantize(Xs[i % R][K], xf, codes=c0, scales=s0))
+        t_fu = timer(lambda i: kq.transform_quantize_lowrank(Xs[i % R][K], xf, L1d, codes=c0, scales=s0, T=T0,
+                                                             workspace=wsp))
+        t_gm = timer(lambda i: kq.w4a4_linear_t(acts[i % R][0], acts[i % R][1], wc, ws, T=acts[i % R][2], L2=L2d,
+                                                Y=Y))
+        tb = transform_bytes(M, K, False)
+        gfl = gemm_flops(M, K, N, r, False)
+        lin = layer_flops(M, K, N, r, False)
+        out.append({"layer": name, "M": M, "K": K, "N": N,
+                    "transform_quant_us": round(t_tq * 1e3, 2), "transform_quant_GBps": round(tb / t_tq / 1e6, 1),
+                    "transform_quant_frac_hbm": round(tb / t_tq / 1e6 / PEAK_HBM_GBS, 4),
+                    "transform_lowrank_fused_us": round(t_fu * 1e3, 2),
+                    "w4a4_gemm_us": round(t_gm * 1e3, 2), "w4a4_gemm_TFLOPs": round(gfl / t_gm / 1e9, 1),
+                    "w4a4_gemm_frac_fp4": round(gfl / t_gm / 1e9 / PEAK_FP4_TFLOPS, 4),
+                    "layer_us": round((t_fu + t_gm) * 1e3, 2), "layer_TFLOPs": round(lin / (t_fu + t_gm) / 1e9, 1)})
+        log(f"cfg {cfg_idx} {name}: kron transform {t_tq*1e3:7.2f} us {tb/t_tq/1e6:7.1f} GB/s | fused with "
+            f"lowrank {t_fu*1e3:7.2f} us | W4A4 {t_gm*1e3:8.2f} us {gfl/t_gm/1e9:7.1f} TFLOP/s")
+        del acts
+    del Xs
+    torch.cuda.empty_cache()
+    return {"workload": cfg["name"], "M": M, "rotated_input_sets": R, "layers": out}
 
 
 def main():
@@ -135,7 +297,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="activation buffer sets (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-variants", action="store_true", help="skip the transform-variant timings")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other configurations and the transform variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -156,6 +319,7 @@ def main():
     kq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    timer = Timer(torch)
     CFG = 3
     cfg = synth.CONFIGS[CFG]
     M, r, center = cfg["M"], cfg["rank"], cfg["center"]
@@ -163,8 +327,7 @@ def main():
     # ---- inputs and offline preparation (untimed)
     widths = sorted({K for _, K, _ in cfg["layers"]})
     X0 = {K: torch.from_numpy(synth.activations(M, K, CFG, cfg["sigma_mu"], cfg["frames"])).to(dev) for K in widths}
-    set_bytes = sum(x.numel() * 2 for x in X0.values())
-    R = args.rotate or max(2, math.ceil((1 << 30) / set_bytes))
+    R = args.rotate or rotation_count(sum(x.numel() * 2 for x in X0.values()))
     Xsets = [X0] + [{K: x.clone() for K, x in X0.items()} for _ in range(R - 1)]
     layers = []
     for li, (name, K, N) in enumerate(cfg["layers"]):
@@ -182,36 +345,28 @@ def main():
             lrws=torch.empty((max(kq.lowrank_down_workspace_bytes(M, K, r), 16),), dtype=torch.uint8, device=dev),
             Y=torch.empty((M, N), dtype=torch.float16, device=dev)))
     torch.cuda.synchronize()
-
-    # The calls of one step, per layer: transform, low-rank projection, GEMM.  The first two
-    # are independent and read the same X; in this order the projection, the more
-    # bandwidth-bound of the two, finds X in the last-level cache (about 2% off the step).
-    # Input set s % R feeds step s.
     nl = len(layers)
 
-    def call(li, k, s):
+    def act_pass(li, s):
         L, X = layers[li], Xsets[s % R][layers[li]["K"]]
-        if k == 0:
-            kq.lowrank_down(X, L["L1"], T=L["T"], workspace=L["lrws"])
-        elif k == 1:
-            kq.transform_quantize(X, L["xf"], fmt="mxfp4", center=center, codes=L["codes"], scales=L["scales"],
-                                  mu=L["mu"])
-        else:
-            kq.w4a4_linear_t(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
-                           wbar=L["wbar"], Y=L["Y"])
+        kq.transform_quantize_lowrank(X, L["xf"], L["L1"], center=center, codes=L["codes"], scales=L["scales"],
+                                      mu=L["mu"], T=L["T"], workspace=L["lrws"])
+
+    def gemm(li):
+        L = layers[li]
+        kq.w4a4_linear_t(L["codes"], L["scales"], L["wc"], L["ws"], T=L["T"], L2=L["L2"], mu=L["mu"],
+                         wbar=L["wbar"], Y=L["Y"])
 
     def step(s):
         for li in range(nl):
-            for k in (1, 0, 2):
-                call(li, k, s)
+            act_pass(li, s)
+            gemm(li)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps between two events on the stream the kernels run
-    # on, with nothing between the launches (an event recorded between two launches
-    # leaves the GPU idle for several microseconds)
+    # ---- timed region: K whole steps between two events on the stream the kernels run on
     t0 = time.perf_counter()
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_start.record()
@@ -222,29 +377,46 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us per step")
 
-    # ---- per-launch durations: each call of the step, K launches back to back between two
-    # events (the same arguments, the activations rotated as in the step), so a launch's
-    # figure is its kernels' time as the profiler's trace sees it
-    dur = [[0.0, 0.0, 0.0] for _ in range(nl)]   # [transform, low-rank, GEMM] per layer
-    for li in range(nl):
-        for k in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for s in range(args.steps):
-                call(li, k, args.warmup + s)
-            b.record()
-            torch.cuda.synchronize()
-            dur[li][(1, 0, 2)[k]] = a.elapsed_time(b) / args.steps
+    # ---- per-launch durations, each call of the step on its own.  The GEMM reads packed
+    # activations, T and mu rotated like the inputs (one set per input copy, made here)
+    per_layer = []
+    dur = []
+    for li, L in enumerate(layers):
+        K = L["K"]
+        sets = []
+        for s in range(R):
+            c, sc, mu_s, T_s = kq.transform_quantize_lowrank(Xsets[s][K], L["xf"], L["L1"], center=center,
+                                                              workspace=L["lrws"])
+            sets.append((c, sc, mu_s, T_s))
+        t_tq = timer(lambda i: kq.transform_quantize(Xsets[i % R][K], L["xf"], center=center, codes=L["codes"],
+                                                     scales=L["scales"], mu=L["mu"]))
+        t_lr = timer(lambda i: kq.lowrank_down(Xsets[i % R][K], L["L1"], T=L["T"], workspace=L["lrws"]))
+        t_fu = timer(lambda i: act_pass(li, i))
+        t_gm = timer(lambda i: kq.w4a4_linear_t(sets[i % R][0], sets[i % R][1], L["wc"], L["ws"], T=sets[i % R][3],
+                                                L2=L["L2"], mu=sets[i % R][2], wbar=L["wbar"], Y=L["Y"]))
+        dur.append((t_tq, t_lr, t_fu, t_gm))
+        log(f"per-launch {L['name']}: {t_tq * 1e3:.2f} / {t_lr * 1e3:.2f} / {t_fu * 1e3:.2f} / {t_gm * 1e3:.2f} us")
+        del sets
 
-    # ---- transform variants beside the path (not part of the step): the Kronecker factors
-    # and a dense 32x32 P on the same streaming matrix-core kernel, per-block factors on
-    # theirs, MXFP4 without centring,
-    # each also behind power-of-two channel scaling (exponent 6 on the planted outlier
-    # channels), at the step's widths; event pair around back-to-back launches over the
-    # rotated inputs
-    variants = []
+    # ---- the GPU clock while the GEMMs run
+    def gemm_round():
+        for li in range(nl):
+            gemm(li)
+    clock_mhz = sample_clock(torch, gemm_round)
+
+    # ---- the other configurations, per launch
+    others = {}
+    variants, sana = [], []
     if not args.no_variants:
+        for ci, key in ((4, "cogvideox_like_cfg4"), (1, "pixart_block_cfg1"), (0, "pixart_single_cfg0")):
+            others[key] = kron_config(torch, kq, synth, timer, ci, dev)
+
+        # transform variants beside the path (not part of the step), at the step's widths:
+        # the Kronecker factors and a dense 32x32 P on the streaming matrix-core kernel,
+        # per-block factors on theirs, MXFP4 without centring, each also behind
+        # power-of-two channel scaling (exponent 6 on the planted outlier channels)
         for K in widths:
             A, B = synth.kron_factors(CFG, 0)
             P = torch.from_numpy(synth.dense_block(CFG, 0)).to(dev)
@@ -254,85 +426,39 @@ def main():
             Ab, Bb = synth.kron_block_factors(CFG, 0, K // 32)
             AB = torch.from_numpy(kq.Xform.pack_block_factors(Ab, Bb)).to(dev)
             kx, dx, bx = kq.Xform.kron(A, B, K), kq.Xform.dense(P, K), kq.Xform.kron_blocks(AB, K)
-            for name, xf in (("kron_4x8", kx), ("dense_32", dx), ("kron_blocks", bx), ("kron_4x8+pts", kx.with_pts(pts)),
-                             ("dense_32+pts", dx.with_pts(pts)), ("kron_blocks+pts", bx.with_pts(pts))):
-                def run(i, xf=xf, K=K):
-                    kq.transform_quantize(Xsets[i % R][K], xf, fmt="mxfp4", codes=codes, scales=scales)
-                run(0)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                n = 20
-                a.record()
-                for i in range(n):
-                    run(i + 1)
-                b.record()
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / n
-                tb = transform_bytes(M, K, False)
+            L = next(L for L in layers if L["K"] == K)
+            for name, xf, c in (("rpbh_32 (no centring)", L["xf"], False), ("rpbh_32 centred", L["xf"], True),
+                                ("kron_4x8", kx, False), ("dense_32", dx, False), ("kron_blocks", bx, False),
+                                ("kron_4x8+pts", kx.with_pts(pts), False), ("dense_32+pts", dx.with_pts(pts), False),
+                                ("kron_blocks+pts", bx.with_pts(pts), False)):
+                ms = timer(lambda i, xf=xf, c=c: kq.transform_quantize(Xsets[i % R][K], xf, fmt="mxfp4", center=c,
+                                                                       codes=codes, scales=scales, mu=L["mu"]))
+                tb = transform_bytes(M, K, c)
                 variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
                                  "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
-                log(f"variant {name:>15} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
-            # the Kronecker transform and the rank-32 down-projection: two calls (X read
-            # twice) against the fused pass (X read once)
-            L1 = torch.from_numpy(np.ascontiguousarray(synth.weights(K, 64, CFG, 0, 32)[1])).to(dev)
-            T = torch.empty((M, 32), dtype=torch.float16, device=dev)
-            nbw = kq.lowrank_down_workspace_bytes(M, K, 32)
-            wsp = torch.empty((max(nbw, 16),), dtype=torch.uint8, device=dev)
-            tb = transform_bytes(M, K, False) + 2 * 32 * K + 2 * M * 32
-            for name in ("kron_4x8 then lowrank", "kron_4x8+lowrank fused"):
-                def run(i, name=name, K=K):
-                    Xi = Xsets[i % R][K]
-                    if name.endswith("fused"):
-                        kq.transform_quantize_lowrank(Xi, kx, L1, codes=codes, scales=scales, T=T, workspace=wsp)
-                    else:
-                        kq.transform_quantize(Xi, kx, fmt="mxfp4", codes=codes, scales=scales)
-                        kq.lowrank_down(Xi, L1, T=T, workspace=wsp)
-                run(0)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                n = 20
-                a.record()
-                for i in range(n):
-                    run(i + 1)
-                b.record()
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / n
-                variants.append({"transform": name, "M": M, "K": K, "us": round(ms * 1e3, 2),
-                                 "GBps": round(tb / ms / 1e6, 1), "frac": round(tb / ms / 1e6 / PEAK_HBM_GBS, 4)})
-                log(f"variant {name:>22} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s (X read once: algorithmic)")
+                log(f"variant {name:>22} K={K:5d}: {ms*1e3:7.2f} us {tb/ms/1e6:8.1f} GB/s")
 
-    # ---- the SANA-like workload's Lloyd-Max path, beside the step: per layer the RPBH +
-    # per-token Lloyd-Max transform (4-bit sign-magnitude codes, one fp32 scale per token)
-    # and the W2A4 linear (2-bit weights with fp16 group scales, dequantized through LDS
-    # tables to fp16 for the matrix cores: its roofline is the fp16 peak), each an event
-    # pair around back-to-back launches over rotated copies of the input
-    sana = []
-    if not args.no_variants:
+        # the SANA-like workload's Lloyd-Max path: per layer the RPBH + per-token Lloyd-Max
+        # transform (4-bit sign-magnitude codes, one fp32 scale per token) and the W2A4 linear
+        # (2-bit weights with fp16 group scales, dequantized through LDS tables to fp16 for
+        # the matrix cores: its roofline is the fp16 peak)
         c2 = synth.CONFIGS[2]
         M2 = c2["M"]
         for li, (name, K, N) in enumerate(c2["layers"]):
             X2 = torch.from_numpy(synth.activations(M2, K, 2, c2["sigma_mu"], c2["frames"])).to(dev)
-            nrot = max(2, math.ceil((1 << 30) / (X2.numel() * 2)))
+            nrot = rotation_count(X2.numel() * 2)
             X2s = [X2] + [X2.clone() for _ in range(nrot - 1)]
             W2, _, _ = synth.weights(K, N, 2, li, 0)
             perm, sign = synth.rpbh_params(K, 2, li)
             xf2 = kq.Xform.rpbh(torch.from_numpy(perm).to(dev), torch.from_numpy(sign).to(dev))
             wc2, ws2, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W2).to(dev), xf2, fmt="lm2")
+            sets2 = [kq.transform_quantize(X2s[s], xf2, fmt="lm4")[:2] for s in range(nrot)]
             codes2 = torch.empty((M2, K // 2), dtype=torch.uint8, device=dev)
             scales2 = torch.empty((M2,), dtype=torch.float32, device=dev)
             Y2 = torch.empty((M2, N), dtype=torch.float16, device=dev)
-
-            def timed(fn, n=20):
-                fn(0)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                for i in range(n):
-                    fn(i + 1)
-                b.record()
-                torch.cuda.synchronize()
-                return a.elapsed_time(b) / n
-
-            ms_tq = timed(lambda i: kq.transform_quantize(X2s[i % nrot], xf2, fmt="lm4", codes=codes2,
-                                                          scales=scales2))
-            ms_mm = timed(lambda i: kq.w4a4_linear_t(codes2, scales2, wc2, ws2, fmt="lm2", Y=Y2))
+            ms_tq = timer(lambda i: kq.transform_quantize(X2s[i % nrot], xf2, fmt="lm4", codes=codes2, scales=scales2))
+            ms_mm = timer(lambda i: kq.w4a4_linear_t(sets2[i % nrot][0], sets2[i % nrot][1], wc2, ws2, fmt="lm2",
+                                                     Y=Y2))
             tb = M2 * K * 2 + M2 * K // 2 + M2 * 4
             fl = 2 * M2 * N * K
             sana.append({"layer": name, "M": M2, "K": K, "N": N,
@@ -342,7 +468,7 @@ def main():
                          "w2a4_frac_fp16_peak": round(fl / ms_mm / 1e9 / PEAK_FP16_TFLOPS, 4)})
             log(f"sana-like {name}: RPBH+LM4 {ms_tq*1e3:7.2f} us {tb/ms_tq/1e6:8.1f} GB/s | "
                 f"W2A4 {ms_mm*1e3:7.2f} us {fl/ms_mm/1e9:8.1f} TFLOP/s")
-            del X2s
+            del X2s, sets2
 
     if args.copy_calibration:
         # a plain elementwise pass over 256 MiB (read 256 MiB, write 256 MiB): the reference
@@ -355,10 +481,10 @@ def main():
 
     traffic_gemm = recorded_traffic("w4a4_gemm")
     traffic_tq = recorded_traffic("transform")
-    per_layer = []
     tot_flops = tot_gemm_flops = tot_tq_bytes = 0
-    tot_tq_ms = tot_lr_ms = tot_gemm_ms = 0.0
-    for L, (tq_ms, lr_ms, gm_ms) in zip(layers, dur):
+    tot_tq_ms = tot_lr_ms = tot_fu_ms = tot_gemm_ms = 0.0
+    floor_s = 0.0
+    for L, (tq_ms, lr_ms, fu_ms, gm_ms) in zip(layers, dur):
         K, N = L["K"], L["N"]
         fl = layer_flops(M, K, N, r, center)
         gfl = gemm_flops(M, K, N, r, center)
@@ -368,29 +494,38 @@ def main():
         tot_tq_bytes += tb
         tot_tq_ms += tq_ms
         tot_lr_ms += lr_ms
+        tot_fu_ms += fu_ms
         tot_gemm_ms += gm_ms
+        floor_s += composite_floor_s(M, K, N, r)
         per_layer.append({
             "layer": L["name"], "M": M, "K": K, "N": N,
             "transform_quant_us": round(tq_ms * 1e3, 2),
             "transform_quant_GBps": round(tb / tq_ms / 1e6, 1),
+            "transform_quant_frac_hbm": round(tb / tq_ms / 1e6 / PEAK_HBM_GBS, 4),
             "lowrank_down_us": round(lr_ms * 1e3, 2),
+            "transform_lowrank_call_us": round(fu_ms * 1e3, 2),
             "w4a4_gemm_us": round(gm_ms * 1e3, 2),
             "w4a4_gemm_TFLOPs": round(gfl / gm_ms / 1e9, 1),
+            "w4a4_gemm_frac_fp4": round(gfl / gm_ms / 1e9 / PEAK_FP4_TFLOPS, 4),
             "w4a4_gemm_algorithmic_bytes": gemm_bytes(M, K, N, r, center),
             "w4a4_gemm_traffic_bytes": traffic_gemm.get(L["name"]) if traffic_gemm else None,
             "transform_quant_traffic_bytes": traffic_tq.get(L["name"]) if traffic_tq else None,
             "linear_TFLOPs": round(fl / (lr_ms + gm_ms) / 1e9, 1),
+            "composite_g2g3_frac": round(composite_floor_s(M, K, N, r) / ((lr_ms + gm_ms) * 1e-3), 4),
         })
         log(f"{L['name']:>4}: transform+quant {tq_ms*1e3:8.2f} us {tb/tq_ms/1e6:8.1f} GB/s | lowrank-down "
-            f"{lr_ms*1e3:7.2f} us | W4A4 GEMM {gm_ms*1e3:8.2f} us {gfl/gm_ms/1e9:8.1f} TFLOP/s")
+            f"{lr_ms*1e3:7.2f} us | both in one call {fu_ms*1e3:7.2f} us | W4A4 GEMM {gm_ms*1e3:8.2f} us "
+            f"{gfl/gm_ms/1e9:8.1f} TFLOP/s")
 
     value = tot_flops / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = tot_gemm_flops / (tot_gemm_ms * 1e-3) / 1e12
     tq_gbs = tot_tq_bytes / (tot_tq_ms * 1e-3) / 1e9
+    composite = floor_s / ((tot_lr_ms + tot_gemm_ms) * 1e-3)
+    peak_at_clock = PEAK_FP4_TFLOPS * clock_mhz / PEAK_CLOCK_MHZ if clock_mhz else None
     log(f"step {ms_per_step*1e3:.1f} us; whole-step linear throughput {value:.1f} TFLOP/s; "
-        f"GEMM {gemm_tflops:.1f} TFLOP/s ({gemm_tflops/PEAK_FP4_TFLOPS:.1%} of MXFP4 peak); "
-        f"transform+quant {tq_gbs:.1f} GB/s ({tq_gbs/PEAK_HBM_GBS:.1%} of HBM peak); wall {wall:.2f} s; "
-        f"host submission {host_submit / args.steps * 1e6:.1f} us per step")
+        f"GEMM {gemm_tflops:.1f} TFLOP/s ({gemm_tflops/PEAK_FP4_TFLOPS:.1%} of MXFP4 peak); composite "
+        f"G2+G3 {composite:.1%}; transform+quant {tq_gbs:.1f} GB/s ({tq_gbs/PEAK_HBM_GBS:.1%} of HBM peak); "
+        f"clock {clock_mhz} MHz; wall {wall:.2f} s; host submission {host_submit / args.steps * 1e6:.1f} us per step")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -401,13 +536,20 @@ def main():
                                "qkv 3072->9216, fc1 3072->12288, fc2 12288->3072; centred RPBH-32 + MXFP4 "
                                "activations and weights, rank-32 fp16 branch, rank-1 mean restore",
                    "tokens": M, "rotated_input_sets": R},
-        "roofline": {"bound": "mfma", "kernel": "kq_w4a4_linear (W4A4 GEMM + fused low-rank/rank-1 epilogue), "
+        "roofline": {"bound": "mfma", "kernel": "kq_w4a4_linear_t (W4A4 GEMM + fused low-rank/rank-1 epilogue), "
                                                 "the three launches of one step",
                      "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": (round(sum(traffic_gemm.get(L["name"], 0.0) for L in layers))
                                  if traffic_gemm else None),
-                     "algorithmic_bytes": sum(gemm_bytes(M, L["K"], L["N"], r, center) for L in layers)},
+                     "algorithmic_bytes": sum(gemm_bytes(M, L["K"], L["N"], r, center) for L in layers),
+                     "peak_at_measured_clock": round(peak_at_clock, 1) if peak_at_clock else None,
+                     "frac_at_measured_clock": round(gemm_tflops / peak_at_clock, 4) if peak_at_clock else None},
+        "roofline_composite_g2g3": {"bound": "mfma", "definition": "(2MNK / MXFP4 peak + 2Mr(K+N) / fp16 peak) / "
+                                                                  "(down-projection + GEMM time), the three layers",
+                                    "frac": round(composite, 4),
+                                    "floor_us": round(floor_s * 1e6, 2),
+                                    "time_us": round((tot_lr_ms + tot_gemm_ms) * 1e3, 2)},
         "roofline_transform": {"bound": "hbm", "kernel": "kq_transform_quantize (centre + RPBH-32 + MXFP4), "
                                                          "the three launches of one step",
                                "achieved": round(tq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -415,10 +557,14 @@ def main():
                                "traffic": (round(sum(traffic_tq.get(L["name"], 0.0) for L in layers))
                                            if traffic_tq else None),
                                "algorithmic_bytes": tot_tq_bytes},
+        "clock": {"gfx_mhz_during_gemm": clock_mhz, "peak_engine_mhz": PEAK_CLOCK_MHZ,
+                  "source": "SMI current graphics clock (median over the compute dies), median of samples taken every 2 ms while the step's GEMMs ran"},
         "transform_quant_GBps": round(tq_gbs, 1),
         "w4a4_gemm_TFLOPs": round(gemm_tflops, 1),
         "linear_TFLOPs": round(tot_flops / ((tot_lr_ms + tot_gemm_ms) * 1e-3) / 1e12, 1),
         "per_layer": per_layer,
+        "timing": "per-launch: median of 5 group means, 50 launches after 10 warm-up, host queued ahead",
+        "other_configs": others,
         "context": "KroQuant page: its quantization kernel up to 14% faster than SmoothQuant's on an MI350 "
                    "(relative only, other chip)",
         "transform_variants": variants,

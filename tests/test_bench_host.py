@@ -44,3 +44,12 @@ def test_recorded_traffic_is_per_layer_or_absent(kind):
     or nothing."""
     t = bench.recorded_traffic(kind)
     assert t is None or (set(t) == {"qkv", "fc1", "fc2"} and all(v > 0 for v in t.values()))
+
+
+def test_composite_floor_prices_each_product_at_its_own_peak():
+    """The linear's floor: the 4-bit product at the MXFP4 peak, both fp16 low-rank
+    projections (X L1^T and T L2^T) at the fp16 peak."""
+    M, K, N, r = 4608, 3072, 9216, 32
+    want = 2 * M * N * K / 10.1e15 + 2 * M * r * (K + N) / 2.5e15
+    assert bench.composite_floor_s(M, K, N, r) == pytest.approx(want, rel=1e-12)
+    assert bench.composite_floor_s(M, K, N, 0) == pytest.approx(2 * M * N * K / 10.1e15, rel=1e-12)
