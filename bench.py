@@ -22,8 +22,8 @@ durations.  Activations (and, for the GEMM, the packed activation codes, T and m
 over >= 1 GiB of copies in these passes too.  The other configurations (CogVideoX-like,
 PixArt-like, SANA-like) are timed the same way, per launch.  The "traffic" fields come
 from the HBM byte counters recorded in profiles/ for the same kernel source (null when the
-source has changed since).  The GPU clock is sampled through the SMI library while GEMMs
-run, and the matrix-core peak is also given at that clock.
+source has changed since).  The shader clock is measured by the library's clock probe on a
+second stream while the GEMMs run, and the matrix-core peak is also given at that clock.
 """
 
 import argparse
@@ -33,7 +33,6 @@ import math
 import os
 import re
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -177,63 +176,28 @@ class Timer:
         return means[len(means) // 2]          # ms
 
 
-def _clock_reader(torch):
-    """A function returning the current graphics clock in MHz (the median over the compute
-    dies where the SMI library reports them one by one), or None when there is no SMI."""
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
-
-        def read():
-            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-            per_die = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and v > 0]
-            if per_die:
-                return sorted(per_die)[len(per_die) // 2]
-            v = m.get("current_gfxclk")
-            return float(v) if isinstance(v, (int, float)) else None
-        read()
-        return read
-    except Exception as e:                      # noqa: BLE001 -- no SMI access on this host
-        log(f"SMI clock unavailable ({e}); trying torch.cuda.clock_rate")
-    try:
-        torch.cuda.clock_rate(0)
-        return lambda: float(torch.cuda.clock_rate(0))
-    except Exception as e:                      # noqa: BLE001
-        log(f"clock sampling unavailable: {e}")
-        return None
-
-
-def sample_clock(torch, run, seconds=0.25):
-    """Median GPU (graphics) clock in MHz while `run()` keeps the device busy; None when it
-    cannot be read."""
-    read = _clock_reader(torch)
-    if read is None:
-        return None
-    samples, stop = [], threading.Event()
-
-    def poll():
-        while not stop.is_set():
-            try:
-                v = read()
-                if v:
-                    samples.append(v)
-            except Exception:                   # noqa: BLE001
-                pass
-            time.sleep(0.002)
-
-    th = threading.Thread(target=poll, daemon=True)
-    run()
-    torch.cuda.synchronize()
-    th.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        run()
+def probe_clock(torch, kq, run=None, spin_us=300, samples=5):
+    """Median shader clock in MHz from the library's clock probe (one wavefront counting
+    shader cycles against the 100 MHz reference counter), launched on a stream of its own
+    while `run()` keeps the GPU busy on the current stream (or on an idle GPU)."""
+    side = torch.cuda.Stream()
+    vals = []
+    for _ in range(samples):
+        out = torch.empty((2,), dtype=torch.int64, device="cuda")
         torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    samples.sort()
-    return samples[len(samples) // 2] if samples else None
+        if run is not None:
+            for _ in range(4):          # about a millisecond of work first: the clock settles under load
+                run()
+        kq.clock_probe(spin_us, out=out, stream=side)
+        if run is not None:
+            for _ in range(4):
+                run()
+        torch.cuda.synchronize()
+        cyc, ticks = (int(v) for v in out.tolist())
+        if ticks > 0:
+            vals.append(100.0 * cyc / ticks)
+    vals.sort()
+    return round(vals[len(vals) // 2], 1) if vals else None
 
 
 def rotation_count(set_bytes):
@@ -404,7 +368,9 @@ def main():
     def gemm_round():
         for li in range(nl):
             gemm(li)
-    clock_mhz = sample_clock(torch, gemm_round)
+    clock_mhz = probe_clock(torch, kq, gemm_round)
+    clock_idle = probe_clock(torch, kq)
+    log(f"shader clock: {clock_mhz} MHz while the GEMMs run, {clock_idle} MHz idle")
 
     # ---- the other configurations, per launch
     others = {}
@@ -557,8 +523,10 @@ def main():
                                "traffic": (round(sum(traffic_tq.get(L["name"], 0.0) for L in layers))
                                            if traffic_tq else None),
                                "algorithmic_bytes": tot_tq_bytes},
-        "clock": {"gfx_mhz_during_gemm": clock_mhz, "peak_engine_mhz": PEAK_CLOCK_MHZ,
-                  "source": "SMI current graphics clock (median over the compute dies), median of samples taken every 2 ms while the step's GEMMs ran"},
+        "clock": {"shader_mhz_during_gemm": clock_mhz, "shader_mhz_idle": clock_idle,
+                  "peak_engine_mhz": PEAK_CLOCK_MHZ,
+                  "source": "kq_clock_probe (shader cycles over 300 us of the 100 MHz reference counter) on a "
+                            "second stream while the step's three GEMMs run back to back; median of 5"},
         "transform_quant_GBps": round(tq_gbs, 1),
         "w4a4_gemm_TFLOPs": round(gemm_tflops, 1),
         "linear_TFLOPs": round(tot_flops / ((tot_lr_ms + tot_gemm_ms) * 1e-3) / 1e12, 1),

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KQ_ABI_VERSION 6
+#define KQ_ABI_VERSION 7
 
 typedef int32_t kq_status;
 enum {
@@ -135,6 +135,14 @@ const char* kq_status_str(kq_status s);
  * unit Gaussian (OrbitQuant §03: one fixed codebook), as the library computes and
  * uses them; n = 4 or 16.  Host memory, n/2 doubles.  Runs on the host only. */
 kq_status kq_lloyd_max_levels(int32_t n, double* levels_out);
+
+/* Measurement helper, outside the activation path: the shader clock as the chip runs it
+ * (the matrix-core peak scales with it), e.g. while other work occupies the GPU on another
+ * stream.  One 64-thread workgroup on `stream` counts shader-clock cycles over spin_us
+ * microseconds of the constant 100 MHz reference counter and writes the cycle count and
+ * the reference ticks to out[0] and out[1] (device memory, caller-owned, 8-byte aligned);
+ * the clock in MHz is 100 out[0] / out[1].  1 <= spin_us <= 1000000. */
+kq_status kq_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t stream);
 
 /* Online activation path (KroQuant §01-§03; OrbitQuant §03; CentriQ abstract):
  *   [centre]  mu_t = fp16(mean_k X[t,k]) (float32 sum), x <- x - mu_t      if center

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 6
+    assert kq.abi_version() == 7
     for s in range(0, 8):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
@@ -231,6 +231,14 @@ def test_linear_workspace_size(lib):
     # at least what the split down-projection alone uses at any K
     for K in (128, 3072, 12288):
         assert kq.w4a4_linear_workspace_bytes(4608, 32) >= kq.lowrank_down_workspace_bytes(4608, K, 32) + 4608 * 32 * 2
+
+
+def test_clock_probe_validation(lib):
+    f = lib.kq_clock_probe
+    assert f(100, None, None) == 1
+    assert f(0, FAKE, None) == 4
+    assert f(1000001, FAKE, None) == 4
+    assert f(100, ctypes.c_void_p(0x100004), None) == 3
 
 
 def test_lowrank_validation(lib):

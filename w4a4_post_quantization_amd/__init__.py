@@ -67,6 +67,8 @@ def load():
     lib.kq_abi_version.argtypes = []
     lib.kq_status_str.restype = ctypes.c_char_p
     lib.kq_status_str.argtypes = [i32]
+    lib.kq_clock_probe.restype = i32
+    lib.kq_clock_probe.argtypes = [i32, vp, vp]
     lib.kq_lloyd_max_levels.restype = i32
     lib.kq_lloyd_max_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_double)]
     lib.kq_transform_quantize.restype = i32
@@ -105,6 +107,20 @@ def abi_version():
 
 def status_str(s):
     return load().kq_status_str(int(s)).decode()
+
+
+def clock_probe(spin_us, out=None, stream=None):
+    """Launch the shader-clock probe on `stream` (see kq_clock_probe): returns the device
+    uint64 [2] tensor that will hold (shader cycles, 100 MHz reference ticks)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((2,), dtype=torch.int64, device="cuda")      # no fill kernel to race with
+        _on_stream(stream, out)
+    _check(out, "out", torch.int64, (2,))
+    s = load().kq_clock_probe(int(spin_us), _ptr(out), _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_clock_probe")
+    return out
 
 
 def lloyd_max_levels(n):

@@ -148,6 +148,13 @@ kq_status kq_lloyd_max_levels(int32_t n, double* levels_out) {
   return lloyd_max_levels(n, levels_out) ? KQ_OK : KQ_ERR_UNSUPPORTED;
 }
 
+kq_status kq_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t stream) {
+  if (!out) return KQ_ERR_NULL;
+  if (spin_us < 1 || spin_us > 1000000) return KQ_ERR_UNSUPPORTED;
+  if (!aligned(out, 8)) return KQ_ERR_ALIGN;
+  return hip_status(launch_clock_probe(spin_us, out, stream));
+}
+
 kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center, const void* X, int64_t M,
                                 int64_t K, uint8_t* codes, void* scales, void* mu, hipStream_t stream) {
   if (!X || !codes || !scales) return KQ_ERR_NULL;

@@ -94,6 +94,10 @@ hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t
 
 int device_cu_count();
 // Workgroups of `kernel` that can be resident on one compute unit at once.
+// Shader-clock cycles and 100 MHz reference ticks over spin_us microseconds (out: device
+// uint64 [2]); one 64-thread workgroup.
+hipError_t launch_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t s);
+
 int resident_blocks_per_cu(const void* kernel, int threads, size_t lds);
 
 }  // namespace kq
