@@ -17,9 +17,9 @@ the pages (cited per function):
   (iselia-ai.com/papers/2607-02461): §03 (RPBH(X) = X.P.H.D, W' = R^-1 W,
   one Lloyd-Max codebook).
 * CentriQ: Calibration-Free Quantization of DiTs via Exact Mean Centering
-  (physicalainews.jp/papers/2610.06260): arXiv abstract (centre each token before
-  rotation, restore the mean through a rank-1 full-precision branch, closed-form
-  per-token scale).
+  (physicalainews.jp/papers/2610.06260): arXiv abstract (each token is centred
+  before the rotation and its mean added back afterwards by a rank-1 term kept in
+  high precision; a closed-form per-token scale).
 * SVDQuant explainer (aibr.jp/archives/95399): §3 (16-bit low-rank branch L1 L2
   beside the 4-bit residual product, fused in the engine).
 

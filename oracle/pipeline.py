@@ -7,8 +7,8 @@ OrbitQuant §03 / CentriQ's closed-form scale) -> packed codes.
 
 fold_weights: W' = P^-1 W offline (KroQuant §01, OrbitQuant §03), quantized along K
 with the same rules (MXFP4) or to 2-bit Lloyd-Max groups; plus the rank-1 restore
-vector wbar = 1^T W (CentriQ abstract: the mean is restored exactly through a rank-1
-full-precision branch, since (x - mu 1^T) W + mu (1^T W) = x W).
+vector wbar = 1^T W (CentriQ abstract: a rank-1 high-precision term gives back what
+the centring removed, since (x - mu 1^T) W + mu (1^T W) = x W).
 
 Transform descriptors are plain dicts:
   {"kind": "kron", "A": float32 [4, 4], "B": float32 [8, 8]}
