@@ -13,7 +13,8 @@ resident in HBM; the activation buffers rotate over enough copies (>= 1 GiB) tha
 reads them from the 256 MB last-level cache.
 
 Prints ONE JSON line.  The step time comes from two HIP events around the timed steps, on
-the stream the kernels run on, with nothing between the launches.  Per-launch durations:
+the stream the kernels run on, with nothing between the launches; before the warm-up steps
+each rotated input set goes through one step, so that none is first touched while timed.  Per-launch durations:
 10 untimed launches, then 50 timed ones in 5 groups of 10 back to back between two events,
 each group queued behind a short device-side sleep so that the GPU never waits for the
 host (a launch through the binding costs about 11 us of host time, more than some of the
@@ -24,6 +25,8 @@ PixArt-like, SANA-like) are timed the same way, per launch.  The "traffic" field
 from the HBM byte counters recorded in profiles/ for the same kernel source (null when the
 source has changed since).  The shader clock is measured by the library's clock probe on a
 second stream while the GEMMs run, and the matrix-core peak is also given at that clock.
+The vendor library's MXFP4 GEMM (hipBLASLt, through torch._scaled_mm) is timed beside this
+library's GEMM on the same packed operands, as a comparison outside the step.
 """
 
 import argparse
@@ -253,16 +256,53 @@ def kron_config(torch, kq, synth, timer, cfg_idx, dev):
     return {"workload": cfg["name"], "M": M, "rotated_input_sets": R, "layers": out}
 
 
+def vendor_gemm(torch, kq, timer, layers, Xsets, R, center, M):
+    """Per layer: the vendor MXFP4 GEMM (torch._scaled_mm over hipBLASLt, bf16 output) and this
+    library's GEMM without the low-rank and rank-1 terms, on the same packed activations and
+    weights, with their relative Frobenius difference.  None where torch has no such path."""
+    rows = []
+    for L in layers:
+        K, N = L["K"], L["N"]
+        sets = [kq.transform_quantize(Xsets[s][K], L["xf"], center=center)[:2] for s in range(R)]
+        Yv = torch.empty((M, N), dtype=torch.float16, device=Xsets[0][K].device)
+        a = [c.view(torch.float4_e2m1fn_x2) for c, _ in sets]
+        sa = [sc.view(torch.float8_e8m0fnu) for _, sc in sets]
+        b = L["wc"].view(torch.float4_e2m1fn_x2).t()
+        sb = L["ws"].view(torch.float8_e8m0fnu)
+        try:
+            ref = torch._scaled_mm(a[0], b, sa[0], sb, out_dtype=torch.bfloat16)
+        except (RuntimeError, TypeError, ValueError) as e:
+            log(f"vendor MXFP4 GEMM unavailable: {str(e)[:200]}")
+            return None
+        kq.w4a4_linear_t(sets[0][0], sets[0][1], L["wc"], L["ws"], Y=Yv)
+        torch.cuda.synchronize()
+        rel = float(torch.linalg.norm(ref.float() - Yv.float()) / torch.linalg.norm(Yv.float()))
+        t_v = timer(lambda i: torch._scaled_mm(a[i % R], b, sa[i % R], sb, out_dtype=torch.bfloat16))
+        t_o = timer(lambda i: kq.w4a4_linear_t(sets[i % R][0], sets[i % R][1], L["wc"], L["ws"], Y=Yv))
+        fl = 2 * M * N * K
+        rows.append({"layer": L["name"], "M": M, "K": K, "N": N,
+                     "vendor_us": round(t_v * 1e3, 2), "vendor_TFLOPs": round(fl / t_v / 1e9, 1),
+                     "library_us": round(t_o * 1e3, 2), "library_TFLOPs": round(fl / t_o / 1e9, 1),
+                     "speedup": round(t_v / t_o, 3), "rel_fro_diff_bf16_vs_fp16": round(rel, 5)})
+        log(f"vendor MXFP4 GEMM {L['name']}: {t_v*1e3:7.2f} us vs library {t_o*1e3:7.2f} us "
+            f"(x{t_v/t_o:.2f}); rel diff {rel:.2e}")
+        del sets, a, sa, ref
+    return {"api": "torch._scaled_mm (hipBLASLt), MXFP4 x MXFP4 with E8M0 block scales, bf16 output",
+            "layers": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=0, help="activation buffer sets (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens per linear in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the other configurations and the transform variants")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-library MXFP4 GEMM timed beside the library's")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -326,6 +366,10 @@ def main():
             act_pass(li, s)
             gemm(li)
 
+    # every rotated input set goes through the step once before the warm-up steps, so that
+    # none is first touched (address translation, caches) inside the timed region
+    for s in range(R):
+        step(s)
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -371,6 +415,13 @@ def main():
     clock_mhz = probe_clock(torch, kq, gemm_round)
     clock_idle = probe_clock(torch, kq)
     log(f"shader clock: {clock_mhz} MHz while the GEMMs run, {clock_idle} MHz idle")
+
+    # ---- the vendor library's MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on the step's
+    # packed operands, beside this library's GEMM with no epilogue terms (the same product):
+    # a comparison only, nothing of the step goes through it
+    vendor = None
+    if not args.no_vendor:
+        vendor = vendor_gemm(torch, kq, timer, layers, Xsets, R, center, M)
 
     # ---- the other configurations, per launch
     others = {}
@@ -537,6 +588,7 @@ def main():
                    "(relative only, other chip)",
         "transform_variants": variants,
         "sana_like_lloyd_max": sana,
+        "vendor_mxfp4_gemm": vendor,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -173,13 +173,29 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
 }
 
 // T[m][c] = fp16(sum over slices s, in order, of part[s][m][c]); four columns per thread.
+// The slices' loads go out eight at a time (range-checked: those past the last slice read
+// zeros, which leave the sum unchanged), so a thread waits one memory latency per eight
+// slices instead of one per slice.
+constexpr int LR_RED_THREADS = 64;
+constexpr int LR_RED_BATCH = 8;
+
 template <int RR>
-__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ part, int M, int slices,
-                                                             __half* __restrict__ T) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // first of four elements
-  if (e >= (int64_t)M * RR) return;
-  v4f v = *reinterpret_cast<const v4f*>(part + e);
-  for (int s = 1; s < slices; ++s) v += *reinterpret_cast<const v4f*>(part + (int64_t)s * M * RR + e);
+__global__ __launch_bounds__(LR_RED_THREADS) void lowrank_reduce_kernel(const float* __restrict__ part, int M,
+                                                                        int slices, __half* __restrict__ T) {
+  const int e = (blockIdx.x * LR_RED_THREADS + threadIdx.x) * 4;   // first of four elements
+  if (e >= M * RR) return;
+  const int plane = M * RR * 4;                                     // bytes per slice
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (int64_t)slices * plane);
+  v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < slices; s0 += LR_RED_BATCH) {
+    v4f t[LR_RED_BATCH];
+#pragma unroll
+    for (int j = 0; j < LR_RED_BATCH; ++j)
+      t[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + j) * plane + 4 * e, 0, 0));
+    v = s0 == 0 ? t[0] : v + t[0];
+#pragma unroll
+    for (int j = 1; j < LR_RED_BATCH; ++j) v += t[j];
+  }
   const __half2 h0 = __floats2half2_rn(v[0], v[1]), h1 = __floats2half2_rn(v[2], v[3]);
   typedef uint32_t v2u __attribute__((ext_vector_type(2)));
   *reinterpret_cast<v2u*>(T + e) = v2u{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
@@ -224,9 +240,12 @@ static hipError_t lowrank_launch(const __half* X, const __half* L1, int64_t M, i
   hipLaunchKernelGGL((lowrank_down_kernel<RR, NS, XK>), dim3((unsigned)(blocks * slices)), dim3(256), 0, s, X, L1,
                      (int)M, (int)K, slices, cps, part, T, fk, P, codes, scales);
   if (slices > 1) {
+    // the reduction addresses the partial sums with 32-bit offsets (the split only runs
+    // while the row blocks are fewer than four per compute unit, so they are small)
+    if ((int64_t)(slices + LR_RED_BATCH) * M * RR * 4 > INT32_MAX) return hipErrorInvalidValue;
     const int64_t threads = M * RR / 4;
-    hipLaunchKernelGGL((lowrank_reduce_kernel<RR>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       part, (int)M, slices, T);
+    hipLaunchKernelGGL((lowrank_reduce_kernel<RR>), dim3((unsigned)((threads + LR_RED_THREADS - 1) / LR_RED_THREADS)),
+                       dim3(LR_RED_THREADS), 0, s, part, (int)M, slices, T);
   }
   return hipGetLastError();
 }

@@ -2,35 +2,86 @@
 // codebook for all rotated coordinates; §04: 2-bit weights, 4-bit activations; CentriQ
 // abstract: closed-form per-token scale):
 //   Y[m][n] = s_t[m] * sum_g s_g[n][g] * sum_{k in g} l16[qx[m][k]] * l4[qw[n][k]].
-// The codes are table-dequantized to fp16 in LDS once per workgroup tile (activation
-// levels without their per-token scale, weight levels times their fp16 group scale) and
-// multiplied on the fp16 matrix cores (fp32 accumulation); the per-token scale multiplies
-// the accumulator before the fp16 store.  Two forms: 128 x 128 tiles of 16 x 16 x 32
-// products, and 256 x 256 tiles of 32 x 32 x 16 products for grids of at least 1.5 rounds.
+// The codes are dequantized to fp16 in registers (byte-permute table lookups: activation
+// levels without their per-token scale, weight levels times their fp16 group scale), staged
+// in LDS once per workgroup tile and multiplied on the fp16 matrix cores (fp32
+// accumulation); the per-token scale multiplies the accumulator before the fp16 store.  Two
+// forms: 128 x 128 tiles of 16 x 16 x 32 products, and 256 x 256 tiles of 32 x 32 x 16
+// products for grids of at least 1.5 rounds.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
 namespace kq {
 
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ int chunk_swz2(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// Dequantization tables in LDS, entry b for a byte of codes: lut16[b] = the fp16 levels of
-// its two 4-bit codes (low nibble first; bit 3 the sign), lut4[b] = those of its four 2-bit
-// codes (low pair first; bit 1 the sign).  Threads tid, tid + nt, ... fill the entries.
-__device__ __forceinline__ void build_lm_luts(const LmTables& lm, uint32_t* lut16, uint2* lut4, int tid, int nt) {
-  for (int b = tid; b < 256; b += nt) {
-    const int c0 = b & 15, c1 = b >> 4;
-    const float v0 = (c0 & 8) ? -lm.l16[c0 & 7] : lm.l16[c0 & 7];
-    const float v1 = (c1 & 8) ? -lm.l16[c1 & 7] : lm.l16[c1 & 7];
-    lut16[b] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v0, v1));
-    float w[4];
+// Dequantization in registers, by byte permutes (v_perm_b32 picks each result byte out of
+// eight source bytes, so two registers form an eight-entry byte table):
+//   - activation codes (4 bits, bit 3 the sign): the low and the high bytes of the eight
+//     fp16 magnitude levels are two such tables; the sign goes into bit 15;
+//   - weight codes (2 bits, bit 1 the sign): the four fp16 values of the group (both
+//     magnitudes times the group scale, and their negations) are one table of 2-byte
+//     entries, and a code selects bytes 2c and 2c + 1.
+// The values are the same fp16 numbers a table of fp16(+-level) (times the scale, one
+// fp16 product) would hold: negation only flips the sign bit.
+struct LmRegTables {
+  uint32_t lo0, lo1, hi0, hi1;   // bytes of fp16(l16[m]): low bytes m = 0..3, 4..7, then high bytes
+  uint32_t l4;                   // fp16(l4[0]) | fp16(l4[1]) << 16
+};
+
+__device__ __forceinline__ LmRegTables lm_reg_tables(const LmTables& lm) {
+  LmRegTables t{0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = (b >> (2 * e)) & 3;
-      w[e] = (c & 2) ? -lm.l4[c & 1] : lm.l4[c & 1];
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t hv = __half_as_ushort(__float2half_rn(lm.l16[m]));
+    const int sh = 8 * (m & 3);
+    if (m < 4) {
+      t.lo0 |= (hv & 0xFFu) << sh;
+      t.hi0 |= (hv >> 8) << sh;
+    } else {
+      t.lo1 |= (hv & 0xFFu) << sh;
+      t.hi1 |= (hv >> 8) << sh;
     }
-    lut4[b] = make_uint2(__builtin_bit_cast(uint32_t, __floats2half2_rn(w[0], w[1])),
-                         __builtin_bit_cast(uint32_t, __floats2half2_rn(w[2], w[3])));
+  }
+  t.l4 = __builtin_bit_cast(uint32_t, __floats2half2_rn(lm.l4[0], lm.l4[1]));
+  return t;
+}
+
+// Eight 4-bit activation codes (code i in bits 4i .. 4i + 3) -> eight fp16 levels, in
+// order, packed two per dword.
+__device__ __forceinline__ void dequant_a4(uint32_t x, const LmRegTables& t, uint32_t out[4]) {
+  const uint32_t me = x & 0x07070707u, mo = (x >> 4) & 0x07070707u;   // magnitudes: even, odd codes
+  const uint32_t le = __builtin_amdgcn_perm(t.lo1, t.lo0, me);
+  const uint32_t he = __builtin_amdgcn_perm(t.hi1, t.hi0, me) | ((x & 0x08080808u) << 4);
+  const uint32_t lo = __builtin_amdgcn_perm(t.lo1, t.lo0, mo);
+  const uint32_t ho = __builtin_amdgcn_perm(t.hi1, t.hi0, mo) | (x & 0x80808080u);
+  const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u);    // codes 0, 2
+  const uint32_t e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);    // codes 4, 6
+  const uint32_t o01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);    // codes 1, 3
+  const uint32_t o23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);    // codes 5, 7
+  out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+}
+
+// The group's table for weight codes: (+m0, +m1) and (-m0, -m1), m = fp16(l4) * fp16 scale.
+__device__ __forceinline__ void w2_group_table(const LmRegTables& t, __half sg, uint32_t& t0, uint32_t& t1) {
+  t0 = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, t.l4), __half2half2(sg)));
+  t1 = t0 ^ 0x80008000u;
+}
+
+// Eight 2-bit weight codes (code i in bits 2i, 2i + 1 of x, x < 2^16) -> eight fp16 values.
+// Pair d's codes go to the two 16-bit halves of (z >> 4d) & 0x30003, z = x | x << 14, and
+// each half c becomes the byte selectors 2c, 2c + 1.
+__device__ __forceinline__ void dequant_w2(uint32_t x, uint32_t t0, uint32_t t1, uint32_t out[4]) {
+  const uint32_t z = x | (x << 14);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t a = (z >> (4 * d)) & 0x00030003u;
+    out[d] = __builtin_amdgcn_perm(t1, t0, a * 0x0202u + 0x01000100u);
   }
 }
 
@@ -44,14 +95,11 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
   static_assert(BN + BM == NT, "one staging row per thread");
   constexpr int A_OFF = 0, B_OFF = BN * 64, BUF = (BN + BM) * 64;
   __shared__ __align__(16) uint8_t lds[2 * BUF];
-  __shared__ uint32_t lut16[256];   // byte of two 4-bit codes -> two fp16 levels
-  __shared__ uint2 lut4[256];       // byte of four 2-bit codes -> four fp16 levels
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid % WN, wm = wid / WN;
   const int lr = lane & 15, q = lane >> 4;
-
-  build_lm_luts(lm, lut16, lut4, tid, NT);
+  const LmRegTables lt = lm_reg_tables(lm);
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile_n = blockIdx.x % tiles_n, tile_m = blockIdx.x / tiles_n;
@@ -88,18 +136,15 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
     uint8_t* base = lds + buf * BUF + lrow;
     uint32_t h[16];
     if (is_w) {
-      const __half2 s2 = __half2half2(sg);
+      uint32_t t0, t1;
+      w2_group_table(lt, sg, t0, t1);
       const uint32_t wv[2] = {raw.x, raw.y};
 #pragma unroll
-      for (int bI = 0; bI < 8; ++bI) {
-        const uint2 p = lut4[(wv[bI >> 2] >> (8 * (bI & 3))) & 0xFF];
-        h[2 * bI] = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, p.x), s2));
-        h[2 * bI + 1] = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, p.y), s2));
-      }
+      for (int c = 0; c < 4; ++c) dequant_w2((wv[c >> 1] >> (16 * (c & 1))) & 0xFFFFu, t0, t1, h + 4 * c);
     } else {
       const uint32_t xv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int bI = 0; bI < 16; ++bI) h[bI] = lut16[(xv[bI >> 2] >> (8 * (bI & 3))) & 0xFF];
+      for (int c = 0; c < 4; ++c) dequant_a4(xv[c], lt, h + 4 * c);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -107,7 +152,6 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
   };
 
   const int wrow_a = wn * (BN / WN), wrow_b = wm * (BM / WM);
-  __syncthreads();  // tables ready
   gload(0);
   lstore(0);
   __syncthreads();
@@ -156,14 +200,21 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
 // (v_mfma_f32_32x32x16_f16: lane l holds row l % 32 and k = 8 (l / 32) .. + 7 of each
 // 16-wide step; result register 4 g + e of lane l is C[8 g + 4 (l / 32) + e][l % 32]).
 // Against 64 x 64 wave tiles of 16 x 16 products this reads half the LDS bytes per
-// product.  A k-step is two groups (64 k): a barrier then separates 64 products per
-// wavefront, and the global loads of the next step, issued before them, have that long
-// to land.  Thread t stages weight row t and token row t; LDS rows are 128 bytes, their
-// 16-byte chunks XOR-swizzled by the row's low bits.
-// What bounds it is LDS: per step the compute unit reads 128 KiB of fragments, makes
-// 12 K table lookups at random addresses and stores 64 KiB, about as long as the step's
-// matrix-core work.
-// A last step with one group left (K % 64 = 32) leaves the other group's values zero.
+// product.  A k-step is two groups (64 k) held as fp16 in one of two LDS buffers: thread t
+// dequantizes weight row t and token row t into the buffer the next step reads, LDS rows of
+// 128 bytes with their 16-byte chunks XOR-swizzled by the row's low bits.
+// Schedule of a step, pinned with scheduling barriers so that the matrix cores never wait
+// for a whole phase:
+//   - the fragments of the step's first 16-wide slice are read;
+//   - the 64 products run as four slices of 16; after each of the first eight products of
+//     a slice one fragment of the next slice is read, and after every fourth product one of
+//     the sixteen 8-code chunks of the next step is dequantized and stored to the other
+//     buffer;
+//   - one barrier: the next step's buffer is complete, this one is free.
+// The codes a step dequantizes were loaded one step earlier (the loads of step ks + 2 go
+// out at the start of step ks), so the dequantization never waits for memory.  Loads past
+// the last step or of a missing second group (K % 64 = 32) are outside the buffer ranges
+// and read zeros: the group's scale is then zero and so are its products.
 __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
     const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales, int N, LmTables lm,
@@ -171,14 +222,11 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   constexpr int BN = 256, BM = 256, TN = 4, TM = 4, RB = 128;   // RB: LDS bytes per row and step
   constexpr int A_OFF = 0, B_OFF = BN * RB, BUF = (BN + BM) * RB;
   __shared__ __align__(16) uint8_t lds[2 * BUF];
-  __shared__ uint32_t lut16[256];   // byte of two 4-bit codes -> two fp16 levels
-  __shared__ uint2 lut4[256];       // byte of four 2-bit codes -> four fp16 levels
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int l32 = lane & 31, h = lane >> 5;
-
-  build_lm_luts(lm, lut16, lut4, tid, 256);
+  const LmRegTables lt = lm_reg_tables(lm);
 
   // tiles walked column by column in groups of 8 along M, die-contiguous (as the W4A4 form)
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -197,13 +245,49 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   const int n0 = tile_n * BN, m0 = tile_m * BM;
   const int ng = K >> 5, nks = (ng + 1) >> 1;             // groups, 64-wide steps
 
-  // staging rows of this thread: weight row tid, token row tid; rows past the matrix repeat
-  // its last row (their results are never stored)
-  const int64_t wrow = min(n0 + tid, N - 1), xrow = min(m0 + tid, M - 1);
-  const uint8_t* const gw = wcodes + wrow * (K >> 2);
-  const __half* const gs = wscales + wrow * (K >> 5);
-  const uint8_t* const gx = xcodes + xrow * (K >> 1);
+  // staging rows of this thread, relative to the tile: weight row tid, token row tid; rows
+  // past the matrix repeat its last row (their results are never stored)
+  const int wr = min(n0 + tid, N - 1) - n0, xr = min(m0 + tid, M - 1) - m0;
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(wcodes + (int64_t)n0 * (K >> 2), (int64_t)(N - n0) * (K >> 2));
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(wscales + (int64_t)n0 * ng, (int64_t)(N - n0) * ng * 2);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(xcodes + (int64_t)m0 * (K >> 1), (int64_t)(M - m0) * (K >> 1));
+  const int ow = wr * (K >> 2), os = wr * ng * 2, ox = xr * (K >> 1);
   const int sw = tid & 7;
+
+  // the codes of one step: the two groups' weight codes (8 bytes each) and fp16 scales, and
+  // their activation codes (16 bytes each)
+  struct Raw {
+    v2u w[2];
+    uint32_t s[2];
+    v4u x[2];
+  };
+  auto gload = [&](int ks, Raw& r) {
+    const bool v0 = ks < nks, v1 = 2 * ks + 1 < ng;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool v = q == 0 ? v0 : v1;
+      r.w[q] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rW, v ? ow + 16 * ks + 8 * q : KQ_OOB, 0, 0));
+      r.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rS, v ? os + 4 * ks + 2 * q : KQ_OOB, 0, 0);
+      r.x[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rX, v ? ox + 32 * ks + 16 * q : KQ_OOB, 0, 0));
+    }
+  };
+  // chunk j (0..15) of a step into buffer buf: j < 8 the weight row's chunk j (group j / 4),
+  // else the token row's chunk j - 8; each is 8 codes -> 16 bytes of fp16
+  uint32_t tw[2][2];                                      // the two groups' weight tables
+  auto dq_chunk = [&](const Raw& r, int buf, int j) {
+    uint8_t* const base = lds + buf * BUF;
+    uint32_t o[4];
+    if (j < 8) {
+      const int q = j >> 2, c = j & 3;
+      if (c == 0) w2_group_table(lt, __ushort_as_half((unsigned short)r.s[q]), tw[q][0], tw[q][1]);
+      dequant_w2((r.w[q][c >> 1] >> (16 * (c & 1))) & 0xFFFFu, tw[q][0], tw[q][1], o);
+      *reinterpret_cast<v4u*>(base + A_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) = v4u{o[0], o[1], o[2], o[3]};
+    } else {
+      const int q = (j - 8) >> 2, c = (j - 8) & 3;
+      dequant_a4(r.x[q][c], lt, o);
+      *reinterpret_cast<v4u*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) = v4u{o[0], o[1], o[2], o[3]};
+    }
+  };
 
   v16f acc[TN][TM];
 #pragma unroll
@@ -213,85 +297,67 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  uint2 rw[2];      // codes of the step's two groups (8 bytes each)
-  __half sg[2];
-  uint4 rx[2];      // ... 16 bytes each
-  auto gload = [&](int ks) {
-    const bool two = 2 * ks + 1 < ng;                      // the step's second group exists
-    rw[0] = *reinterpret_cast<const uint2*>(gw + 16 * ks);
-    sg[0] = gs[2 * ks];
-    rw[1] = two ? *reinterpret_cast<const uint2*>(gw + 16 * ks + 8) : make_uint2(0u, 0u);
-    sg[1] = two ? gs[2 * ks + 1] : __float2half(0.0f);     // a zero scale zeroes the group
-    rx[0] = *reinterpret_cast<const uint4*>(gx + 32 * ks);
-    rx[1] = two ? *reinterpret_cast<const uint4*>(gx + 32 * ks + 16) : make_uint4(0u, 0u, 0u, 0u);
+  const int wrow_a = wn * 128, wrow_b = wm * 128;
+  // fragment i of a wave reads row wrow + 32 i + l32, whose swizzle (row & 7) is the lane's
+  const int fa_off = A_OFF + (wrow_a + l32) * RB, fb_off = B_OFF + (wrow_b + l32) * RB, swl = l32 & 7;
+  auto rd_a = [&](int buf, int sub, int i) {
+    return *reinterpret_cast<const v8h*>(lds + buf * BUF + fa_off + 32 * RB * i + 16 * ((2 * sub + h) ^ swl));
   };
-  auto lstore = [&](int buf, bool two) {
-    uint8_t* const base = lds + buf * BUF;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {                          // group q: chunks 4 q .. 4 q + 3
-      const __half2 s2 = __half2half2(sg[q]);
-      const uint32_t wv[2] = {rw[q].x, rw[q].y};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t hw[4];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int bI = 2 * c + u;
-          const uint2 pr = lut4[(wv[bI >> 2] >> (8 * (bI & 3))) & 0xFF];
-          hw[2 * u] = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, pr.x), s2));
-          hw[2 * u + 1] = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, pr.y), s2));
-        }
-        *reinterpret_cast<uint4*>(base + A_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) =
-            make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t xv[4] = {rx[q].x, rx[q].y, rx[q].z, rx[q].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t hx[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int bI = 4 * c + u;
-          hx[u] = (q == 0 || two) ? lut16[(xv[bI >> 2] >> (8 * (bI & 3))) & 0xFF] : 0u;
-        }
-        *reinterpret_cast<uint4*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) =
-            make_uint4(hx[0], hx[1], hx[2], hx[3]);
-      }
-    }
+  auto rd_b = [&](int buf, int sub, int j) {
+    return *reinterpret_cast<const v8h*>(lds + buf * BUF + fb_off + 32 * RB * j + 16 * ((2 * sub + h) ^ swl));
   };
 
-  const int wrow_a = wn * 128, wrow_b = wm * 128;
-  gload(0);
-  __syncthreads();  // tables ready
-  lstore(0, 1 < ng);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    if (ks + 1 < nks) gload(ks + 1);
-    const uint8_t* const base = lds + (ks & 1) * BUF;
+  // step ks: products from buffer ks & 1, the codes of ks + 1 (in `cur`, loaded during step
+  // ks - 1) dequantized into the other buffer, the loads of ks + 2 into `ld`.  The loop runs
+  // two steps per iteration, so that the two register sets alternate without copies (a copy
+  // would wait for the loads still in flight).  The buffer index is hidden from the compiler:
+  // knowing it, it would keep both buffers' LDS addresses in registers and spill.
+  auto step = [&](int ks, const Raw& cur, Raw& ld) {
+    int buf = ks & 1;
+    asm volatile("" : "+s"(buf));
+    gload(ks + 2, ld);
+    v8h fa[2][TN], fb[2][TM];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {       // four 16-wide steps: chunks 2 sub + (l / 32)
-      const int ch = 2 * sub + h;
-      v8h fa[TN], fb[TM];
+    for (int i = 0; i < TN; ++i) fa[0][i] = rd_a(buf, 0, i);
 #pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const int row = wrow_a + 32 * i + l32;
-        fa[i] = *reinterpret_cast<const v8h*>(base + A_OFF + row * RB + 16 * (ch ^ (row & 7)));
+    for (int j = 0; j < TM; ++j) fb[0][j] = rd_b(buf, 0, j);
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const int c = sub & 1, n = c ^ 1;
+#pragma unroll
+      for (int m = 0; m < TN * TM; ++m) {
+        const int i = m / TM, j = m % TM;
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (sub < 3 && m < TN + TM) {
+          if (m < TN) fa[n][m] = rd_a(buf, sub + 1, m);
+          else fb[n][m - TN] = rd_b(buf, sub + 1, m - TN);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if ((m & 3) == 3) {
+          dq_chunk(cur, buf ^ 1, 4 * sub + (m >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int row = wrow_b + 32 * j + l32;
-        fb[j] = *reinterpret_cast<const v8h*>(base + B_OFF + row * RB + 16 * (ch ^ (row & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < nks) lstore((ks + 1) & 1, 2 * (ks + 1) + 1 < ng);
-    __syncthreads();
+    lds_barrier();                                        // the next buffer is complete, this one free
+  };
+
+  Raw ra, rb;
+  gload(0, ra);
+  gload(1, rb);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dq_chunk(ra, 0, j);
+  lds_barrier();
+  // pairs of steps, then the last step when their number is odd (a conditional second step
+  // inside the loop makes the register allocator copy the accumulators, and spill)
+  int ks = 0;
+  for (; ks + 1 < nks; ks += 2) {
+    step(ks, rb, ra);
+    step(ks + 1, ra, rb);
   }
+  if (ks < nks) step(ks, rb, ra);
 
   // acc[i][j][4 g + e] = (unscaled) Y[m][n] for m = m0 + wrow_b + 32 j + l % 32,
   // n = n0 + wrow_a + 32 i + 8 g + 4 (l / 32) + e: one 8-byte store per (i, j, g)
