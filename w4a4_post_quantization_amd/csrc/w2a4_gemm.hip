@@ -212,7 +212,8 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
 //     buffer;
 //   - one barrier: the next step's buffer is complete, this one is free.
 // The codes a step dequantizes were loaded one step earlier (the loads of step ks + 2 go
-// out at the start of step ks), so the dequantization never waits for memory.  Loads past
+// out during step ks, one at a time between products), so the dequantization never waits
+// for memory.  Loads past
 // the last step or of a missing second group (K % 64 = 32) are outside the buffer ranges
 // and read zeros: the group's scale is then zero and so are its products.
 __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
@@ -261,15 +262,23 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     uint32_t s[2];
     v4u x[2];
   };
-  auto gload = [&](int ks, Raw& r) {
-    const bool v0 = ks < nks, v1 = 2 * ks + 1 < ng;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const bool v = q == 0 ? v0 : v1;
+  // load u (0..5) of step ks: u / 3 is the group, u % 3 picks weight codes, scale or
+  // activation codes.  Each load touches one cache line per lane (a row per thread), so the
+  // six go out one at a time between products: issued together they would hold the wave,
+  // and its matrix core, for their whole address-unit time.
+  auto gload1 = [&](int ks, Raw& r, int u) {
+    const int q = u / 3;
+    const bool v = q == 0 ? ks < nks : 2 * ks + 1 < ng;
+    if (u % 3 == 0)
       r.w[q] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rW, v ? ow + 16 * ks + 8 * q : KQ_OOB, 0, 0));
+    else if (u % 3 == 1)
       r.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rS, v ? os + 4 * ks + 2 * q : KQ_OOB, 0, 0);
+    else
       r.x[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rX, v ? ox + 32 * ks + 16 * q : KQ_OOB, 0, 0));
-    }
+  };
+  auto gload = [&](int ks, Raw& r) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u) gload1(ks, r, u);
   };
   // chunk j (0..15) of a step into buffer buf: j < 8 the weight row's chunk j (group j / 4),
   // else the token row's chunk j - 8; each is 8 codes -> 16 bytes of fp16
@@ -315,7 +324,6 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   auto step = [&](int ks, const Raw& cur, Raw& ld) {
     int buf = ks & 1;
     asm volatile("" : "+s"(buf));
-    gload(ks + 2, ld);
     v8h fa[2][TN], fb[2][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i) fa[0][i] = rd_a(buf, 0, i);
@@ -337,6 +345,10 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
         }
         if ((m & 3) == 3) {
           dq_chunk(cur, buf ^ 1, 4 * sub + (m >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (sub < 3 && (m == 1 || m == 9)) {
+          gload1(ks + 2, ld, 2 * sub + (m >> 3));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
