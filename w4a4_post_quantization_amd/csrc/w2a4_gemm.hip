@@ -21,9 +21,9 @@ __device__ __forceinline__ int chunk_swz2(int row) { return ((row >> 1) ^ (row >
 // eight source bytes, so two registers form an eight-entry byte table):
 //   - activation codes (4 bits, bit 3 the sign): the low and the high bytes of the eight
 //     fp16 magnitude levels are two such tables; the sign goes into bit 15;
-//   - weight codes (2 bits, bit 1 the sign): the four fp16 values of the group (both
-//     magnitudes times the group scale, and their negations) are one table of 2-byte
-//     entries, and a code selects bytes 2c and 2c + 1.
+//   - weight codes (2 bits, bit 1 the sign): the low and the high bytes of the group's four
+//     fp16 values (both magnitudes times the group scale, and their negations) are two
+//     four-entry tables indexed by the code.
 // The values are the same fp16 numbers a table of fp16(+-level) (times the scale, one
 // fp16 product) would hold: negation only flips the sign bit.
 struct LmRegTables {
@@ -49,40 +49,45 @@ __device__ __forceinline__ LmRegTables lm_reg_tables(const LmTables& lm) {
   return t;
 }
 
-// Eight 4-bit activation codes (code i in bits 4i .. 4i + 3) -> eight fp16 levels, in
-// order, packed two per dword.
+// Both operands' eight values of an 8-code chunk are produced in the order
+// (0, 4, 1, 5, 2, 6, 3, 7) of their k positions, the order in which the permutes deliver
+// them most cheaply; the A and B chunks share it, so every product pairs the same k.
+
+// Eight 4-bit activation codes (code i in bits 4i .. 4i + 3) -> eight fp16 levels, two per
+// dword: (0, 4), (1, 5), (2, 6), (3, 7).
 __device__ __forceinline__ void dequant_a4(uint32_t x, const LmRegTables& t, uint32_t out[4]) {
-  const uint32_t me = x & 0x07070707u, mo = (x >> 4) & 0x07070707u;   // magnitudes: even, odd codes
+  const uint32_t me = x & 0x07070707u, mo = (x >> 4) & 0x07070707u;   // magnitudes: codes 0,2,4,6 / 1,3,5,7
   const uint32_t le = __builtin_amdgcn_perm(t.lo1, t.lo0, me);
   const uint32_t he = __builtin_amdgcn_perm(t.hi1, t.hi0, me) | ((x & 0x08080808u) << 4);
   const uint32_t lo = __builtin_amdgcn_perm(t.lo1, t.lo0, mo);
   const uint32_t ho = __builtin_amdgcn_perm(t.hi1, t.hi0, mo) | (x & 0x80808080u);
-  const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u);    // codes 0, 2
-  const uint32_t e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);    // codes 4, 6
-  const uint32_t o01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);    // codes 1, 3
-  const uint32_t o23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);    // codes 5, 7
-  out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  out[0] = __builtin_amdgcn_perm(he, le, 0x06020400u);   // codes 0, 4
+  out[1] = __builtin_amdgcn_perm(ho, lo, 0x06020400u);   // codes 1, 5
+  out[2] = __builtin_amdgcn_perm(he, le, 0x07030501u);   // codes 2, 6
+  out[3] = __builtin_amdgcn_perm(ho, lo, 0x07030501u);   // codes 3, 7
 }
 
-// The group's table for weight codes: (+m0, +m1) and (-m0, -m1), m = fp16(l4) * fp16 scale.
-__device__ __forceinline__ void w2_group_table(const LmRegTables& t, __half sg, uint32_t& t0, uint32_t& t1) {
-  t0 = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, t.l4), __half2half2(sg)));
-  t1 = t0 ^ 0x80008000u;
+// The group's tables for weight codes: the low and the high bytes of (+m0, +m1, -m0, -m1),
+// m = fp16(l4) * fp16 scale (one fp16 product each).
+__device__ __forceinline__ void w2_group_table(const LmRegTables& t, __half sg, uint32_t& tlo, uint32_t& thi) {
+  const uint32_t m = __builtin_bit_cast(uint32_t, __hmul2(__builtin_bit_cast(__half2, t.l4), __half2half2(sg)));
+  tlo = __builtin_amdgcn_perm(m, m, 0x02000200u);
+  thi = __builtin_amdgcn_perm(m, m, 0x03010301u) ^ 0x80800000u;
 }
 
-// Eight 2-bit weight codes (code i in bits 2i, 2i + 1 of x, x < 2^16) -> eight fp16 values.
-// Pair d's codes go to the two 16-bit halves of (z >> 4d) & 0x30003, z = x | x << 14, and
-// each half c becomes the byte selectors 2c, 2c + 1.
-__device__ __forceinline__ void dequant_w2(uint32_t x, uint32_t t0, uint32_t t1, uint32_t out[4]) {
+// Eight 2-bit weight codes (code i in bits 2i, 2i + 1 of x, x < 2^16) -> eight fp16 values in
+// the same order.  With z = x | x << 14, the bytes of z & 0x03030303 are codes 0, 4, 1, 5 and
+// those of (z >> 4) & 0x03030303 codes 2, 6, 3, 7: each byte selects its value's low and
+// high byte from the group's tables.
+__device__ __forceinline__ void dequant_w2(uint32_t x, uint32_t tlo, uint32_t thi, uint32_t out[4]) {
   const uint32_t z = x | (x << 14);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t a = (z >> (4 * d)) & 0x00030003u;
-    out[d] = __builtin_amdgcn_perm(t1, t0, a * 0x0202u + 0x01000100u);
-  }
+  const uint32_t s1 = z & 0x03030303u, s2 = (z >> 4) & 0x03030303u;
+  const uint32_t l1 = __builtin_amdgcn_perm(0u, tlo, s1), h1 = __builtin_amdgcn_perm(0u, thi, s1);
+  const uint32_t l2 = __builtin_amdgcn_perm(0u, tlo, s2), h2 = __builtin_amdgcn_perm(0u, thi, s2);
+  out[0] = __builtin_amdgcn_perm(h1, l1, 0x05010400u);   // codes 0, 4
+  out[1] = __builtin_amdgcn_perm(h1, l1, 0x07030602u);   // codes 1, 5
+  out[2] = __builtin_amdgcn_perm(h2, l2, 0x05010400u);   // codes 2, 6
+  out[3] = __builtin_amdgcn_perm(h2, l2, 0x07030602u);   // codes 3, 7
 }
 
 template <int BN, int BM, int WN, int WM>
