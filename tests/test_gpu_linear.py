@@ -364,9 +364,10 @@ def test_w2a4_linear_matches_oracle(kq):
         assert err <= TOL
 
 
-@pytest.mark.parametrize("layer,M,Nr", [(0, 4096, 6720), (0, 4000, 6416), (2, 4096, 2240), (1, 1100, 5600)])
+@pytest.mark.parametrize("layer,M,Nr", [(0, 4096, 6720), (0, 4000, 6416), (1, 4096, 5600), (2, 4096, 2240),
+                                         (1, 1100, 5600)])
 def test_w2a4_full_size_forms(kq, layer, M, Nr):
-    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, and with M and N
+    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, fc1, and with M and N
     ragged against it) and the 128 x 128 form (fc2, and fewer tokens); oracle on sampled rows
     (the edges of the 256- and 128-row tiles) and all columns."""
     import torch

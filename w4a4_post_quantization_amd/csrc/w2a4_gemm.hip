@@ -400,13 +400,13 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
 
 hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t M, int64_t K,
                             const uint8_t* wcodes, const __half* wscales, int64_t N, __half* Y, hipStream_t s) {
-  // The large-tile form does a 256 x 256 tile in about 0.7 of the time of four 128 x 128
-  // ones, but its rounds of tiles are four times coarser: it measured faster at 1.7 rounds
-  // (SANA-like qkv: 232 vs 289 us) and slower at 1.4 and 0.6 (fc1: 220 vs 211, fc2: 256 vs
-  // 223), so it runs from 1.5 rounds up.
+  // The large-tile form does a 256 x 256 tile in about half the time of four 128 x 128
+  // ones, but its rounds of tiles are four times coarser.  At the SANA-like shapes it
+  // measured 162 us at 1.4 rounds (fc1) against 181-203 us for the small tiles; below one
+  // round (fc2, 0.56) the small tiles fill the chip better, so it runs from one round up.
   const int64_t cus = device_cu_count();
   const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
-  if (2 * t256 >= 3 * cus) {
+  if (t256 >= cus) {
     hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3((unsigned)t256), dim3(256), 0, s, xcodes, xscales, (int)M,
                        (int)K, wcodes, wscales, (int)N, lm_tables(), Y);
     return hipGetLastError();
