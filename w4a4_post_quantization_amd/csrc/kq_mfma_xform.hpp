@@ -155,12 +155,16 @@ __device__ __forceinline__ void lm_pack_block(const float* y, int q, const float
   uint32_t h[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    // three-level search over the seven sorted thresholds; each level's threshold is
+    // selected by the earlier levels' outcomes
     const float a = fabsf(y[i]);
-    uint32_t idx = a > ts[3] ? 4u : 0u;
-    const float t1 = idx ? ts[5] : ts[1];
-    idx += a > t1 ? 2u : 0u;
-    const float t0 = idx == 0 ? ts[0] : idx == 2 ? ts[2] : idx == 4 ? ts[4] : ts[6];
-    idx += a > t0 ? 1u : 0u;
+    const bool c2 = a > ts[3];
+    const float tm = c2 ? ts[5] : ts[1];
+    const bool c1 = a > tm;
+    const float tl0 = c1 ? ts[2] : ts[0], tl1 = c1 ? ts[6] : ts[4];
+    const float tl = c2 ? tl1 : tl0;
+    const bool c0 = a > tl;
+    const uint32_t idx = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
     h[i >> 2] |= (idx | (y[i] < 0.0f ? 8u : 0u)) << (4 * (i & 3));
   }
   // outputs 4q..4q+3 are bytes 2q, 2q+1 of the block; 16+4q..16+4q+3 bytes 8+2q, 8+2q+1
