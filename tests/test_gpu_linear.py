@@ -390,6 +390,31 @@ def test_w2a4_full_size_forms(kq, layer, M, Nr):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("K", [2208, 2272])
+def test_w2a4_large_form_odd_group_count(kq, K):
+    """The 256 x 256 W2A4 form (one round of tiles: M = N = 4096) with an odd number of
+    32-wide groups, so that its last 64-wide step holds a single group (the missing group's
+    codes and scale read as zeros); K = 2208 also has an odd step count (the step after the
+    two-step loop), K = 2272 an even one.  Oracle on sampled rows, all columns."""
+    import torch
+    c = synth.CONFIGS[2]
+    M, N = 4096, 4096
+    X16 = synth.activations(M, K, 2, c["sigma_mu"])
+    W16, _, _ = synth.weights(K, N, 2, 0, 0)
+    xf = synth.xform_for(2, 0, K)
+    dxf = _dev_xform(kq, torch, xf, K)
+    xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(np.ascontiguousarray(W16)).cuda(), dxf, fmt="lm2",
+                                               with_wbar=False)
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, fmt="lm2")
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(0, M, 97)) | {0, 255, 256, M - 1}))
+    ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), rows=rows)
+    err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
+    print(f"W2A4 large form K={K}: {err:.3e}")
+    assert err <= TOL
+
+
 def test_w4a4_full_size_sampled(kq):
     """FLUX-like qkv at full size (M = 4608, K = 3072, N = 9216) in the bench's launch
     configuration; oracle on sampled rows and all columns."""
