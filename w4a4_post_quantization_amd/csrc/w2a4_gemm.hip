@@ -7,7 +7,7 @@
 // in LDS once per workgroup tile and multiplied on the fp16 matrix cores (fp32
 // accumulation); the per-token scale multiplies the accumulator before the fp16 store.  Two
 // forms: 128 x 128 tiles of 16 x 16 x 32 products, and 256 x 256 tiles of 32 x 32 x 16
-// products for grids of at least 1.5 rounds.
+// products for grids of at least one round of tiles.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
