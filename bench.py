@@ -26,7 +26,8 @@ from the HBM byte counters recorded in profiles/ for the same kernel source (nul
 source has changed since).  The shader clock is measured by the library's clock probe on a
 second stream while the GEMMs run, and the matrix-core peak is also given at that clock.
 The vendor library's MXFP4 GEMM (hipBLASLt, through torch._scaled_mm) is timed beside this
-library's GEMM on the same packed operands, as a comparison outside the step.
+library's GEMM on the same packed operands, as a comparison outside the step, and the library's
+FP4 matrix-core probe measures what the matrix cores sustain with no memory traffic at all.
 """
 
 import argparse
@@ -201,6 +202,33 @@ def probe_clock(torch, kq, run=None, spin_us=300, samples=5):
             vals.append(100.0 * cyc / ticks)
     vals.sort()
     return round(vals[len(vals) // 2], 1) if vals else None
+
+
+def mfma_probe(torch, kq, codes, iters=1200, reps=5):
+    """The scaled FP4 matrix cores with nothing else to do (kq_mfma_fp4_probe): four
+    workgroups of four wavefronts per compute unit, each issuing independent 32x32x64
+    products on real activation codes; median rate over `reps` launches, each timed alone
+    between two events, and the shader clock while it runs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 4 * cus
+    flops = 16 * iters * wgs * 2 * 32 * 32 * 64
+    out = torch.empty((4 * wgs,), dtype=torch.float32, device=codes.device)
+    kq.mfma_fp4_probe(iters, wgs, codes, out=out)
+    torch.cuda.synchronize()
+    rates = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kq.mfma_fp4_probe(iters, wgs, codes, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        rates.append(flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+    rates.sort()
+    mhz = probe_clock(torch, kq, lambda: kq.mfma_fp4_probe(iters, wgs, codes, out=out))
+    return {"TFLOPs": round(rates[len(rates) // 2], 1), "frac_of_peak": round(rates[len(rates) // 2] / PEAK_FP4_TFLOPS, 4),
+            "shader_mhz": mhz, "workgroups": wgs, "iters": iters,
+            "method": "kq_mfma_fp4_probe: 16 x iters scaled FP4 32x32x64 products per workgroup, no memory "
+                      "traffic, operands from the step's packed activation codes; median of 5 launches"}
 
 
 def rotation_count(set_bytes):
@@ -416,6 +444,10 @@ def main():
     clock_idle = probe_clock(torch, kq)
     log(f"shader clock: {clock_mhz} MHz while the GEMMs run, {clock_idle} MHz idle")
 
+    # ---- what the FP4 matrix cores sustain alone, for the GEMM's standing against it
+    probe = mfma_probe(torch, kq, layers[0]["codes"].view(-1))
+    log(f"FP4 matrix-core probe: {probe['TFLOPs']} TFLOP/s at {probe['shader_mhz']} MHz")
+
     # ---- the vendor library's MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on the step's
     # packed operands, beside this library's GEMM with no epilogue terms (the same product):
     # a comparison only, nothing of the step goes through it
@@ -561,7 +593,8 @@ def main():
                                  if traffic_gemm else None),
                      "algorithmic_bytes": sum(gemm_bytes(M, L["K"], L["N"], r, center) for L in layers),
                      "peak_at_measured_clock": round(peak_at_clock, 1) if peak_at_clock else None,
-                     "frac_at_measured_clock": round(gemm_tflops / peak_at_clock, 4) if peak_at_clock else None},
+                     "frac_at_measured_clock": round(gemm_tflops / peak_at_clock, 4) if peak_at_clock else None,
+                     "frac_of_mfma_probe": round(gemm_tflops / probe["TFLOPs"], 4)},
         "roofline_composite_g2g3": {"bound": "mfma", "definition": "(2MNK / MXFP4 peak + 2Mr(K+N) / fp16 peak) / "
                                                                   "(down-projection + GEMM time), the three layers",
                                     "frac": round(composite, 4),
@@ -589,6 +622,7 @@ def main():
         "transform_variants": variants,
         "sana_like_lloyd_max": sana,
         "vendor_mxfp4_gemm": vendor,
+        "mfma_fp4_probe": probe,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

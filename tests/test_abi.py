@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert kq.abi_version() == 7
+    assert kq.abi_version() == 8
     for s in range(0, 8):
         assert kq.status_str(s).startswith("KQ_")
     assert "UNKNOWN" in kq.status_str(99)
@@ -239,6 +239,18 @@ def test_clock_probe_validation(lib):
     assert f(0, FAKE, None) == 4
     assert f(1000001, FAKE, None) == 4
     assert f(100, ctypes.c_void_p(0x100004), None) == 3
+
+
+def test_mfma_probe_validation(lib):
+    f = lib.kq_mfma_fp4_probe
+    assert f(10, 4, None, FAKE, None) == 1
+    assert f(10, 4, FAKE, None, None) == 1
+    assert f(0, 4, FAKE, FAKE, None) == 4
+    assert f(1000001, 4, FAKE, FAKE, None) == 4
+    assert f(10, 0, FAKE, FAKE, None) == 4
+    assert f(10, 65537, FAKE, FAKE, None) == 4
+    assert f(10, 4, ctypes.c_void_p(0x100004), FAKE, None) == 3
+    assert f(10, 4, FAKE, ctypes.c_void_p(0x100002), None) == 3
 
 
 def test_lowrank_validation(lib):

@@ -21,7 +21,7 @@ another stream's work before the call has finished there.
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
+__all__ = ["mfma_fp4_probe", "load", "lib_path", "abi_version", "status_str", "lloyd_max_levels", "Xform",
            "transform_quantize", "fold_inverse_into_weights", "fold_inverse_into_weights_nk",
            "w4a4_linear", "w4a4_linear_t", "w4a4_linear_workspace_bytes",
            "lowrank_down", "lowrank_down_workspace_bytes", "transform_quantize_lowrank",
@@ -69,6 +69,8 @@ def load():
     lib.kq_status_str.argtypes = [i32]
     lib.kq_clock_probe.restype = i32
     lib.kq_clock_probe.argtypes = [i32, vp, vp]
+    lib.kq_mfma_fp4_probe.restype = i32
+    lib.kq_mfma_fp4_probe.argtypes = [i32, i32, vp, vp, vp]
     lib.kq_lloyd_max_levels.restype = i32
     lib.kq_lloyd_max_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_double)]
     lib.kq_transform_quantize.restype = i32
@@ -120,6 +122,24 @@ def clock_probe(spin_us, out=None, stream=None):
     s = load().kq_clock_probe(int(spin_us), _ptr(out), _stream(stream))
     if s != KQ_OK:
         raise KQError(s, "kq_clock_probe")
+    return out
+
+
+def mfma_fp4_probe(iters, workgroups, codes, out=None, stream=None):
+    """Launch the FP4 matrix-core rate probe on `stream` (see kq_mfma_fp4_probe): `codes` is a
+    device uint8 tensor of at least 2048 bytes (its first 2048 are the operands); returns the
+    float32 [4 * workgroups] tensor of per-wavefront sums.  The caller times the launch; the
+    work is 16 * iters * workgroups products of 2 * 32 * 32 * 64 flops."""
+    torch = _torch()
+    if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous() or codes.numel() < 2048:
+        raise ValueError("codes must be a contiguous device uint8 tensor of at least 2048 bytes")
+    if out is None:
+        out = torch.empty((4 * int(workgroups),), dtype=torch.float32, device=codes.device)
+        _on_stream(stream, out)
+    _check(out, "out", torch.float32, (4 * int(workgroups),))
+    s = load().kq_mfma_fp4_probe(int(iters), int(workgroups), _ptr(codes), _ptr(out), _stream(stream))
+    if s != KQ_OK:
+        raise KQError(s, "kq_mfma_fp4_probe")
     return out
 
 

@@ -155,6 +155,13 @@ kq_status kq_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t stream) {
   return hip_status(launch_clock_probe(spin_us, out, stream));
 }
 
+kq_status kq_mfma_fp4_probe(int32_t iters, int32_t workgroups, const void* codes, float* out, hipStream_t stream) {
+  if (!codes || !out) return KQ_ERR_NULL;
+  if (iters < 1 || iters > 1000000 || workgroups < 1 || workgroups > 65536) return KQ_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(out, 4)) return KQ_ERR_ALIGN;
+  return hip_status(launch_mfma_fp4_probe(iters, workgroups, codes, out, stream));
+}
+
 kq_status kq_transform_quantize(const kq_xform* xf, int32_t fmt, int32_t center, const void* X, int64_t M,
                                 int64_t K, uint8_t* codes, void* scales, void* mu, hipStream_t stream) {
   if (!X || !codes || !scales) return KQ_ERR_NULL;

@@ -97,6 +97,7 @@ int device_cu_count();
 // Shader-clock cycles and 100 MHz reference ticks over spin_us microseconds (out: device
 // uint64 [2]); one 64-thread workgroup.
 hipError_t launch_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t s);
+hipError_t launch_mfma_fp4_probe(int32_t iters, int32_t workgroups, const void* codes, float* out, hipStream_t s);
 
 int resident_blocks_per_cu(const void* kernel, int threads, size_t lds);
 
