@@ -205,13 +205,14 @@ def probe_clock(torch, kq, run=None, spin_us=300, samples=5):
 
 
 def mfma_probe(torch, kq, codes, iters=1200, reps=5):
-    """The scaled FP4 matrix cores with nothing else to do (kq_mfma_fp4_probe): four
-    workgroups of four wavefronts per compute unit, each issuing independent 32x32x64
-    products on real activation codes; median rate over `reps` launches, each timed alone
-    between two events, and the shader clock while it runs."""
+    """The scaled FP4 matrix cores with nothing else to do (kq_mfma_fp4_probe): one workgroup
+    of four wavefronts per compute unit (one per SIMD, as the GEMM runs), each issuing
+    sixteen independent 32x32x64 products per round on real activation codes; median rate
+    over `reps` launches, each timed alone between two events, and the shader clock while it
+    runs."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wgs = 4 * cus
-    flops = 16 * iters * wgs * 2 * 32 * 32 * 64
+    wgs = cus
+    flops = 64 * iters * wgs * 2 * 32 * 32 * 64
     out = torch.empty((4 * wgs,), dtype=torch.float32, device=codes.device)
     kq.mfma_fp4_probe(iters, wgs, codes, out=out)
     torch.cuda.synchronize()
@@ -227,8 +228,9 @@ def mfma_probe(torch, kq, codes, iters=1200, reps=5):
     mhz = probe_clock(torch, kq, lambda: kq.mfma_fp4_probe(iters, wgs, codes, out=out))
     return {"TFLOPs": round(rates[len(rates) // 2], 1), "frac_of_peak": round(rates[len(rates) // 2] / PEAK_FP4_TFLOPS, 4),
             "shader_mhz": mhz, "workgroups": wgs, "iters": iters,
-            "method": "kq_mfma_fp4_probe: 16 x iters scaled FP4 32x32x64 products per workgroup, no memory "
-                      "traffic, operands from the step's packed activation codes; median of 5 launches"}
+            "method": "kq_mfma_fp4_probe: one workgroup of four wavefronts per compute unit, 16 independent "
+                      "scaled FP4 32x32x64 products per wavefront and round, no memory traffic, operands from "
+                      "the step's packed activation codes; median of 5 launches"}
 
 
 def rotation_count(set_bytes):

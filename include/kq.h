@@ -146,13 +146,13 @@ kq_status kq_clock_probe(int32_t spin_us, uint64_t* out, hipStream_t stream);
 
 /* Measurement helper, outside the activation path: the rate the scaled FP4 matrix cores
  * sustain with no memory traffic.  `workgroups` workgroups of four wavefronts on `stream`;
- * each wavefront issues `iters` rounds of four independent v_mfma_scale_f32_32x32x64_f8f6f4
- * (E2M1 x E2M1, scales 2^0) on operands read once from `codes` (device, 2048 bytes, 16-byte
- * aligned, caller-owned: lane l uses bytes 16 l .. 16 l + 15 as A and 1024 + 16 l .. as B)
- * and writes one sum of its accumulators to out[4 * workgroup + wavefront] (device,
- * 4 * workgroups floats, caller-owned).  The work is 4 * 4 * iters * workgroups products of
- * 2 * 32 * 32 * 64 flops; the caller times the launch.  1 <= iters <= 1000000,
- * 1 <= workgroups <= 65536. */
+ * each wavefront issues `iters` rounds of sixteen independent v_mfma_scale_f32_32x32x64_f8f6f4
+ * (E2M1 x E2M1, scales 2^0) on operands a, b read once from `codes` (device, 2048 bytes,
+ * 16-byte aligned, caller-owned: lane l's a is bytes 16 l .. 16 l + 15, its b bytes 1024 + 16 l
+ * .. ; product u of a round is (u & 1 ? a : b) x (u & 2 ? a : b)) and writes one sum of its
+ * accumulators to out[4 * workgroup + wavefront] (device, 4 * workgroups floats,
+ * caller-owned).  The work is 64 * iters * workgroups products of 2 * 32 * 32 * 64 flops; the
+ * caller times the launch.  1 <= iters <= 1000000, 1 <= workgroups <= 65536. */
 kq_status kq_mfma_fp4_probe(int32_t iters, int32_t workgroups, const void* codes, float* out, hipStream_t stream);
 
 /* Online activation path (KroQuant §01-§03; OrbitQuant §03; CentriQ abstract):

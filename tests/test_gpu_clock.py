@@ -20,9 +20,9 @@ def test_clock_probe_reports_a_plausible_clock():
 
 
 def test_mfma_fp4_probe_sums():
-    """Each wavefront's sum equals the four products' total: with every lane holding the same
-    operands, one 32x32x64 product is 64 * (sum over the 32 codes' value products) per output,
-    and the probe adds iters of each of A.B, B.A, A.A and B.B over 1024 outputs."""
+    """Each wavefront's sum equals its products' total: with every lane holding the same
+    operands, one 32x32x64 product is 2 * (the 32 codes' dot product) per output, and each
+    round adds four each of A.B, B.A, A.A and B.B over 1024 outputs."""
     import numpy as np
     import torch
     import w4a4_post_quantization_amd as kq
@@ -41,7 +41,7 @@ def test_mfma_fp4_probe_sums():
     va, vb = vals(a), vals(b)
     # a lane pair (l, l + 32) holds k-blocks 0 and 1 of the 64-wide product, each 32 codes
     dot = lambda x, y: 2.0 * float(np.dot(x, y))
-    per_output = dot(va, vb) * 2 + dot(va, va) + dot(vb, vb)
+    per_output = 4 * (dot(va, vb) * 2 + dot(va, va) + dot(vb, vb))
     expect = iters * per_output * 32 * 32
     got = out.cpu().numpy()
     assert got.shape == (4 * wgs,)

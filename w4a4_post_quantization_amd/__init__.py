@@ -129,7 +129,7 @@ def mfma_fp4_probe(iters, workgroups, codes, out=None, stream=None):
     """Launch the FP4 matrix-core rate probe on `stream` (see kq_mfma_fp4_probe): `codes` is a
     device uint8 tensor of at least 2048 bytes (its first 2048 are the operands); returns the
     float32 [4 * workgroups] tensor of per-wavefront sums.  The caller times the launch; the
-    work is 16 * iters * workgroups products of 2 * 32 * 32 * 64 flops."""
+    work is 64 * iters * workgroups products of 2 * 32 * 32 * 64 flops."""
     torch = _torch()
     if codes.dtype != torch.uint8 or not codes.is_cuda or not codes.is_contiguous() or codes.numel() < 2048:
         raise ValueError("codes must be a contiguous device uint8 tensor of at least 2048 bytes")
