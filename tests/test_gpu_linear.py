@@ -433,11 +433,14 @@ def _sampled_rows(M):
     return np.array(sorted(r for r in rows if 0 <= r < M))
 
 
-@pytest.mark.parametrize("rank,with_mu", [(0, False), (16, True), (64, False), (32, True)])
-def test_w4a4_large_tile_form_ragged(kq, rank, with_mu):
-    """Enough 256 x 256 tiles for the large-tile kernel form (K a multiple of 512), with M
-    and N not multiples of the tile; oracle on sampled rows and all columns."""
-    M, N, K = 1800, 4624, 1024
+@pytest.mark.parametrize("rank,with_mu,K", [(0, False, 1024), (16, True, 1024), (64, False, 1024), (32, True, 1024),
+                                            (32, True, 1152), (0, False, 640), (16, True, 1408)])
+def test_w4a4_large_tile_form_ragged(kq, rank, with_mu, K):
+    """Enough 256 x 256 tiles for the large-tile (direct-to-LDS) kernel form, with M and N not
+    multiples of the tile; K = 1152, 640 and 1408 leave a last group of 1, 1 and 3 k-steps of
+    128 for the scale loads, whose 16-byte pieces then run into the next row (and, on the last
+    row, past the end of the scales).  Oracle on sampled rows and all columns."""
+    M, N = 1800, 4624
     d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=rank, with_mu=with_mu)
     rows = _sampled_rows(M)
     err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))

@@ -14,7 +14,7 @@
 //
 // Two kernel forms share that arithmetic:
 //   - a configurable-tile form that stages the operands global -> registers -> LDS, for
-//     small grids and for K not a multiple of 512;
+//     small grids;
 //   - a 256x256-tile form whose operands go from global memory straight into LDS (buffer
 //     loads with the LDS destination), four stages deep, for the large shapes.
 // Per 128-wide k-step a row contributes 64 code bytes and 4 scale bytes.
@@ -365,8 +365,10 @@ __global__ __launch_bounds__(256, 1) void w4a4_gemm_dma_kernel(
     else lds_load16(rB, st + B_OFF + (64 * wid + 16 * (g - 4)) * 64, off);
   };
   // scale group grp (k-steps 4 grp .. 4 grp + 3), issued only when skip is zero: 16 bytes
-  // per row (K is a multiple of 512, so a group never straddles two rows).  The skip is a
-  // branch inside the assembly so that the loop body stays one block for the instruction
+  // per row.  When K is not a multiple of 512 the last group's piece runs into the next
+  // row's scales (or, on the last row, past the end of the range, which reads zeros per
+  // dword); the bytes of k-steps past the last are never read.  The skip is a branch
+  // inside the assembly so that the loop body stays one block for the instruction
   // scheduler (a compiler branch here lets it move MFMAs across the barrier).
   auto scale_loads = [&](int grp, int skip) {
     const uint32_t sc = lds0 + (uint32_t)(DMA_SC_OFF + (grp & 1) * DMA_SC_BYTES + 16 * 64 * wid);
@@ -665,7 +667,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* xcodes, const uint8_t* xscales, int64
   using Big = GemmCfg<256, 256, 2, 4, 1>;
   using Small = GemmCfg<128, 128, 2, 2, 1>;
   const int64_t big_tiles = ((N + 255) / 256) * ((M + 255) / 256);
-  if (big_tiles >= device_cu_count() / 2 && K % 512 == 0)
+  if (big_tiles >= device_cu_count() / 2 && K % 128 == 0)
     return gemm_dma_launch(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
   if (big_tiles >= device_cu_count() / 2)
     return gemm_launch<Big>(xcodes, xscales, M, K, wcodes, wscales, N, T, L2, r, mu, wbar, Y, s);
