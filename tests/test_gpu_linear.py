@@ -450,8 +450,8 @@ def test_w4a4_large_tile_form_ragged(kq, rank, with_mu, K):
 
 @pytest.mark.parametrize("cfg,layer", [(1, 0), (1, 3), (4, 0), (4, 1)])
 def test_w4a4_full_size_other_configs(kq, cfg, layer):
-    """The PixArt-like (M = 8192; qkv K = 1152 on the register-staged form, fc2 K = 4608 on
-    the large-tile form) and CogVideoX-like (M = 17550, ragged against 256-row tiles) linears
+    """The PixArt-like (M = 8192; qkv K = 1152, a short last scale group, and fc2 K = 4608,
+    both on the large-tile form) and CogVideoX-like (M = 17550, ragged against 256-row tiles) linears
     at full size: oracle on sampled rows and all columns."""
     M = synth.CONFIGS[cfg]["M"]
     d = _linear_case(kq, cfg, layer, M)
