@@ -448,6 +448,19 @@ def test_w4a4_large_tile_form_ragged(kq, rank, with_mu, K):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("N", [2032, 2064])
+def test_w4a4_forms_at_the_threshold(kq, N):
+    """Either side of the switch between the GEMM forms on MI355X's 256 compute units: 64
+    tiles of 256 x 256 (N = 2032) take the 128 x 128 form, 72 (N = 2064) the direct-to-LDS
+    form; M and N ragged, K = 640 (a short last scale group), rank 32 and the rank-1 restore."""
+    M, K = 2041, 640
+    d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=32, with_mu=True)
+    rows = _sampled_rows(M)
+    err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
+    print(f"M={M} N={N} K={K}: {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("cfg,layer", [(1, 0), (1, 3), (4, 0), (4, 1)])
 def test_w4a4_full_size_other_configs(kq, cfg, layer):
     """The PixArt-like (M = 8192; qkv K = 1152, a short last scale group, and fc2 K = 4608,
