@@ -367,8 +367,8 @@ def test_w2a4_linear_matches_oracle(kq):
 @pytest.mark.parametrize("layer,M,Nr", [(0, 4096, 6720), (0, 4000, 6416), (1, 4096, 5600), (2, 4096, 2240),
                                          (1, 1100, 5600)])
 def test_w2a4_full_size_forms(kq, layer, M, Nr):
-    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, fc1, and with M and N
-    ragged against it) and the 128 x 128 form (fc2, and fewer tokens); oracle on sampled rows
+    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, fc1, fc2, and with M
+    and N ragged against it) and the 128 x 128 form (fewer tokens); oracle on sampled rows
     (the edges of the 256- and 128-row tiles) and all columns."""
     import torch
     c = synth.CONFIGS[2]
@@ -412,6 +412,30 @@ def test_w2a4_large_form_odd_group_count(kq, K):
     ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), rows=rows)
     err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
     print(f"W2A4 large form K={K}: {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("Nr", [2032, 2064])
+def test_w2a4_forms_at_the_threshold(kq, Nr):
+    """Either side of the switch between the W2A4 forms on MI355X's 256 compute units: 128
+    tiles of 256 x 256 (N = 2032) take the 128 x 128 form, 144 (N = 2064) the large one; M and
+    N ragged against both tile sizes.  Oracle on sampled rows, all columns."""
+    import torch
+    c = synth.CONFIGS[2]
+    M, K = 4000, 2240
+    X16 = synth.activations(M, K, 2, c["sigma_mu"])
+    W16, _, _ = synth.weights(K, c["layers"][0][2], 2, 0, 0)
+    W16 = np.ascontiguousarray(W16[:Nr])
+    xf = synth.xform_for(2, 0, K)
+    dxf = _dev_xform(kq, torch, xf, K)
+    xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, fmt="lm2")
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(0, M, 89)) | {127, 128, 255, 256, M - 1}))
+    ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), rows=rows)
+    err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
+    print(f"W2A4 M={M} N={Nr} K={K}: {err:.3e}")
     assert err <= TOL
 
 

@@ -7,7 +7,7 @@
 // in LDS once per workgroup tile and multiplied on the fp16 matrix cores (fp32
 // accumulation); the per-token scale multiplies the accumulator before the fp16 store.  Two
 // forms: 128 x 128 tiles of 16 x 16 x 32 products, and 256 x 256 tiles of 32 x 32 x 16
-// products for grids of at least one round of tiles.
+// products for grids of more than half a round of tiles.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -400,13 +400,13 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
 
 hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t M, int64_t K,
                             const uint8_t* wcodes, const __half* wscales, int64_t N, __half* Y, hipStream_t s) {
-  // The large-tile form does a 256 x 256 tile in about half the time of four 128 x 128
-  // ones, but its rounds of tiles are four times coarser.  At the SANA-like shapes it
-  // measured 162 us at 1.4 rounds (fc1) against 181-203 us for the small tiles; below one
-  // round (fc2, 0.56) the small tiles fill the chip better, so it runs from one round up.
+  // The large-tile form does a 256 x 256 tile in about the time of two rounds of 128 x 128
+  // ones, and its rounds of tiles are four times coarser: it runs once the small tiles would
+  // take more than two rounds (measured at K = 2240 and 5600: the small tiles win by 8-40%
+  // up to 128 large tiles, the large ones by 12-70% from 144 up).
   const int64_t cus = device_cu_count();
   const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
-  if (t256 >= cus) {
+  if (2 * t256 > cus) {
     hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3((unsigned)t256), dim3(256), 0, s, xcodes, xscales, (int)M,
                        (int)K, wcodes, wscales, (int)N, lm_tables(), Y);
     return hipGetLastError();
