@@ -439,14 +439,17 @@ def test_w2a4_forms_at_the_threshold(kq, Nr):
     assert err <= TOL
 
 
-def test_w4a4_full_size_sampled(kq):
-    """FLUX-like qkv at full size (M = 4608, K = 3072, N = 9216) in the bench's launch
-    configuration; oracle on sampled rows and all columns."""
-    d = _linear_case(kq, 3, 0, 4608)
-    rows = np.arange(5, 4608, 151)
+@pytest.mark.parametrize("layer", [0, 1])
+def test_w4a4_full_size_sampled(kq, layer):
+    """FLUX-like qkv (M = 4608, K = 3072, N = 9216: 256 x 256 tiles only) and fc1 (N = 12288:
+    its last two tile rows in tiles of half the width) at full size in the bench's launch
+    configuration; oracle on sampled rows (both edges of the switch to the half-width tiles
+    at row 4096 among them) and all columns."""
+    d = _linear_case(kq, 3, layer, 4608)
+    rows = np.array(sorted(set(range(5, 4608, 151)) | {4095, 4096, 4351, 4352, 4607}))
     ref = _ref_Y(d, rows=rows)
     err = linear.rel_frobenius(d["Y"][rows], ref)
-    print(f"full-size sampled rel frobenius {err:.3e}")
+    print(f"layer {layer} full-size sampled rel frobenius {err:.3e}")
     assert err <= TOL
 
 
@@ -472,12 +475,13 @@ def test_w4a4_large_tile_form_ragged(kq, rank, with_mu, K):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("N", [2032, 2064])
-def test_w4a4_forms_at_the_threshold(kq, N):
-    """Either side of the switch between the GEMM forms on MI355X's 256 compute units: 64
-    tiles of 256 x 256 (N = 2032) take the 128 x 128 form, 72 (N = 2064) the direct-to-LDS
-    form; M and N ragged, K = 640 (a short last scale group), rank 32 and the rank-1 restore."""
-    M, K = 2041, 640
+@pytest.mark.parametrize("M,N,K", [(2041, 2032, 640), (2041, 2064, 640), (4600, 12272, 640), (4600, 11008, 1152)])
+def test_w4a4_half_width_tiles(kq, M, N, K):
+    """Grids with tiles of half the width (256 token rows x 128 weight rows) on MI355X's 256
+    compute units: 64 and 72 tiles of 256 x 256 (N = 2032, 2064) run as half-width tiles only;
+    864 tiles (N = 12272) run their last two tile rows half-width, 774 (N = 11008) their last
+    one.  M ragged, N ragged against the half-width tiles too (2064 and 12272), K = 640 and
+    1152 (short last scale groups), rank 32 and the rank-1 restore."""
     d = _linear_case(kq, 1, 1, M, N=N, K=K, rank=32, with_mu=True)
     rows = _sampled_rows(M)
     err = linear.rel_frobenius(d["Y"][rows], _ref_Y(d, rows=rows))
