@@ -391,6 +391,32 @@ def test_w2a4_full_size_forms(kq, layer, M, Nr):
 
 
 @pytest.mark.parametrize("K", [2208, 2272])
+def test_w2a4_half_width_tiles(kq, K):
+    """The 256 x 256 W2A4 form with its last five tile rows in tiles of half the width (352
+    tiles: 96 past the first round, as 220 half-width tiles), M ragged (M = 4000) and N ragged
+    against both tile widths (N = 5584), with an odd number of 32-wide groups (a last step
+    with one group; K = 2208 also an odd step count).  Oracle on sampled rows (both edges of
+    the switch at row 2816 among them), all columns."""
+    import torch
+    c = synth.CONFIGS[2]
+    M, N = 4000, 5584
+    X16 = synth.activations(M, K, 2, c["sigma_mu"])
+    W16, _, _ = synth.weights(K, c["layers"][0][2], 2, 0, 0)
+    W16 = np.ascontiguousarray(W16[:N])
+    xf = synth.xform_for(2, 0, K)
+    dxf = _dev_xform(kq, torch, xf, K)
+    xc, xs, _ = kq.transform_quantize(torch.from_numpy(X16).cuda(), dxf, fmt="lm4")
+    wc, ws, _ = kq.fold_inverse_into_weights_nk(torch.from_numpy(W16).cuda(), dxf, fmt="lm2", with_wbar=False)
+    Y = kq.w4a4_linear_t(xc, xs, wc, ws, fmt="lm2")
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(0, M, 97)) | {2815, 2816, 3839, 3840, M - 1}))
+    ref = linear.w2a4_linear(xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy(), rows=rows)
+    err = linear.rel_frobenius(Y.cpu().numpy()[rows], ref)
+    print(f"W2A4 half-width tiles M={M} N={N} K={K}: {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("K", [2208, 2272])
 def test_w2a4_large_form_odd_group_count(kq, K):
     """The 256 x 256 W2A4 form (one round of tiles: M = N = 4096) with an odd number of
     32-wide groups, so that its last 64-wide step holds a single group (the missing group's

@@ -200,106 +200,124 @@ __global__ __launch_bounds__(WN * WM * 64) void w2a4_gemm_kernel(
   }
 }
 
-// Large-tile form: BN = 256 weight rows x BM = 256 tokens per workgroup on 4 wavefronts
-// (2 x 2), each owning a 128 x 128 block of 32 x 32 output tiles
-// (v_mfma_f32_32x32x16_f16: lane l holds row l % 32 and k = 8 (l / 32) .. + 7 of each
-// 16-wide step; result register 4 g + e of lane l is C[8 g + 4 (l / 32) + e][l % 32]).
-// Against 64 x 64 wave tiles of 16 x 16 products this reads half the LDS bytes per
-// product.  A k-step is two groups (64 k) held as fp16 in one of two LDS buffers: thread t
-// dequantizes weight row t and token row t into the buffer the next step reads, LDS rows of
-// 128 bytes with their 16-byte chunks XOR-swizzled by the row's low bits.
-// Schedule of a step, pinned with scheduling barriers so that the matrix cores never wait
-// for a whole phase:
+// Large-tile form: 64 TN weight rows (TN = 4: 256; TN = 2: 128, a tile of half the width
+// for the last round of a grid) x 256 tokens per workgroup on 4 wavefronts (2 x 2), each
+// owning a 32 TN x 128 block of 32 x 32 output tiles (v_mfma_f32_32x32x16_f16: lane l
+// holds row l % 32 and k = 8 (l / 32) .. + 7 of each 16-wide step; result register 4 g + e
+// of lane l is C[8 g + 4 (l / 32) + e][l % 32]).  Against 64 x 64 wave tiles of 16 x 16
+// products the full tile reads half the LDS bytes per product.  A k-step is two groups
+// (64 k) held as fp16 in one of two LDS buffers: thread t dequantizes token row t and
+// weight row t (TN = 4) or one group of weight row t / 2 (TN = 2) into the buffer the next
+// step reads, LDS rows of 128 bytes with their 16-byte chunks XOR-swizzled by the row's low
+// bits.  Schedule of a step, pinned with scheduling barriers so that the matrix cores never
+// wait for a whole phase:
 //   - the fragments of the step's first 16-wide slice are read;
-//   - the 64 products run as four slices of 16; after each of the first eight products of
-//     a slice one fragment of the next slice is read, and after every fourth product one of
-//     the sixteen 8-code chunks of the next step is dequantized and stored to the other
-//     buffer;
+//   - the 16 TN products run as four slices of 4 TN; after each of the first TN + 4
+//     products of a slice one fragment of the next slice is read, and the thread's 8-code
+//     chunks of the next step (16, or 12 in the half-width tile) are dequantized and stored
+//     to the other buffer one at a time, spread evenly over the products;
 //   - one barrier: the next step's buffer is complete, this one is free.
 // The codes a step dequantizes were loaded one step earlier (the loads of step ks + 2 go
 // out during step ks, one at a time between products), so the dequantization never waits
-// for memory.  Loads past
-// the last step or of a missing second group (K % 64 = 32) are outside the buffer ranges
-// and read zeros: the group's scale is then zero and so are its products.
-__global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
-    const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
-    const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales, int N, LmTables lm,
-    __half* __restrict__ Y) {
-  constexpr int BN = 256, BM = 256, TN = 4, TM = 4, RB = 128;   // RB: LDS bytes per row and step
-  constexpr int A_OFF = 0, B_OFF = BN * RB, BUF = (BN + BM) * RB;
-  __shared__ __align__(16) uint8_t lds[2 * BUF];
+// for memory.  Loads past the last step or of a missing second group (K % 64 = 32) are
+// outside the buffer ranges and read zeros: the group's scale is then zero and so are its
+// products.
+template <int TN>
+struct W2Raw {                     // the codes of one step that a thread stages
+  v2u w[TN == 4 ? 2 : 1];          // weight codes: both groups of its row, or its one group
+  uint32_t s[TN == 4 ? 2 : 1];     // their fp16 group scales
+  v4u x[2];                        // activation codes of both groups of its token row
+};
 
+// The chunk dequantized after product p of a step (-1: none): in the full tile after every
+// fourth product; in the half-width tile chunk j after product 8 j / 3 + 2.
+template <int TN>
+__host__ __device__ constexpr int w2_dq_at(int p) {
+  if (TN == 4) return (p & 3) == 3 ? p >> 2 : -1;
+  for (int j = 0; j < 12; ++j)
+    if (p == 8 * j / 3 + 2) return j;
+  return -1;
+}
+
+// The load issued after product m of slice sub (-1: none): six per step in the full tile
+// (weight codes, scale and activation codes of each group), four in the half-width tile
+// (its group's weight codes and scale, the two groups' activation codes).
+template <int TN>
+__host__ __device__ constexpr int w2_load_at(int sub, int m) {
+  if (TN == 4) return sub < 3 && (m == 1 || m == 9) ? 2 * sub + (m >> 3) : -1;
+  return sub < 2 && (m == 1 || m == 5) ? 2 * sub + (m >> 2) : -1;
+}
+
+template <int TN>
+__device__ __forceinline__ void w2a4_big_tile(uint8_t* __restrict__ lds, const uint8_t* __restrict__ xcodes,
+                                              const float* __restrict__ xscales, int M, int K,
+                                              const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales,
+                                              int N, const LmRegTables& lt, __half* __restrict__ Y, int m0, int n0) {
+  constexpr int TM = 4, RB = 128;                       // RB: LDS bytes per row and step
+  constexpr int A_OFF = 0, B_OFF = 256 * RB, BUF = 512 * RB;   // the full tile's layout in both widths
+  constexpr int NWC = TN == 4 ? 8 : 4;                  // weight chunks a thread dequantizes per step
+  constexpr int NU = TN == 4 ? 6 : 4;                   // loads a thread issues per step
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int l32 = lane & 31, h = lane >> 5;
-  const LmRegTables lt = lm_reg_tables(lm);
-
-  // tiles walked column by column in groups of 8 along M, die-contiguous (as the W4A4 form)
-  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
-  const int ntiles = tiles_n * tiles_m;
-  int pid = blockIdx.x;
-  {
-    const int per = ntiles / 8;
-    if (pid < 8 * per) pid = (pid % 8) * per + pid / 8;
-  }
-  constexpr int GM = 8;
-  const int group = pid / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int tile_m = first_m + (pid % (GM * tiles_n)) % gsize;
-  const int tile_n = (pid % (GM * tiles_n)) / gsize;
-  const int n0 = tile_n * BN, m0 = tile_m * BM;
   const int ng = K >> 5, nks = (ng + 1) >> 1;             // groups, 64-wide steps
 
-  // staging rows of this thread, relative to the tile: weight row tid, token row tid; rows
-  // past the matrix repeat its last row (their results are never stored)
-  const int wr = min(n0 + tid, N - 1) - n0, xr = min(m0 + tid, M - 1) - m0;
+  // staging rows of this thread, relative to the tile: token row tid, and weight row tid
+  // (both groups of a step) or weight row tid / 2 (group tid % 2 of a step); rows past the
+  // matrix repeat its last row (their results are never stored)
+  const int wrow = TN == 4 ? tid : tid >> 1, wq = TN == 4 ? 0 : tid & 1;
+  const int wr = min(n0 + wrow, N - 1) - n0, xr = min(m0 + tid, M - 1) - m0;
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(wcodes + (int64_t)n0 * (K >> 2), (int64_t)(N - n0) * (K >> 2));
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(wscales + (int64_t)n0 * ng, (int64_t)(N - n0) * ng * 2);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(xcodes + (int64_t)m0 * (K >> 1), (int64_t)(M - m0) * (K >> 1));
   const int ow = wr * (K >> 2), os = wr * ng * 2, ox = xr * (K >> 1);
-  const int sw = tid & 7;
+  const int swa = wrow & 7, swb = tid & 7;
 
-  // the codes of one step: the two groups' weight codes (8 bytes each) and fp16 scales, and
-  // their activation codes (16 bytes each)
-  struct Raw {
-    v2u w[2];
-    uint32_t s[2];
-    v4u x[2];
-  };
-  // load u (0..5) of step ks: u / 3 is the group, u % 3 picks weight codes, scale or
-  // activation codes.  Each load touches one cache line per lane (a row per thread), so the
-  // six go out one at a time between products: issued together they would hold the wave,
+  // load u of step ks.  Each load touches one cache line per lane (a row per thread), so
+  // they go out one at a time between products: issued together they would hold the wave,
   // and its matrix core, for their whole address-unit time.
-  auto gload1 = [&](int ks, Raw& r, int u) {
-    const int q = u / 3;
-    const bool v = q == 0 ? ks < nks : 2 * ks + 1 < ng;
-    if (u % 3 == 0)
-      r.w[q] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rW, v ? ow + 16 * ks + 8 * q : KQ_OOB, 0, 0));
-    else if (u % 3 == 1)
-      r.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rS, v ? os + 4 * ks + 2 * q : KQ_OOB, 0, 0);
-    else
+  auto gload1 = [&](int ks, W2Raw<TN>& r, int u) {
+    if (TN == 4) {            // u / 3 is the group, u % 3 picks weight codes, scale or activation codes
+      const int q = u / 3;
+      const bool v = 2 * ks + q < ng;
+      if (u % 3 == 0)
+        r.w[q] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rW, v ? ow + 16 * ks + 8 * q : KQ_OOB, 0, 0));
+      else if (u % 3 == 1)
+        r.s[q] = __builtin_amdgcn_raw_buffer_load_b16(rS, v ? os + 4 * ks + 2 * q : KQ_OOB, 0, 0);
+      else
+        r.x[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rX, v ? ox + 32 * ks + 16 * q : KQ_OOB, 0, 0));
+    } else if (u < 2) {       // the thread's group of its weight row: codes, then scale
+      const bool v = 2 * ks + wq < ng;
+      if (u == 0)
+        r.w[0] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rW, v ? ow + 16 * ks + 8 * wq : KQ_OOB, 0, 0));
+      else
+        r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rS, v ? os + 4 * ks + 2 * wq : KQ_OOB, 0, 0);
+    } else {                  // activation codes of group u - 2
+      const int q = u - 2;
+      const bool v = 2 * ks + q < ng;
       r.x[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rX, v ? ox + 32 * ks + 16 * q : KQ_OOB, 0, 0));
+    }
   };
-  auto gload = [&](int ks, Raw& r) {
+  auto gload = [&](int ks, W2Raw<TN>& r) {
 #pragma unroll
-    for (int u = 0; u < 6; ++u) gload1(ks, r, u);
+    for (int u = 0; u < NU; ++u) gload1(ks, r, u);
   };
-  // chunk j (0..15) of a step into buffer buf: j < 8 the weight row's chunk j (group j / 4),
-  // else the token row's chunk j - 8; each is 8 codes -> 16 bytes of fp16
-  uint32_t tw[2][2];                                      // the two groups' weight tables
-  auto dq_chunk = [&](const Raw& r, int buf, int j) {
+  // chunk j of a step into buffer buf: j < NWC a weight chunk (group j / 4 of the row, or
+  // the thread's group), else token chunk j - NWC; each is 8 codes -> 16 bytes of fp16
+  uint32_t tw[TN == 4 ? 2 : 1][2];                       // the groups' weight tables
+  auto dq_chunk = [&](const W2Raw<TN>& r, int buf, int j) {
     uint8_t* const base = lds + buf * BUF;
     uint32_t o[4];
-    if (j < 8) {
+    if (j < NWC) {
       const int q = j >> 2, c = j & 3;
       if (c == 0) w2_group_table(lt, __ushort_as_half((unsigned short)r.s[q]), tw[q][0], tw[q][1]);
       dequant_w2((r.w[q][c >> 1] >> (16 * (c & 1))) & 0xFFFFu, tw[q][0], tw[q][1], o);
-      *reinterpret_cast<v4u*>(base + A_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) = v4u{o[0], o[1], o[2], o[3]};
+      const int slot = 4 * (TN == 4 ? q : wq) + c;
+      *reinterpret_cast<v4u*>(base + A_OFF + wrow * RB + 16 * (slot ^ swa)) = v4u{o[0], o[1], o[2], o[3]};
     } else {
-      const int q = (j - 8) >> 2, c = (j - 8) & 3;
+      const int q = (j - NWC) >> 2, c = (j - NWC) & 3;
       dequant_a4(r.x[q][c], lt, o);
-      *reinterpret_cast<v4u*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ sw)) = v4u{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<v4u*>(base + B_OFF + tid * RB + 16 * ((4 * q + c) ^ swb)) = v4u{o[0], o[1], o[2], o[3]};
     }
   };
 
@@ -311,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int wrow_a = wn * 128, wrow_b = wm * 128;
+  const int wrow_a = wn * 32 * TN, wrow_b = wm * 128;
   // fragment i of a wave reads row wrow + 32 i + l32, whose swizzle (row & 7) is the lane's
   const int fa_off = A_OFF + (wrow_a + l32) * RB, fb_off = B_OFF + (wrow_b + l32) * RB, swl = l32 & 7;
   auto rd_a = [&](int buf, int sub, int i) {
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   // two steps per iteration, so that the two register sets alternate without copies (a copy
   // would wait for the loads still in flight).  The buffer index is hidden from the compiler:
   // knowing it, it would keep both buffers' LDS addresses in registers and spill.
-  auto step = [&](int ks, const Raw& cur, Raw& ld) {
+  auto step = [&](int ks, const W2Raw<TN>& cur, W2Raw<TN>& ld) {
     int buf = ks & 1;
     asm volatile("" : "+s"(buf));
     v8h fa[2][TN], fb[2][TM];
@@ -348,12 +366,12 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
           else fb[n][m - TN] = rd_b(buf, sub + 1, m - TN);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if ((m & 3) == 3) {
-          dq_chunk(cur, buf ^ 1, 4 * sub + (m >> 2));
+        if (w2_dq_at<TN>(TN * TM * sub + m) >= 0) {
+          dq_chunk(cur, buf ^ 1, w2_dq_at<TN>(TN * TM * sub + m));
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (sub < 3 && (m == 1 || m == 9)) {
-          gload1(ks + 2, ld, 2 * sub + (m >> 3));
+        if (w2_load_at<TN>(sub, m) >= 0) {
+          gload1(ks + 2, ld, w2_load_at<TN>(sub, m));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -361,11 +379,11 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     lds_barrier();                                        // the next buffer is complete, this one free
   };
 
-  Raw ra, rb;
+  W2Raw<TN> ra, rb;
   gload(0, ra);
   gload(1, rb);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) dq_chunk(ra, 0, j);
+  for (int j = 0; j < NWC + 8; ++j) dq_chunk(ra, 0, j);
   lds_barrier();
   // pairs of steps, then the last step when their number is odd (a conditional second step
   // inside the loop makes the register allocator copy the accumulators, and spill)
@@ -398,17 +416,64 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   }
 }
 
+// The large-tile form's kernel: the first full_rows rows of 256 x 256 tiles take the full
+// tile (walked column by column in groups of 8 along M, die-contiguous, as in the W4A4
+// kernel), the tile rows below them, if any, tiles of half the width.
+__global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
+    const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
+    const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales, int N, LmTables lm,
+    __half* __restrict__ Y, int full_rows) {
+  __shared__ __align__(16) uint8_t lds[2 * 512 * 128];
+  const LmRegTables lt = lm_reg_tables(lm);
+  const int tiles_n = (N + 255) / 256;
+  const int nfull = tiles_n * full_rows;
+  int pid = blockIdx.x;
+  if (pid < nfull) {
+    {
+      const int per = nfull / 8;
+      if (pid < 8 * per) pid = (pid % 8) * per + pid / 8;
+    }
+    constexpr int GM = 8;
+    const int group = pid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsize = min(full_rows - first_m, GM);
+    const int tile_m = first_m + (pid % (GM * tiles_n)) % gsize;
+    const int tile_n = (pid % (GM * tiles_n)) / gsize;
+    w2a4_big_tile<4>(lds, xcodes, xscales, M, K, wcodes, wscales, N, lt, Y, 256 * tile_m, 256 * tile_n);
+  } else {
+    const int hrows = (M + 255) / 256 - full_rows;
+    const int nh = ((N + 127) / 128) * hrows;
+    int q = pid - nfull;
+    {
+      const int per = nh / 8;
+      if (q < 8 * per) q = (q % 8) * per + q / 8;
+    }
+    const int tile_m = full_rows + q % hrows, tile_n = q / hrows;
+    w2a4_big_tile<2>(lds, xcodes, xscales, M, K, wcodes, wscales, N, lt, Y, 256 * tile_m, 128 * tile_n);
+  }
+}
+
 hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t M, int64_t K,
                             const uint8_t* wcodes, const __half* wscales, int64_t N, __half* Y, hipStream_t s) {
   // The large-tile form does a 256 x 256 tile in about the time of two rounds of 128 x 128
   // ones, and its rounds of tiles are four times coarser: it runs once the small tiles would
   // take more than two rounds (measured at K = 2240 and 5600: the small tiles win by 8-40%
   // up to 128 large tiles, the large ones by 12-70% from 144 up).
+  // A last round that leaves compute units idle goes to tiles of half the width when those
+  // fit in one round (as in the W4A4 kernel).
   const int64_t cus = device_cu_count();
-  const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
+  const int64_t tiles_n = (N + 255) / 256, tiles_m = (M + 255) / 256, tiles_n2 = (N + 127) / 128;
+  const int64_t t256 = tiles_n * tiles_m;
   if (2 * t256 > cus) {
-    hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3((unsigned)t256), dim3(256), 0, s, xcodes, xscales, (int)M,
-                       (int)K, wcodes, wscales, (int)N, lm_tables(), Y);
+    const int64_t tail = t256 % cus;
+    int64_t full_rows = tiles_m;
+    if (tail > 0) {
+      const int64_t hr = (tail + tiles_n - 1) / tiles_n;     // tile rows that hold the tail
+      if (hr * tiles_n2 <= cus) full_rows = tiles_m - hr;
+    }
+    const unsigned grid = (unsigned)(tiles_n * full_rows + tiles_n2 * (tiles_m - full_rows));
+    hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3(grid), dim3(256), 0, s, xcodes, xscales, (int)M, (int)K, wcodes,
+                       wscales, (int)N, lm_tables(), Y, (int)full_rows);
     return hipGetLastError();
   }
   constexpr int BN = 128, BM = 128, WN = 2, WM = 2;
