@@ -345,6 +345,8 @@ def test_w4a4_end_to_end_quality_informational(kq):
 
 
 def test_w2a4_linear_matches_oracle(kq):
+    """Small grids (the 128 x 128 W2A4 form): SANA-like qkv and fc2 weights on 130 and 64
+    tokens, N cut to 480 and 2240; oracle on every output."""
     import torch
     c = synth.CONFIGS[2]
     for layer, M, Nr in ((0, 130, 480), (2, 64, 2240)):
@@ -367,9 +369,10 @@ def test_w2a4_linear_matches_oracle(kq):
 @pytest.mark.parametrize("layer,M,Nr", [(0, 4096, 6720), (0, 4000, 6416), (1, 4096, 5600), (2, 4096, 2240),
                                          (1, 1100, 5600)])
 def test_w2a4_full_size_forms(kq, layer, M, Nr):
-    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, fc1, fc2, and with M
-    and N ragged against it) and the 128 x 128 form (fewer tokens); oracle on sampled rows
-    (the edges of the 256- and 128-row tiles) and all columns."""
+    """The W2A4 linear at the SANA-like sizes: the 256 x 256 form (qkv, fc2, and with M and N
+    ragged against it), with its last five tile rows in half-width tiles (fc1), and in
+    half-width tiles only (fewer tokens: 110 tiles of 256 x 256); oracle on sampled rows (the
+    edges of the 256- and 128-row tiles) and all columns."""
     import torch
     c = synth.CONFIGS[2]
     _, K, N = c["layers"][layer]
@@ -443,9 +446,10 @@ def test_w2a4_large_form_odd_group_count(kq, K):
 
 @pytest.mark.parametrize("Nr", [2032, 2064])
 def test_w2a4_forms_at_the_threshold(kq, Nr):
-    """Either side of the switch between the W2A4 forms on MI355X's 256 compute units: 128
-    tiles of 256 x 256 (N = 2032) take the 128 x 128 form, 144 (N = 2064) the large one; M and
-    N ragged against both tile sizes.  Oracle on sampled rows, all columns."""
+    """Either side of the switch to full-width tiles of the W2A4 large form on MI355X's 256
+    compute units: 128 tiles of 256 x 256 (N = 2032) run as 256 half-width tiles, 144
+    (N = 2064) as full ones; M and N ragged against both tile widths.  Oracle on sampled rows,
+    all columns."""
     import torch
     c = synth.CONFIGS[2]
     M, K = 4000, 2240

@@ -6,8 +6,8 @@
 // levels without their per-token scale, weight levels times their fp16 group scale), staged
 // in LDS once per workgroup tile and multiplied on the fp16 matrix cores (fp32
 // accumulation); the per-token scale multiplies the accumulator before the fp16 store.  Two
-// forms: 128 x 128 tiles of 16 x 16 x 32 products, and 256 x 256 tiles of 32 x 32 x 16
-// products for grids of more than half a round of tiles.
+// forms: 128 x 128 tiles of 16 x 16 x 32 products for small grids, and 256 x 256 tiles (or
+// 256 x 128 ones in a grid's last round) of 32 x 32 x 16 products.
 #include "kq_device.hpp"
 #include "kq_launch.hpp"
 
@@ -458,13 +458,15 @@ hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t
   // The large-tile form does a 256 x 256 tile in about the time of two rounds of 128 x 128
   // ones, and its rounds of tiles are four times coarser: it runs once the small tiles would
   // take more than two rounds (measured at K = 2240 and 5600: the small tiles win by 8-40%
-  // up to 128 large tiles, the large ones by 12-70% from 144 up).
-  // A last round that leaves compute units idle goes to tiles of half the width when those
-  // fit in one round (as in the W4A4 kernel).
+  // up to 128 large tiles, the large ones by 12-70% from 144 up).  A last round that leaves
+  // compute units idle goes to tiles of half the width when those fit in one round (as in
+  // the W4A4 kernel); so does a grid of at most half a round when its half-width tiles fill
+  // a quarter round or more (measured: they beat the small tiles by 2-25% from 64 of them
+  // up, and lose by 2-7% at 18-36).
   const int64_t cus = device_cu_count();
   const int64_t tiles_n = (N + 255) / 256, tiles_m = (M + 255) / 256, tiles_n2 = (N + 127) / 128;
   const int64_t t256 = tiles_n * tiles_m;
-  if (2 * t256 > cus) {
+  if (2 * t256 > cus || 4 * tiles_m * tiles_n2 >= cus) {
     const int64_t tail = t256 % cus;
     int64_t full_rows = tiles_m;
     if (tail > 0) {
