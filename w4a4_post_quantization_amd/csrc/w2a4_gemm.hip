@@ -257,7 +257,11 @@ __device__ __forceinline__ void w2a4_big_tile(uint8_t* __restrict__ lds, const u
   constexpr int A_OFF = 0, B_OFF = 256 * RB, BUF = 512 * RB;   // the full tile's layout in both widths
   constexpr int NWC = TN == 4 ? 8 : 4;                  // weight chunks a thread dequantizes per step
   constexpr int NU = TN == 4 ? 6 : 4;                   // loads a thread issues per step
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the thread index, hidden from the compiler: in the kernel's tile loop it would otherwise
+  // hoist every lane-dependent offset out of the loop and keep them live through it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wid = tid >> 6;
   const int wn = wid & 1, wm = wid >> 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int ng = K >> 5, nks = (ng + 1) >> 1;             // groups, 64-wide steps
@@ -418,7 +422,8 @@ __device__ __forceinline__ void w2a4_big_tile(uint8_t* __restrict__ lds, const u
 
 // The large-tile form's kernel: the first full_rows rows of 256 x 256 tiles take the full
 // tile (walked column by column in groups of 8 along M, die-contiguous, as in the W4A4
-// kernel), the tile rows below them, if any, tiles of half the width.
+// kernel), the tile rows below them, if any, tiles of half the width; with none of those,
+// each workgroup loops over every grid-th tile.
 __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     const uint8_t* __restrict__ xcodes, const float* __restrict__ xscales, int M, int K,
     const uint8_t* __restrict__ wcodes, const __half* __restrict__ wscales, int N, LmTables lm,
@@ -427,8 +432,7 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
   const LmRegTables lt = lm_reg_tables(lm);
   const int tiles_n = (N + 255) / 256;
   const int nfull = tiles_n * full_rows;
-  int pid = blockIdx.x;
-  if (pid < nfull) {
+  auto full_tile = [&](int pid) {
     {
       const int per = nfull / 8;
       if (pid < 8 * per) pid = (pid % 8) * per + pid / 8;
@@ -440,6 +444,19 @@ __global__ __launch_bounds__(256, 1) void w2a4_gemm_big_kernel(
     const int tile_m = first_m + (pid % (GM * tiles_n)) % gsize;
     const int tile_n = (pid % (GM * tiles_n)) / gsize;
     w2a4_big_tile<4>(lds, xcodes, xscales, M, K, wcodes, wscales, N, lt, Y, 256 * tile_m, 256 * tile_n);
+  };
+  if (full_rows == (M + 255) / 256) {
+    // full tiles only: workgroup b takes tiles b, b + G, .. (G = the grid, a multiple of the 8
+    // compute dies)
+    for (int t = blockIdx.x; t < nfull; t += gridDim.x) {
+      full_tile(t);
+      __syncthreads();
+    }
+    return;
+  }
+  const int pid = blockIdx.x;
+  if (pid < nfull) {
+    full_tile(pid);
   } else {
     const int hrows = (M + 255) / 256 - full_rows;
     const int nh = ((N + 127) / 128) * hrows;
@@ -473,9 +490,15 @@ hipError_t launch_w2a4_gemm(const uint8_t* xcodes, const float* xscales, int64_t
       const int64_t hr = (tail + tiles_n - 1) / tiles_n;     // tile rows that hold the tail
       if (hr * tiles_n2 <= cus) full_rows = tiles_m - hr;
     }
-    const unsigned grid = (unsigned)(tiles_n * full_rows + tiles_n2 * (tiles_m - full_rows));
-    hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3(grid), dim3(256), 0, s, xcodes, xscales, (int)M, (int)K, wcodes,
-                       wscales, (int)N, lm_tables(), Y, (int)full_rows);
+    int64_t grid = tiles_n * full_rows + tiles_n2 * (tiles_m - full_rows);
+    if (full_rows == tiles_m) {
+      // no half-width tiles: even rounds, as in the W4A4 kernel
+      const int64_t rounds = (t256 + cus - 1) / cus;
+      const int64_t even = ((t256 + rounds - 1) / rounds + 7) / 8 * 8;
+      if (even < grid) grid = even;
+    }
+    hipLaunchKernelGGL(w2a4_gemm_big_kernel, dim3((unsigned)grid), dim3(256), 0, s, xcodes, xscales, (int)M, (int)K,
+                       wcodes, wscales, (int)N, lm_tables(), Y, (int)full_rows);
     return hipGetLastError();
   }
   constexpr int BN = 128, BM = 128, WN = 2, WM = 2;
