@@ -4,7 +4,7 @@
 //
 // The projection only streams X (r is small), so the kernel is built for HBM bandwidth:
 //   - a workgroup owns 64 rows and a slice of K (split-K), so L1 is re-read once per 64
-//     rows and the grid has enough workgroups to keep every compute unit streaming;
+//     rows and the grid fills the compute units;
 //   - X and L1 go from global memory straight into LDS in 128-wide k-chunks (buffer loads
 //     with the LDS destination, full 128-byte lines), NS chunks deep;
 //   - each of the four wavefronts owns 16 rows and all r columns: v_mfma_f32_16x16x32_f16
@@ -201,13 +201,16 @@ __global__ __launch_bounds__(LR_RED_THREADS) void lowrank_reduce_kernel(const fl
   *reinterpret_cast<v2u*>(T + e) = v2u{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
 }
 
-// Slices of K per 64-row block: enough workgroups for every compute unit to hold a few,
-// a slice of at least four chunks, and (with `cap` bytes of workspace) partials that fit.
+// Slices of K per 64-row block: with fewer row blocks than compute units, as many as fill
+// the compute units once (at M = 4608, 3 slices, 216 workgroups, against 6 and 15 before:
+// the FLUX-like step 3.8 us faster); with more, enough workgroups for every compute unit to
+// hold a few.  A slice has at least four chunks, and (with `cap` bytes of workspace) the
+// partials fit.
 static int lr_slices(int64_t M, int64_t K, int r, size_t cap) {
   const int64_t blocks = (M + LR_ROWS - 1) / LR_ROWS;
   const int64_t nch = (K + LR_KC - 1) / LR_KC;
-  const int64_t want = 4 * (int64_t)device_cu_count();
-  int64_t s = (want + blocks - 1) / blocks;
+  const int64_t cus = device_cu_count();
+  int64_t s = blocks < cus ? cus / blocks : (4 * cus + blocks - 1) / blocks;
   s = std::min<int64_t>(s, std::max<int64_t>(1, nch / 4));
   while (s > 1 && (size_t)(s * M * r * 4) > cap) --s;
   return (int)std::max<int64_t>(s, 1);
