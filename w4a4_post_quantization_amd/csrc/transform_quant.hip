@@ -266,8 +266,9 @@ __global__ __launch_bounds__(512) void row_quant_kernel(const __half* __restrict
 }
 
 // Streaming Kronecker (or identity) + MXFP4 on the matrix cores: the activations are a
-// flat sequence of 32-element blocks; a wavefront handles 16 blocks (1 KiB) per step with
-// one 16-byte load per lane and writes 256 contiguous code bytes.
+// flat sequence of 32-element blocks; a wavefront handles U chunks of 16 blocks (1 KiB)
+// per step, each with one 16-byte load per lane, and writes 256 contiguous code bytes per
+// chunk.  The next step's chunks are loaded while the current ones are transformed.
 // KIND: 0 identity, 1 Kronecker A (x) B, 3 dense P (both through the hi + lo split).
 // PTS (DMQ explainer, channel-wise power-of-two scaling): before the transform, input
 // channel c is divided by 2^pts[c] in fp16 (exact unless the result is subnormal); channel
@@ -316,14 +317,21 @@ __global__ __launch_bounds__(256) void kron_mx_mfma_stream_kernel(const uint4* _
     cstep = (int32_t)((nwaves * 16) % nbk);
     fetch_exponents(ev);
   }
-  for (int64_t c0 = wave; c0 < nchunks; c0 += nwaves * U) {
-    uint4 raw[U];
+  uint4 nxt[U];     // the chunks of the next step, in flight while this one is transformed
+  auto load_step = [&](int64_t c0, uint4* r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * nwaves;
       const int64_t blk = c * 16 + bl;
-      raw[u] = (c < nchunks && blk < nblocks) ? X[blk * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
+      r[u] = (c < nchunks && blk < nblocks) ? X[blk * 4 + q] : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  if (wave < nchunks) load_step(wave, nxt);
+  for (int64_t c0 = wave; c0 < nchunks; c0 += nwaves * U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+    if (c0 + nwaves * U < nchunks) load_step(c0 + nwaves * U, nxt);
     uint2 ev_next[U];
     if (PTS) fetch_exponents(ev_next);
 #pragma unroll
@@ -710,54 +718,70 @@ __global__ __launch_bounds__((64 * rg_maxw<R, FMT>())) void rpbh_mx_group_kernel
   }
 }
 
-template <int U, int KIND>
-static void stream_launch(dim3 g, hipStream_t s, const uint4* X, int64_t nblocks, const KronFactors& f, const float* P,
+// Persistent workgroups: one per U chunks of each wavefront, at most as many as are
+// resident at once (a grid past that would run its last workgroups in a partial second
+// round, each with a full share of the chunks).
+template <int U, int KIND, bool PTS>
+static void stream_launch(int64_t nblocks, hipStream_t s, const uint4* X, const KronFactors& f, const float* P,
                           const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales) {
-  if (pts)
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, KIND, true>), g, dim3(256), 0, s, X, nblocks, f, P, pts, nbk,
-                       codes, scales);
-  else
-    hipLaunchKernelGGL((kron_mx_mfma_stream_kernel<U, KIND, false>), g, dim3(256), 0, s, X, nblocks, f, P, pts, nbk,
-                       codes, scales);
-}
-
-hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
-                               const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  constexpr int U = 4;
+  const auto kern = kron_mx_mfma_stream_kernel<U, KIND, PTS>;
   const int64_t nchunks = (nblocks + 15) / 16;
   const int64_t waves = (nchunks + U - 1) / U;
   int64_t grid = (waves + 3) / 4;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t cap =
+      (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), 256, 0);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, X, nblocks, f, P, pts, nbk, codes, scales);
+}
+
+template <int U, int KIND>
+static void stream_launch(int64_t nblocks, hipStream_t s, const uint4* X, const KronFactors& f, const float* P,
+                          const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales) {
+  if (pts) stream_launch<U, KIND, true>(nblocks, s, X, f, P, pts, nbk, codes, scales);
+  else stream_launch<U, KIND, false>(nblocks, s, X, f, P, pts, nbk, codes, scales);
+}
+
+// Two chunks per step with the next step's loads in flight (as many registers as four
+// chunks without them, so as many workgroups stay resident): against four chunks without,
+// 4-11% faster from M = 4608, K = 3072 to M = 8192, K = 4608 and equal at M = 8192,
+// K = 1152 and M = 17550, K = 3072; with one chunk per step (eight resident workgroups per
+// compute unit instead of five) the large shapes were 2-10% slower on one of three GPUs.
+hipError_t launch_kron_mx_mfma(int kind, const __half* X, int64_t nblocks, const KronFactors& f, const float* P,
+                               const int8_t* pts, int64_t nbk, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  constexpr int U = 2;
   const uint4* Xv = reinterpret_cast<const uint4*>(X);
-  const dim3 g((unsigned)grid);
-  if (kind == 1) stream_launch<U, 1>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
-  else if (kind == 3) stream_launch<U, 3>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
-  else stream_launch<U, 0>(g, s, Xv, nblocks, f, P, pts, nbk, codes, scales);
+  if (kind == 1) stream_launch<U, 1>(nblocks, s, Xv, f, P, pts, nbk, codes, scales);
+  else if (kind == 3) stream_launch<U, 3>(nblocks, s, Xv, f, P, pts, nbk, codes, scales);
+  else stream_launch<U, 0>(nblocks, s, Xv, f, P, pts, nbk, codes, scales);
   return hipGetLastError();
 }
 
 // Per-block factors: ceil(nbk / U) * nseg wavefronts, segment s of a run taking the 8-row
-// groups [s gps, (s + 1) gps).  About eight workgroups per compute unit in total.
-hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
-                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+// groups [s gps, (s + 1) gps); at most as many wavefronts as are resident at once, so that
+// no partial second round of workgroups follows the first.
+template <bool PTS>
+static void kron_blocks_launch(const uint4* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
+                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
   constexpr int U = 4, G = 2;
+  const auto kern = kron_blocks_mx_kernel<U, G, PTS>;
   const int64_t nbk = K / 32, nrun = (nbk + U - 1) / U, ngroups = (M + 7) / 8;
-  const int64_t target = (int64_t)device_cu_count() * 8 * 4;
-  int64_t nseg = (target + nrun - 1) / nrun;
+  const int64_t target =
+      (int64_t)device_cu_count() * resident_blocks_per_cu(reinterpret_cast<const void*>(kern), 256, 0) * 4;
+  int64_t nseg = target / nrun;
   if (nseg > ngroups) nseg = ngroups;
   if (nseg < 1) nseg = 1;
   const int64_t gps = (ngroups + nseg - 1) / nseg;
   nseg = (ngroups + gps - 1) / gps;                        // no empty segment
-  const dim3 g((unsigned)((nrun * nseg + 3) / 4));
+  hipLaunchKernelGGL(kern, dim3((unsigned)((nrun * nseg + 3) / 4)), dim3(256), 0, s, X, M, nbk, nseg, gps, AB, pts,
+                     codes, scales);
+}
+
+hipError_t launch_kron_blocks_mx(const __half* X, int64_t M, int64_t K, const float* AB, const int8_t* pts,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const uint4* Xv = reinterpret_cast<const uint4*>(X);
-  if (pts)
-    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, G, true>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
-                       scales);
-  else
-    hipLaunchKernelGGL((kron_blocks_mx_kernel<U, G, false>), g, dim3(256), 0, s, Xv, M, nbk, nseg, gps, AB, pts, codes,
-                       scales);
+  if (pts) kron_blocks_launch<true>(Xv, M, K, AB, pts, codes, scales, s);
+  else kron_blocks_launch<false>(Xv, M, K, AB, pts, codes, scales, s);
   return hipGetLastError();
 }
 
