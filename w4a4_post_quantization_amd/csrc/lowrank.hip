@@ -42,6 +42,7 @@ struct LrCfg {
   static constexpr int STAGE = X_BYTES + RR * 256;      // ... and of L1
   static constexpr int LDS = NS * STAGE;
   static constexpr int LPW = 4 + RR / 16;               // load instructions per wave per chunk
+  static constexpr int SPW = 8;                         // store instructions per wave per chunk (fused form)
 };
 
 template <int RR, int NS, int XK>
@@ -115,13 +116,24 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
       }
   }
   const int nbk = K >> 5;
+  // the fused form's codes and scales of this row block (rows past M are outside both ranges)
+  const __amdgpu_buffer_rsrc_t rcodes = make_rsrc(codes + (int64_t)m0 * (K >> 1), (int64_t)(M - m0) * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rscales = make_rsrc(scales + (int64_t)m0 * nbk, (int64_t)(M - m0) * nbk);
 
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) issue(p);
   const int arow = 16 * w + (lane & 15);
   for (int f = 0; f < nc; ++f) {
-    // chunk f has landed once at most the NS - 2 younger chunks' loads are outstanding
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * C::LPW));
+    // chunk f has landed once at most the operations issued after its loads are outstanding:
+    // the NS - 2 younger chunks' loads and, in the fused form, the SPW stores (all issued,
+    // masked lanes out of range) of each chunk processed since (at most NS - 1)
+    if (XK < 0 || f == 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * C::LPW));
+    } else if (NS == 2 || f == 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * C::LPW + C::SPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * C::LPW + 2 * C::SPW));
+    }
     lds_barrier();                                           // ... for every wave; stage (f - 1) % NS is free
     issue(f + NS - 1);
     const uint8_t* st = lds + (f % NS) * C::STAGE;
@@ -143,12 +155,13 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const __half* __restr
         uint32_t wd, sb;
         int off;
         mx_pack_block(y, lane >> 4, wd, off, sb);
+        // one code and one scale store per step, whatever the lanes hold (the wait above
+        // counts them)
         const int kb = (c0 + f) * 4 + s;
-        if (kb < nbk && m0 + arow < M) {
-          const int64_t blk = (int64_t)(m0 + arow) * nbk + kb;
-          *reinterpret_cast<uint32_t*>(codes + blk * 16 + off) = wd;
-          if ((lane >> 4) == 0) scales[blk] = (uint8_t)sb;
-        }
+        const int blk = arow * nbk + kb;                     // within the row block
+        __builtin_amdgcn_raw_buffer_store_b32(wd, rcodes, kb < nbk ? blk * 16 + off : KQ_OOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rscales, kb < nbk && (lane >> 4) == 0 ? blk : KQ_OOB, 0,
+                                             0);
       }
     }
   }
