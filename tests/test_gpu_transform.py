@@ -322,6 +322,32 @@ def test_rpbh_centred_row_group_widths(kq, K, rows):
     _mx_check(kq, X16, {"kind": "rpbh", "perm": perm, "sign": sign}, True, f"rpbh centred K={K} M={rows}")
 
 
+@pytest.mark.parametrize("kind,pts,M,K", [("kron", True, 8192, 4608), ("dense", True, 8192, 4608),
+                                           ("none", False, 8191, 4608), ("kron", False, 8193, 1152),
+                                           ("kron_blocks", False, 8192, 1152), ("kron_blocks", True, 8193, 4608)])
+def test_streaming_forms_full_size_sampled(kq, kind, pts, M, K):
+    """The streaming transforms at the PixArt-like sizes, on a grid of one resident round:
+    every wavefront takes several steps with the next step's chunks in flight (and, with
+    power-of-two scaling on the planted outlier channels, the next step's exponents); the
+    per-block kernel with segments of several row groups.  Ragged M; parity on sampled rows
+    (rows are independent)."""
+    X16 = synth.activations(M, K, 19, 2.0)
+    xf = {"kind": kind}
+    if kind == "kron":
+        xf["A"], xf["B"] = synth.kron_factors(19, 0)
+    elif kind == "dense":
+        xf["P"] = synth.dense_block(19, 0)
+    elif kind == "kron_blocks":
+        xf["A"], xf["B"] = synth.kron_block_factors(19, 0, K // 32)
+    if pts:
+        xf["pts"] = synth.pts_exponents(K, synth.outlier_channels(M, K, 19, 2.0))
+    codes, scales, _ = _run(kq, X16, xf, "mxfp4", False)
+    rows = np.unique(np.concatenate([np.arange(0, M, 131), [M - 2, M - 1]]))
+    y, tau, _ = gpu_util.oracle_activation_reference(X16[rows], xf, False)
+    gpu_util.assert_mx_parity(codes[rows], scales[rows], y, tau,
+                              label=f"{kind} pts={pts} M={M} K={K} sampled {len(rows)}")
+
+
 @pytest.mark.parametrize("cfg,layer", [(3, 0), (3, 2), (4, 0)])
 def test_full_size_sampled_rows(kq, cfg, layer):
     """Full workload size in the launch configuration of the bench; parity on sampled rows
